@@ -1,0 +1,74 @@
+"""Seeded synthetic inputs for the small-M FP8 block-scale GEMM.
+
+This module only draws random numbers and lays them out; it holds none of the method's
+arithmetic (no quantisation, no scales, no products).  Both the GPU library's tests/benchmark
+and the CPU oracle take their inputs from here.
+
+Recipe (the pages' workloads are Qwen3.5-397B-A17B TP4 projection shapes run on 1-32 decode or
+verify rows, see sglang "[AMD] Small-M FP8 block-scale GEMM with fused activation quant for
+gfx950 (Qwen3.5)", sections Modifications and Kernel microbenchmarks; trained weights are not
+used, these synthetic draws stand in for them):
+
+* X, bf16 [M, K]: z ~ N(0, 1) in fp32, each 1x128 group multiplied by f = 2^u with
+  u ~ U(-4, 4) drawn once per (row, group); x = bf16_rne(fp32(z * f)).  numpy PCG64 seeded with
+  the tuple (seed, 0).
+* Outlier rows (optional): ceil(0.05 * M) rows picked by a seeded permutation; in every 1x128
+  group of those rows one uniformly chosen position is set to +-1000 (exact in bf16) with a
+  random sign.  Seed tuple (seed, 0, 1).
+* W, fp32 [N, K]: w ~ N(0, 0.02), weight copy i drawn with seed tuple (seed, 1, i).  The fp8
+  weight and its block scales are derived from it by a quantiser (oracle or library), never
+  here.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bit patterns.
+
+    Used only to produce bf16 inputs; inputs here are always finite."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def gen_x(M: int, K: int, seed: int = 0, outliers: bool = False) -> np.ndarray:
+    """bf16 activations as uint16 bit patterns, shape [M, K]."""
+    assert K % 128 == 0
+    rng = np.random.default_rng([seed, 0])
+    z = rng.standard_normal((M, K), dtype=np.float32)
+    u = rng.uniform(-4.0, 4.0, size=(M, K // 128))
+    f = np.exp2(u).astype(np.float32)
+    v = (z.reshape(M, K // 128, 128) * f[:, :, None]).astype(np.float32).reshape(M, K)
+    x = f32_to_bf16_bits(v)
+    if outliers and M > 0:
+        orng = np.random.default_rng([seed, 0, 1])
+        n_out = math.ceil(0.05 * M)
+        rows = orng.permutation(M)[:n_out]
+        G = K // 128
+        pos = orng.integers(0, 128, size=(n_out, G))
+        sgn = orng.integers(0, 2, size=(n_out, G))
+        one_k = np.uint16(0x447A)  # 1000.0 in bf16
+        for i, r in enumerate(rows):
+            for g in range(G):
+                x[r, 128 * g + pos[i, g]] = one_k | (np.uint16(0x8000) if sgn[i, g] else np.uint16(0))
+    return x
+
+
+def gen_w(N: int, K: int, seed: int = 0, copy: int = 0) -> np.ndarray:
+    """fp32 master weights ~ N(0, 0.02), shape [N, K]."""
+    rng = np.random.default_rng([seed, 1, copy])
+    return rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+
+
+def outlier_rows(M: int, seed: int = 0) -> np.ndarray:
+    """The rows gen_x(..., outliers=True) turns into outlier rows."""
+    orng = np.random.default_rng([seed, 0, 1])
+    return orng.permutation(M)[: math.ceil(0.05 * M)]
