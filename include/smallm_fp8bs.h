@@ -1,0 +1,147 @@
+/*
+ * smallm_fp8bs.h -- C ABI of libsmallm_fp8bs.so: small-M FP8 block-scale GEMM with fused
+ * activation quantisation for MI355X (gfx950).
+ *
+ *   Y[m, n] (bf16) = sum_k q(X)[m, k] * sx[m, k/128] * W8[n, k] * sw[n/128, k/128]
+ *
+ * The operation is the one described on the sglang page "[AMD] Small-M FP8 block-scale GEMM
+ * with fused activation quant for gfx950 (Qwen3.5)", section Modifications: bf16 activations
+ * are quantised to e4m3 in 1x128 groups (one scale per row and 128-column group), the e4m3
+ * weight carries one fp32 scale per 128x128 block (shape [N/128, K/128]), each 128-wide K
+ * block's partial sum is multiplied by x_scale * w_scale in fp32, and the result is written
+ * as bf16.  The e8m0 entry points follow "[Perf] [AMD] dsv4: optional e8m0 mxscale GEMM for
+ * dense 128x128 fp8 linears" (Modifications, commit message): the same GEMM with
+ * power-of-two scales stored as one e8m0 byte each (value 2^(byte - 127)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library allocates no
+ *    memory, keeps no state between calls, never synchronises the host and enqueues work only
+ *    on `stream` (a hipStream_t; NULL is the legacy default stream).  Every call can therefore
+ *    be captured into a HIP graph.
+ *  - bf16 is passed as uint16_t bit patterns; e4m3 (OCP float8 e4m3fn) and e8m0 as uint8_t.
+ *  - Matrices are row-major with an explicit leading dimension in ELEMENTS (ldx, ldq, ldy).
+ *  - Activation scales are [M, K/128] row-major (fp32 or e8m0 bytes); weight scales are
+ *    [N/128, K/128] row-major, contiguous.
+ *  - Shapes: 1 <= M <= SMALLM_FP8BS_MAX_M, N and K positive multiples of 128, else
+ *    SMALLM_ERR_SHAPE.  M <= 32 is the design range (decode and verify rows); larger M is
+ *    accepted to locate the crossover with tiled GEMMs.
+ *  - Alignment: x, q, w8, w_packed and w must be 16-byte aligned and their row pitches
+ *    multiples of 16 bytes; y must be 2-byte aligned; else SMALLM_ERR_ALIGN.
+ *  - Every error except SMALLM_ERR_HIP is detected before anything is enqueued; on an error
+ *    the outputs are left untouched.  SMALLM_ERR_HIP means the launch itself failed.
+ *  - Inputs must be finite; the results for NaN or infinite inputs are unspecified.
+ *  - Results are deterministic: the same inputs give bit-identical outputs, eagerly or replayed
+ *    from a graph (fixed reduction order, no atomics).
+ */
+#ifndef SMALLM_FP8BS_H
+#define SMALLM_FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMALLM_FP8BS_ABI_VERSION 1
+#define SMALLM_FP8BS_MAX_M 256
+
+typedef enum {
+  SMALLM_OK = 0,
+  SMALLM_ERR_INVALID = 1, /* a required pointer is NULL */
+  SMALLM_ERR_SHAPE = 2,   /* M, N, K or a leading dimension out of range */
+  SMALLM_ERR_ALIGN = 3,   /* pointer or row pitch misaligned */
+  SMALLM_ERR_LAYOUT = 4,  /* packed-weight layout id does not match this library */
+  SMALLM_ERR_HIP = 5      /* the HIP launch failed */
+} smallm_status;
+
+/* Version of this ABI (SMALLM_FP8BS_ABI_VERSION of the header the library was built with). */
+int smallm_fp8bs_abi_version(void);
+
+/* Identifier of the packed weight layout produced by smallm_fp8bs_pack_weight.  The GEMM
+ * entry points take it back and refuse weights packed for another layout (the pages' guard
+ * only takes the fused path for a weight marked as preshuffled, section Modifications). */
+uint32_t smallm_fp8bs_weight_layout_id(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* smallm_fp8bs_strerror(int status);
+
+/* Host-only shape check for the fused path: SMALLM_OK if (M, N, K, ldx) is accepted by
+ * smallm_fp8bs_quant_gemm, else the status it would return.  Enqueues nothing. */
+int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx);
+
+/* --------------------------------------------------------------------------------------------
+ * Load-time weight preparation (not on the per-token path)
+ * ------------------------------------------------------------------------------------------ */
+
+/* Quantise an fp32 weight to e4m3 with one fp32 scale per 128x128 block:
+ * sw = RN32(amax / 448) over the block, w8 = e4m3_rne_sat(RN32(w / sw)); an all-zero block gets
+ * sw = 0 and signed-zero codes.  w: fp32 [N, ldw]; w8: e4m3 [N, K] (row pitch K);
+ * sw: fp32 [N/128, K/128].  The pages start from weights already in this form
+ * (weight_scale_inv, section Modifications); this entry produces them from fp32 masters. */
+int smallm_fp8bs_quant_weight(const float* w, int64_t ldw, uint8_t* w8, float* sw,
+                              int N, int K, void* stream);
+
+/* Same with power-of-two block scales stored as e8m0 bytes: E = log2(amax / 448) rounded to the
+ * nearest integer, clamped to [-127, 127] (all-zero block: -127); byte = E + 127;
+ * w8 = e4m3_rne(w * 2^-E) saturated to +-448. */
+int smallm_fp8bs_quant_weight_e8m0(const float* w, int64_t ldw, uint8_t* w8, uint8_t* sw_e8m0,
+                                   int N, int K, void* stream);
+
+/* Permute a row-major e4m3 weight [N, K] (row pitch K) into the library's packed layout
+ * (N*K bytes, id smallm_fp8bs_weight_layout_id()).  Each 16-column x 128-K block becomes one
+ * contiguous 2 KiB fragment laid out in the lane order of the gfx950 16x16x128 fp8 MFMA B
+ * operand, so that one wave reads it with two fully coalesced 16-byte loads per lane.
+ * w8 and w_packed must not overlap. */
+int smallm_fp8bs_pack_weight(const uint8_t* w8, uint8_t* w_packed, int N, int K, void* stream);
+
+/* Inverse of smallm_fp8bs_pack_weight (used by tests). */
+int smallm_fp8bs_unpack_weight(const uint8_t* w_packed, uint8_t* w8, int N, int K, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * Per-token path
+ * ------------------------------------------------------------------------------------------ */
+
+/* Activation quantisation in 1x128 groups with fp32 scales (the pages' standalone quant, the
+ * first of the two launches the fused kernel replaces; section Motivation):
+ * sx[m, g] = RN32(amax_g / 448); q = e4m3_rne(RN32(x / sx)) with the sign of zero kept; an
+ * all-zero group gets sx = 0 and signed-zero codes.  x: bf16 [M, ldx]; q: e4m3 [M, ldq];
+ * sx: fp32 [M, K/128]. */
+int smallm_fp8bs_quant(const uint16_t* x, int64_t ldx, uint8_t* q, int64_t ldq, float* sx,
+                       int M, int K, void* stream);
+
+/* Activation quantisation with ue8m0 group scales ("per-1x128 ue8m0 quant", commit message of
+ * the e8m0 page): E = smallest integer with amax_g <= 448 * 2^E, clamped to [-127, 127]
+ * (all-zero group: -127); sx byte = E + 127; q = e4m3_rne(x * 2^-E). */
+int smallm_fp8bs_quant_e8m0(const uint16_t* x, int64_t ldx, uint8_t* q, int64_t ldq,
+                            uint8_t* sx_e8m0, int M, int K, void* stream);
+
+/* GEMM on pre-quantised activations (the second of the two launches): q e4m3 [M, ldq],
+ * sx fp32 [M, K/128], packed weight, sw fp32 [N/128, K/128]  ->  y bf16 [M, ldy] (RNE). */
+int smallm_fp8bs_gemm(const uint8_t* q, int64_t ldq, const float* sx, const uint8_t* w_packed,
+                      uint32_t layout_id, const float* sw, uint16_t* y, int64_t ldy,
+                      int M, int N, int K, void* stream);
+
+/* Same with e8m0 activation and weight scales. */
+int smallm_fp8bs_gemm_e8m0(const uint8_t* q, int64_t ldq, const uint8_t* sx_e8m0,
+                           const uint8_t* w_packed, uint32_t layout_id, const uint8_t* sw_e8m0,
+                           uint16_t* y, int64_t ldy, int M, int N, int K, void* stream);
+
+/* The fused path (one launch): quantise x exactly as smallm_fp8bs_quant does, then the GEMM,
+ * without writing q to memory.  If q_dbg / sx_dbg are non-NULL the kernel also writes the q
+ * bytes ([M, K], pitch K) and scales ([M, K/128]) it used, for bit-exact testing. */
+int smallm_fp8bs_quant_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                            uint32_t layout_id, const float* sw, uint16_t* y, int64_t ldy,
+                            int M, int N, int K, uint8_t* q_dbg, float* sx_dbg, void* stream);
+
+/* Fused path with e8m0 scales (activation quant as smallm_fp8bs_quant_e8m0). */
+int smallm_fp8bs_quant_gemm_e8m0(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                 uint32_t layout_id, const uint8_t* sw_e8m0, uint16_t* y,
+                                 int64_t ldy, int M, int N, int K, uint8_t* q_dbg,
+                                 uint8_t* sx_dbg_e8m0, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMALLM_FP8BS_H */

@@ -1,0 +1,338 @@
+"""Python binding of libsmallm_fp8bs.so: small-M FP8 block-scale GEMM with fused activation
+quantisation for MI355X (gfx950).
+
+The functions below carry the names of the C entry points declared in include/smallm_fp8bs.h
+and only marshal arguments: torch provides device memory and the current HIP stream, every step
+of the computation runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if
+the shared library is missing or a call fails, an exception is raised.
+
+The library must bind to the HIP runtime torch already loaded (a second libamdhip64 in the
+process makes launches on torch's streams fail; sglang "[AMD] Small-M MXFP4 fused-MoE kernel for
+gfx950 (Qwen)", loader fix in the commit history).  torch is therefore imported and initialised
+before the library is opened, and the loader checks that only one libamdhip64 is mapped.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsmallm_fp8bs.so")
+
+SMALLM_OK = 0
+SMALLM_ERR_INVALID = 1
+SMALLM_ERR_SHAPE = 2
+SMALLM_ERR_ALIGN = 3
+SMALLM_ERR_LAYOUT = 4
+SMALLM_ERR_HIP = 5
+MAX_M = 256
+
+EXPORTS = (
+    "smallm_fp8bs_abi_version",
+    "smallm_fp8bs_weight_layout_id",
+    "smallm_fp8bs_strerror",
+    "smallm_fp8bs_supported",
+    "smallm_fp8bs_quant_weight",
+    "smallm_fp8bs_quant_weight_e8m0",
+    "smallm_fp8bs_pack_weight",
+    "smallm_fp8bs_unpack_weight",
+    "smallm_fp8bs_quant",
+    "smallm_fp8bs_quant_e8m0",
+    "smallm_fp8bs_gemm",
+    "smallm_fp8bs_gemm_e8m0",
+    "smallm_fp8bs_quant_gemm",
+    "smallm_fp8bs_quant_gemm_e8m0",
+)
+
+
+class SmallmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({strerror(status)})")
+
+
+_lib = None
+
+
+def _hip_runtimes_mapped() -> set:
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                p = line.split()[-1]
+                if "libamdhip64" in p:
+                    paths.add(os.path.realpath(p))
+    except OSError:
+        pass
+    return paths
+
+
+def lib():
+    """Open libsmallm_fp8bs.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with precision_gemm_x128_amd.build.build() "
+                          "(there is no fallback path)")
+    if torch.cuda.is_available():
+        torch.cuda.init()
+    L = ctypes.CDLL(LIB_PATH)
+    rts = _hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(rts)}")
+    P, I, I64, U32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
+    sig = {
+        "smallm_fp8bs_abi_version": (I, []),
+        "smallm_fp8bs_weight_layout_id": (U32, []),
+        "smallm_fp8bs_strerror": (ctypes.c_char_p, [I]),
+        "smallm_fp8bs_supported": (I, [I, I, I, I64]),
+        "smallm_fp8bs_quant_weight": (I, [P, I64, P, P, I, I, P]),
+        "smallm_fp8bs_quant_weight_e8m0": (I, [P, I64, P, P, I, I, P]),
+        "smallm_fp8bs_pack_weight": (I, [P, P, I, I, P]),
+        "smallm_fp8bs_unpack_weight": (I, [P, P, I, I, P]),
+        "smallm_fp8bs_quant": (I, [P, I64, P, I64, P, I, I, P]),
+        "smallm_fp8bs_quant_e8m0": (I, [P, I64, P, I64, P, I, I, P]),
+        "smallm_fp8bs_gemm": (I, [P, I64, P, P, U32, P, P, I64, I, I, I, P]),
+        "smallm_fp8bs_gemm_e8m0": (I, [P, I64, P, P, U32, P, P, I64, I, I, I, P]),
+        "smallm_fp8bs_quant_gemm": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
+        "smallm_fp8bs_quant_gemm_e8m0": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------------------------------------
+# host-only queries
+# ---------------------------------------------------------------------------------------------
+
+def smallm_fp8bs_abi_version() -> int:
+    return int(lib().smallm_fp8bs_abi_version())
+
+
+def smallm_fp8bs_weight_layout_id() -> int:
+    return int(lib().smallm_fp8bs_weight_layout_id())
+
+
+def strerror(status: int) -> str:
+    return lib().smallm_fp8bs_strerror(int(status)).decode()
+
+
+smallm_fp8bs_strerror = strerror
+
+
+def smallm_fp8bs_supported(M: int, N: int, K: int, ldx: int) -> int:
+    return int(lib().smallm_fp8bs_supported(M, N, K, ldx))
+
+
+# ---------------------------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------------------------
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, where: str):
+    if status != SMALLM_OK:
+        raise SmallmError(status, where)
+
+
+def _need(t, dtypes, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_U8 = (torch.uint8,)
+_F8 = (torch.uint8, torch.float8_e4m3fn)
+_BF = (torch.bfloat16,)
+_F32 = (torch.float32,)
+
+
+# ---------------------------------------------------------------------------------------------
+# load-time weight preparation
+# ---------------------------------------------------------------------------------------------
+
+def smallm_fp8bs_quant_weight(w, w8=None, sw=None, stream=None):
+    """fp32 [N, K] -> (e4m3 bytes uint8 [N, K], fp32 block scales [N/128, K/128])."""
+    _need(w, _F32, "w")
+    N, K = w.shape
+    w8 = torch.empty((N, K), dtype=torch.uint8, device=w.device) if w8 is None else w8
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device) if sw is None else sw
+    _check(lib().smallm_fp8bs_quant_weight(_ptr(w), w.stride(0), _ptr(w8), _ptr(sw), N, K, _stream(stream)),
+           "smallm_fp8bs_quant_weight")
+    return w8, sw
+
+
+def smallm_fp8bs_quant_weight_e8m0(w, w8=None, sw=None, stream=None):
+    """fp32 [N, K] -> (e4m3 bytes uint8 [N, K], e8m0 block scale bytes uint8 [N/128, K/128])."""
+    _need(w, _F32, "w")
+    N, K = w.shape
+    w8 = torch.empty((N, K), dtype=torch.uint8, device=w.device) if w8 is None else w8
+    sw = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=w.device) if sw is None else sw
+    _check(lib().smallm_fp8bs_quant_weight_e8m0(_ptr(w), w.stride(0), _ptr(w8), _ptr(sw), N, K, _stream(stream)),
+           "smallm_fp8bs_quant_weight_e8m0")
+    return w8, sw
+
+
+def smallm_fp8bs_pack_weight(w8, out=None, stream=None):
+    """Row-major e4m3 [N, K] -> packed weight (uint8, same shape, library layout)."""
+    _need(w8, _F8, "w8")
+    _contig(w8, "w8")
+    N, K = w8.shape
+    out = torch.empty((N, K), dtype=torch.uint8, device=w8.device) if out is None else out
+    _check(lib().smallm_fp8bs_pack_weight(_ptr(w8), _ptr(out), N, K, _stream(stream)), "smallm_fp8bs_pack_weight")
+    return out
+
+
+def smallm_fp8bs_unpack_weight(w_packed, out=None, stream=None):
+    _need(w_packed, _U8, "w_packed")
+    _contig(w_packed, "w_packed")
+    N, K = w_packed.shape
+    out = torch.empty((N, K), dtype=torch.uint8, device=w_packed.device) if out is None else out
+    _check(lib().smallm_fp8bs_unpack_weight(_ptr(w_packed), _ptr(out), N, K, _stream(stream)),
+           "smallm_fp8bs_unpack_weight")
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# per-token path
+# ---------------------------------------------------------------------------------------------
+
+def smallm_fp8bs_quant(x, q=None, sx=None, stream=None):
+    """bf16 [M, K] -> (e4m3 bytes uint8 [M, K], fp32 group scales [M, K/128])."""
+    _need(x, _BF, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    sx = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if sx is None else sx
+    _check(lib().smallm_fp8bs_quant(_ptr(x), x.stride(0), _ptr(q), q.stride(0), _ptr(sx), M, K, _stream(stream)),
+           "smallm_fp8bs_quant")
+    return q, sx
+
+
+def smallm_fp8bs_quant_e8m0(x, q=None, sx=None, stream=None):
+    """bf16 [M, K] -> (e4m3 bytes uint8 [M, K], ue8m0 group scale bytes uint8 [M, K/128])."""
+    _need(x, _BF, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    sx = torch.empty((M, K // 128), dtype=torch.uint8, device=x.device) if sx is None else sx
+    _check(lib().smallm_fp8bs_quant_e8m0(_ptr(x), x.stride(0), _ptr(q), q.stride(0), _ptr(sx), M, K,
+                                         _stream(stream)), "smallm_fp8bs_quant_e8m0")
+    return q, sx
+
+
+def _check_weight(w_packed, sw, K, e8m0):
+    N = w_packed.shape[0]
+    if w_packed.shape[1] != K:
+        raise ValueError(f"packed weight is [{N}, {w_packed.shape[1]}] but the activations have K={K}")
+    if tuple(sw.shape) != (N // 128, K // 128):
+        raise ValueError(f"weight scales must be [{N // 128}, {K // 128}], got {tuple(sw.shape)}")
+    if sw.dtype != (torch.uint8 if e8m0 else torch.float32):
+        raise TypeError(f"weight scales must be {'uint8 (e8m0)' if e8m0 else 'float32'}, got {sw.dtype}")
+    return N
+
+
+def _check_act_scales(sx, M, K, e8m0):
+    if tuple(sx.shape) != (M, K // 128):
+        raise ValueError(f"activation scales must be [{M}, {K // 128}], got {tuple(sx.shape)}")
+    if sx.dtype != (torch.uint8 if e8m0 else torch.float32):
+        raise TypeError(f"activation scales must be {'uint8 (e8m0)' if e8m0 else 'float32'}, got {sx.dtype}")
+
+
+def _out(y, M, N, device):
+    if y is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _need(y, _BF, "y")
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [{M}, {N}], got {tuple(y.shape)}")
+    return y
+
+
+def smallm_fp8bs_gemm(q, sx, w_packed, sw, y=None, layout_id=None, stream=None):
+    """Pre-quantised q [M, K] (uint8) and fp32 sx [M, K/128] times the packed weight -> bf16 [M, N]."""
+    _need(q, _F8, "q")
+    _need(w_packed, _U8, "w_packed")
+    _contig(sx, "sx")
+    _contig(sw, "sw")
+    M, K = q.shape
+    N = _check_weight(w_packed, sw, K, False)
+    _check_act_scales(sx, M, K, False)
+    y = _out(y, M, N, q.device)
+    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_gemm(_ptr(q), q.stride(0), _ptr(sx), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
+                                   y.stride(0), M, N, K, _stream(stream)), "smallm_fp8bs_gemm")
+    return y
+
+
+def smallm_fp8bs_gemm_e8m0(q, sx, w_packed, sw, y=None, layout_id=None, stream=None):
+    _need(q, _F8, "q")
+    _need(w_packed, _U8, "w_packed")
+    _contig(sx, "sx")
+    _contig(sw, "sw")
+    M, K = q.shape
+    N = _check_weight(w_packed, sw, K, True)
+    _check_act_scales(sx, M, K, True)
+    y = _out(y, M, N, q.device)
+    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_gemm_e8m0(_ptr(q), q.stride(0), _ptr(sx), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
+                                        y.stride(0), M, N, K, _stream(stream)), "smallm_fp8bs_gemm_e8m0")
+    return y
+
+
+def smallm_fp8bs_quant_gemm(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, layout_id=None, stream=None):
+    """Fused path: bf16 x [M, K], packed weight [N, K], fp32 sw [N/128, K/128] -> bf16 y [M, N]."""
+    _need(x, _BF, "x")
+    _need(w_packed, _U8, "w_packed")
+    _contig(sw, "sw")
+    M, K = x.shape
+    N = _check_weight(w_packed, sw, K, False)
+    y = _out(y, M, N, x.device)
+    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_quant_gemm(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
+                                         y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
+           "smallm_fp8bs_quant_gemm")
+    return y
+
+
+def smallm_fp8bs_quant_gemm_e8m0(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, layout_id=None, stream=None):
+    _need(x, _BF, "x")
+    _need(w_packed, _U8, "w_packed")
+    _contig(sw, "sw")
+    M, K = x.shape
+    N = _check_weight(w_packed, sw, K, True)
+    y = _out(y, M, N, x.device)
+    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_quant_gemm_e8m0(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
+                                              y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
+           "smallm_fp8bs_quant_gemm_e8m0")
+    return y
+
+
+def algorithmic_bytes(M: int, N: int, K: int, e8m0: bool = False) -> int:
+    """Bytes one fused call must move at minimum: the fp8 weight once, its block scales, the bf16
+    activations and the bf16 output."""
+    s_w = 1 if e8m0 else 4
+    return N * K + s_w * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N

@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol the
+header declares, and rejects bad arguments before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_gemm_x128_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smallm_fp8bs.h")
+
+
+def header_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(smallm_fp8bs_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_what_binding_lists():
+    assert header_symbols() == sorted(P.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = P.lib()
+    for name in header_symbols():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {P.LIB_PATH}").read()
+    for name in header_symbols():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_layout_and_strerror():
+    assert P.smallm_fp8bs_abi_version() == 1
+    assert P.smallm_fp8bs_weight_layout_id() == 0x46384231
+    for s in range(6):
+        assert len(P.strerror(s)) > 0
+    assert P.strerror(99) == "unknown status"
+
+
+@pytest.mark.parametrize("M,N,K,ldx,expect", [
+    (1, 4096, 2048, 2048, 0), (32, 5120, 4096, 4096, 0), (256, 4096, 2048, 2048, 0),
+    (0, 4096, 2048, 2048, 2), (257, 4096, 2048, 2048, 2), (4, 4000, 2048, 2048, 2),
+    (4, 4096, 2000, 2000, 2), (4, 4096, 2048, 2047, 2), (4, 4096, 2048, 2052, 3),
+    (4, 4096, 2048, 2056, 0), (4, 0, 2048, 2048, 2), (4, 4096, -128, 2048, 2),
+])
+def test_supported(M, N, K, ldx, expect):
+    assert P.smallm_fp8bs_supported(M, N, K, ldx) == expect
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def test_rejections_happen_before_any_launch():
+    """Invalid arguments are refused on the host; these calls never reach HIP (no GPU here)."""
+    L = P.lib()
+    lid = P.smallm_fp8bs_weight_layout_id()
+    f = _fake()
+    # null pointers
+    assert L.smallm_fp8bs_quant_gemm(None, 2048, f, lid, f, f, 4096, 4, 4096, 2048, None, None, None) == 1
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, None, lid, f, f, 4096, 4, 4096, 2048, None, None, None) == 1
+    assert L.smallm_fp8bs_gemm(f, 2048, None, f, lid, f, f, 4096, 4, 4096, 2048, None) == 1
+    assert L.smallm_fp8bs_quant(None, 2048, f, 2048, f, 4, 2048, None) == 1
+    assert L.smallm_fp8bs_pack_weight(None, f, 128, 128, None) == 1
+    assert L.smallm_fp8bs_quant_weight(f, 128, None, f, 128, 128, None) == 1
+    # shapes
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid, f, f, 4096, 0, 4096, 2048, None, None, None) == 2
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid, f, f, 4096, 257, 4096, 2048, None, None, None) == 2
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid, f, f, 4096, 4, 4100, 2048, None, None, None) == 2
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid, f, f, 4000, 4, 4096, 2048, None, None, None) == 2
+    assert L.smallm_fp8bs_quant_gemm_e8m0(f, 2048, f, lid, f, f, 4096, 4, 4096, 2000, None, None, None) == 2
+    assert L.smallm_fp8bs_quant(f, 2048, f, 2048, f, 4, 2100, None) == 2
+    assert L.smallm_fp8bs_pack_weight(f, f, 100, 128, None) == 2
+    # alignment: x base, x row pitch, weight base, odd y, q_dbg
+    assert L.smallm_fp8bs_quant_gemm(_fake(0x10008), 2048, f, lid, f, f, 4096, 4, 4096, 2048, None, None, None) == 3
+    assert L.smallm_fp8bs_quant_gemm(f, 2052, f, lid, f, f, 4096, 4, 4096, 2048, None, None, None) == 3
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, _fake(0x10004), lid, f, f, 4096, 4, 4096, 2048, None, None, None) == 3
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid, f, _fake(0x10001), 4096, 4, 4096, 2048, None, None, None) == 3
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid, f, f, 4096, 4, 4096, 2048, _fake(0x10002), None, None) == 3
+    assert L.smallm_fp8bs_gemm(f, 2056, f, f, lid, f, f, 4096, 4, 4096, 2048, None) == 3
+    assert L.smallm_fp8bs_quant(f, 2048, f, 2056, f, 4, 2048, None) == 3
+    # layout id
+    assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid ^ 1, f, f, 4096, 4, 4096, 2048, None, None, None) == 4
+    assert L.smallm_fp8bs_gemm_e8m0(f, 2048, f, f, 0, f, f, 4096, 4, 4096, 2048, None) == 4
+
+
+def test_binding_rejects_wrong_dtypes_without_gpu():
+    import torch
+    x16 = torch.zeros((4, 256), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        P.smallm_fp8bs_quant_gemm(x16, torch.zeros((128, 256), dtype=torch.uint8), torch.zeros((1, 2)))
+    xb = torch.zeros((4, 256), dtype=torch.bfloat16)  # host tensor: refused, never handed to HIP
+    with pytest.raises(ValueError):
+        P.smallm_fp8bs_quant(xb)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(P, "_lib", None)
+    monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        P.lib()
