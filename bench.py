@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused small-M FP8 block-scale quant+GEMM on one MI355X.
+
+Workload (the shape the pages' kernel microbenchmark is quoted on, sglang "[AMD] Small-M FP8
+block-scale GEMM with fused activation quant for gfx950 (Qwen3.5)", section Kernel
+microbenchmarks): N=5120, K=4096 (the in_proj_qkvz shard), bf16 activations at
+M = 1, 4, 8, 16, 32 rows, e4m3 weights with fp32 128x128 block scales, bf16 output, graph replay,
+weights rotated over 24 distinct copies so they are not cache resident.
+
+For every M a HIP graph of 24 fused calls is captured, call i on weight copy i.  One step is one
+replay of each M's graph: 24 calls at every M of the sweep, 120 calls in all.  value = algorithmic
+bytes moved by the timed calls / elapsed time of the timed steps (HIP events on the stream the
+graphs run on).  Each M's graph is also timed on its own for the per-M us/call.
+
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/call + achieved HBM GB/s (% of MI355X peak), fused quant+FP8 GEMM, M=1–32"
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+N_DEFAULT, K_DEFAULT = 5120, 4096
+M_SWEEP = (1, 4, 8, 16, 32)
+COPIES = 24
+# The pages' fused-kernel times for this shape (us), same hardware and method: context for vs_baseline.
+PAGES_FUSED_US = {1: 6.8, 4: 7.3, 8: 7.7, 16: 9.0, 32: 12.8}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    src = os.path.join(ROOT, "precision_gemm_x128_amd", "csrc", "smallm_fp8bs.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kname):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_fused_5120x4096.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    k = d.get("kernels", {}).get(kname)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=COPIES)
+    ap.add_argument("--N", type=int, default=N_DEFAULT)
+    ap.add_argument("--K", type=int, default=K_DEFAULT)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="target seconds per CPU leg")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import precision_gemm_x128_amd as P
+    import synthgen
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    N, K, copies = args.N, args.K, args.copies
+    P.lib()
+
+    # ---- inputs: 24 cold weight copies, quantised and packed on the device (load-time work) ----
+    t0 = time.time()
+    wps, sws = [], []
+    for i in range(copies):
+        w = torch.from_numpy(synthgen.gen_w(N, K, seed=0, copy=i)).to(dev)
+        w8, sw = P.smallm_fp8bs_quant_weight(w)
+        wps.append(P.smallm_fp8bs_pack_weight(w8))
+        sws.append(sw)
+        del w, w8
+    torch.cuda.synchronize()
+    log(f"[bench] prepared {copies} weight copies {N}x{K} in {time.time() - t0:.1f}s")
+    xs = {M: torch.from_numpy(synthgen.gen_x(M, K, seed=0).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+          for M in M_SWEEP}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in M_SWEEP}
+
+    # ---- one graph of `copies` calls per M ----
+    graphs = {}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for M in M_SWEEP:
+            for i in range(copies):
+                P.smallm_fp8bs_quant_gemm(xs[M], wps[i], sws[i], y=ys[M])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for M in M_SWEEP:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(copies):
+                P.smallm_fp8bs_quant_gemm(xs[M], wps[i], sws[i], y=ys[M])
+        graphs[M] = g
+    # launch floor: the same number of trivial launches in a graph
+    tiny = torch.zeros(1, device=dev)
+    gfloor = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gfloor):
+        for i in range(copies):
+            tiny.add_(1.0)
+    torch.cuda.synchronize()
+
+    def run_step():
+        for M in M_SWEEP:
+            graphs[M].replay()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps ----
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {step_ms:.4f} ms/step (wall {1e3 * (wall1 - wall0) / args.steps:.4f})")
+
+    bytes_per_call = {M: P.algorithmic_bytes(M, N, K) for M in M_SWEEP}
+    step_bytes = copies * sum(bytes_per_call.values())
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+
+    # ---- per-M breakdown (each M's graph timed on its own, same stream) ----
+    reps = max(args.steps, 20)
+    sweep = {}
+    for M in M_SWEEP:
+        graphs[M].replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            graphs[M].replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * copies)
+        gbs = bytes_per_call[M] / (us * 1e-6) / 1e9
+        sweep[str(M)] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
+                         "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                         "algorithmic_bytes": bytes_per_call[M], "kernel": P.kernel_name(M, N, K),
+                         "plan": P.smallm_fp8bs_launch_plan(M, N, K)}
+        log(f"[bench] M={M}: {us:.3f} us/call, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
+    gfloor.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        gfloor.replay()
+    b.record()
+    torch.cuda.synchronize()
+    floor_us = a.elapsed_time(b) * 1e3 / (reps * copies)
+    log(f"[bench] trivial-kernel launch floor in a graph: {floor_us:.3f} us/launch")
+
+    # ---- roofline of the dominant kernel instantiation (largest share of the step's time) ----
+    by_kernel = {}
+    for M in M_SWEEP:
+        k = sweep[str(M)]["kernel"]
+        d = by_kernel.setdefault(k, {"bytes": 0, "us": 0.0, "launches": 0})
+        d["bytes"] += bytes_per_call[M]
+        d["us"] += sweep[str(M)]["us_per_call"]
+        d["launches"] += 1
+    dom = max(by_kernel, key=lambda k: by_kernel[k]["us"])
+    d = by_kernel[dom]
+    achieved = (d["bytes"] / d["launches"]) / (d["us"] / d["launches"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom),
+                "kernel": dom, "avg_launch_us": round(d["us"] / d["launches"], 3),
+                "launch_ms": [m for m in M_SWEEP if sweep[str(m)]["kernel"] == dom]}
+
+    # ---- pages' kernel on the same workload (same hardware): context ratio ----
+    pages_step_us = sum(PAGES_FUSED_US[M] for M in M_SWEEP)
+    pages_gbs = sum(bytes_per_call.values()) / (pages_step_us * 1e-6) / 1e9
+    vs_baseline = round(value / pages_gbs, 3) if (N, K) == (5120, 4096) else None
+
+    # ---- CPU oracle baseline (rank 0, N=1 only), bounded sample ----
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(N, K, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs_baseline,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 in/out",
+        "data": "synthetic (seeded N(0,1) x 2^U(-4,4) per 1x128 group activations; N(0,0.02) weights quantised per 128x128 block)",
+        "config": {"workload": f"fused quant+fp8 block-scale GEMM N={N} K={K}, M sweep {list(M_SWEEP)}, "
+                               f"{copies} cold weight copies rotated in a HIP graph",
+                   "N": N, "K": K, "M": list(M_SWEEP), "weight_copies": copies,
+                   "calls_per_step": copies * len(M_SWEEP), "parallelism": "single GPU"},
+        "sweep": sweep,
+        "launch_floor_us": round(floor_us, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "gpu": torch.cuda.get_device_name(0),
+        "hip": torch.version.hip,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(N, K, target_s):
+    """The oracle as it stands, on the host cores: quant + GEMM of the M sweep on weight copy 0,
+    restricted to a column window sized to roughly `target_s` seconds per leg."""
+    import numpy as np
+
+    import oracle
+    import synthgen
+
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.time()
+    w8, sw = oracle.quant_weight(synthgen.gen_w(N, K, seed=0, copy=0))
+    log(f"[bench] oracle weight quant (untimed) {time.time() - t0:.1f}s")
+    xs = {M: synthgen.gen_x(M, K, seed=0) for M in M_SWEEP}
+
+    def run(ncols, threads):
+        t = time.perf_counter()
+        for M in M_SWEEP:
+            oracle.quant_gemm(xs[M], w8, sw, n0=0, n1=ncols, threads=threads)
+        return time.perf_counter() - t
+
+    def sample_bytes(ncols):
+        return sum(ncols * K + 4 * ((ncols + 127) // 128) * (K // 128) + 2 * M * K + 2 * M * ncols
+                   for M in M_SWEEP)
+
+    legs = {}
+    for name, threads in (("all_cores", cores), ("single_thread", 1)):
+        probe = 128
+        tp = run(probe, threads)
+        ncols = int(min(N, max(128, probe * (target_s / 3) / max(tp, 1e-3))) // 128 * 128)
+        t = float(np.median([run(ncols, threads) for _ in range(3)]))
+        legs[name] = {"GB_s": sample_bytes(ncols) / t / 1e9, "cols": ncols, "seconds": t, "threads": threads}
+        log(f"[bench] oracle {name}: {ncols} columns, {t:.2f}s, {legs[name]['GB_s']:.4f} GB/s")
+    model = ""
+    try:
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True).stdout.splitlines():
+            if line.startswith("Model name"):
+                model = line.split(":", 1)[1].strip()
+    except OSError:
+        model = platform.processor()
+    a = legs["all_cores"]
+    return {"value": round(a["GB_s"], 5), "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
+            "sample": f"quant+GEMM of the M sweep {list(M_SWEEP)} on weight copy 0, output columns "
+                      f"[0, {a['cols']}) of {N} (algorithmic bytes of that window), median of runs",
+            "single_thread": {"value": round(legs["single_thread"]["GB_s"], 5), "cores": 1,
+                              "sample": f"output columns [0, {legs['single_thread']['cols']})"},
+            "cpu_model": model}
+
+
+if __name__ == "__main__":
+    main()

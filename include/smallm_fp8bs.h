@@ -24,7 +24,8 @@
  *  - Activation scales are [M, K/128] row-major (fp32 or e8m0 bytes); weight scales are
  *    [N/128, K/128] row-major, contiguous.
  *  - Shapes: 1 <= M <= SMALLM_FP8BS_MAX_M, N and K positive multiples of 128, else
- *    SMALLM_ERR_SHAPE.  M <= 32 is the design range (decode and verify rows); larger M is
+ *    SMALLM_ERR_SHAPE; the GEMM entries also need 32 activation rows to span less than 2 GiB
+ *    ((31 * ld + K) * element bytes < 2^31).  M <= 32 is the design range (decode and verify rows); larger M is
  *    accepted to locate the crossover with tiled GEMMs.
  *  - Alignment: x, q, w8, w_packed and w must be 16-byte aligned and their row pitches
  *    multiples of 16 bytes; y must be 2-byte aligned; else SMALLM_ERR_ALIGN.
@@ -58,10 +59,13 @@ typedef enum {
 /* Version of this ABI (SMALLM_FP8BS_ABI_VERSION of the header the library was built with). */
 int smallm_fp8bs_abi_version(void);
 
-/* Identifier of the packed weight layout produced by smallm_fp8bs_pack_weight.  The GEMM
- * entry points take it back and refuse weights packed for another layout (the pages' guard
- * only takes the fused path for a weight marked as preshuffled, section Modifications). */
-uint32_t smallm_fp8bs_weight_layout_id(void);
+/* Identifier of the packed layout smallm_fp8bs_pack_weight produces for an [N, K] weight (0 for
+ * an invalid shape).  The layout groups C consecutive weight columns (C = 16, 8, 4 or 2, chosen
+ * from N and K so that the column groups split evenly over the GPU's 256 compute units), and the
+ * id encodes C.  The GEMM entry points take the id back and refuse weights packed for another
+ * layout (the pages' guard only takes the fused path for a weight marked as preshuffled, section
+ * Modifications). */
+uint32_t smallm_fp8bs_weight_layout_id(int N, int K);
 
 /* Static description of a status code.  Never NULL. */
 const char* smallm_fp8bs_strerror(int status);
@@ -69,6 +73,12 @@ const char* smallm_fp8bs_strerror(int status);
 /* Host-only shape check for the fused path: SMALLM_OK if (M, N, K, ldx) is accepted by
  * smallm_fp8bs_quant_gemm, else the status it would return.  Enqueues nothing. */
 int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx);
+
+/* Host-only description of the launch the GEMM entry points make for (M, N, K), for tools and
+ * benchmarks: plan7 receives {C columns per group, column groups per workgroup, workgroups
+ * along N, MFMA waves sharing one column group, weight fragments per MFMA wave per round, K
+ * blocks per round, 16-row M tiles per workgroup}.  Returns SMALLM_OK or the shape error. */
+int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan7);
 
 /* --------------------------------------------------------------------------------------------
  * Load-time weight preparation (not on the per-token path)
@@ -89,10 +99,12 @@ int smallm_fp8bs_quant_weight_e8m0(const float* w, int64_t ldw, uint8_t* w8, uin
                                    int N, int K, void* stream);
 
 /* Permute a row-major e4m3 weight [N, K] (row pitch K) into the library's packed layout
- * (N*K bytes, id smallm_fp8bs_weight_layout_id()).  Each 16-column x 128-K block becomes one
- * contiguous 2 KiB fragment laid out in the lane order of the gfx950 16x16x128 fp8 MFMA B
- * operand, so that one wave reads it with two fully coalesced 16-byte loads per lane.
- * w8 and w_packed must not overlap. */
+ * (N*K bytes, id smallm_fp8bs_weight_layout_id(N, K)).  With C columns per group and S = 16/C,
+ * every (C columns x S K-blocks of 128) piece becomes one contiguous 2 KiB fragment laid out in
+ * the lane order of the B operand of the gfx950 16x16x128 fp8 MFMA (B column j = c*S + s is
+ * column c of the group in K-block s), so that one wave reads it with two fully coalesced
+ * 16-byte loads per lane; the fragments of a column group follow each other along K, and the
+ * column groups follow each other along N.  w8 and w_packed must not overlap. */
 int smallm_fp8bs_pack_weight(const uint8_t* w8, uint8_t* w_packed, int N, int K, void* stream);
 
 /* Inverse of smallm_fp8bs_pack_weight (used by tests). */

@@ -34,6 +34,7 @@ EXPORTS = (
     "smallm_fp8bs_weight_layout_id",
     "smallm_fp8bs_strerror",
     "smallm_fp8bs_supported",
+    "smallm_fp8bs_launch_plan",
     "smallm_fp8bs_quant_weight",
     "smallm_fp8bs_quant_weight_e8m0",
     "smallm_fp8bs_pack_weight",
@@ -86,9 +87,10 @@ def lib():
     P, I, I64, U32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32
     sig = {
         "smallm_fp8bs_abi_version": (I, []),
-        "smallm_fp8bs_weight_layout_id": (U32, []),
+        "smallm_fp8bs_weight_layout_id": (U32, [I, I]),
         "smallm_fp8bs_strerror": (ctypes.c_char_p, [I]),
         "smallm_fp8bs_supported": (I, [I, I, I, I64]),
+        "smallm_fp8bs_launch_plan": (I, [I, I, I, P]),
         "smallm_fp8bs_quant_weight": (I, [P, I64, P, P, I, I, P]),
         "smallm_fp8bs_quant_weight_e8m0": (I, [P, I64, P, P, I, I, P]),
         "smallm_fp8bs_pack_weight": (I, [P, P, I, I, P]),
@@ -116,8 +118,14 @@ def smallm_fp8bs_abi_version() -> int:
     return int(lib().smallm_fp8bs_abi_version())
 
 
-def smallm_fp8bs_weight_layout_id() -> int:
-    return int(lib().smallm_fp8bs_weight_layout_id())
+def smallm_fp8bs_weight_layout_id(N: int, K: int) -> int:
+    """Id of the packed layout smallm_fp8bs_pack_weight produces for an [N, K] weight."""
+    return int(lib().smallm_fp8bs_weight_layout_id(N, K))
+
+
+def layout_columns(N: int, K: int) -> int:
+    """Weight columns per group (C) of the packed layout for an [N, K] weight."""
+    return smallm_fp8bs_weight_layout_id(N, K) & 0xFF
 
 
 def strerror(status: int) -> str:
@@ -129,6 +137,22 @@ smallm_fp8bs_strerror = strerror
 
 def smallm_fp8bs_supported(M: int, N: int, K: int, ldx: int) -> int:
     return int(lib().smallm_fp8bs_supported(M, N, K, ldx))
+
+
+PLAN_FIELDS = ("C", "CGW", "nwg", "WPG", "FPW", "KC", "MT")
+
+
+def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
+    """The launch the GEMM entry points make for (M, N, K) (host-only query)."""
+    buf = (ctypes.c_int * 7)()
+    _check(lib().smallm_fp8bs_launch_plan(M, N, K, ctypes.cast(buf, ctypes.c_void_p)), "smallm_fp8bs_launch_plan")
+    return dict(zip(PLAN_FIELDS, list(buf)))
+
+
+def kernel_name(M: int, N: int, K: int, mode: int = 0) -> str:
+    """Name of the GEMM kernel instantiation (mode 0 fused fp32, 1 fused e8m0, 2/3 pre-quantised)."""
+    p = smallm_fp8bs_launch_plan(M, N, K)
+    return f"smallm_gemm_kernel<{p['MT']}, {p['C']}, {p['FPW']}, {mode}>"
 
 
 # ---------------------------------------------------------------------------------------------
@@ -281,7 +305,7 @@ def smallm_fp8bs_gemm(q, sx, w_packed, sw, y=None, layout_id=None, stream=None):
     N = _check_weight(w_packed, sw, K, False)
     _check_act_scales(sx, M, K, False)
     y = _out(y, M, N, q.device)
-    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_gemm(_ptr(q), q.stride(0), _ptr(sx), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
                                    y.stride(0), M, N, K, _stream(stream)), "smallm_fp8bs_gemm")
     return y
@@ -296,7 +320,7 @@ def smallm_fp8bs_gemm_e8m0(q, sx, w_packed, sw, y=None, layout_id=None, stream=N
     N = _check_weight(w_packed, sw, K, True)
     _check_act_scales(sx, M, K, True)
     y = _out(y, M, N, q.device)
-    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_gemm_e8m0(_ptr(q), q.stride(0), _ptr(sx), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
                                         y.stride(0), M, N, K, _stream(stream)), "smallm_fp8bs_gemm_e8m0")
     return y
@@ -310,7 +334,7 @@ def smallm_fp8bs_quant_gemm(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, la
     M, K = x.shape
     N = _check_weight(w_packed, sw, K, False)
     y = _out(y, M, N, x.device)
-    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_quant_gemm(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
                                          y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
            "smallm_fp8bs_quant_gemm")
@@ -324,7 +348,7 @@ def smallm_fp8bs_quant_gemm_e8m0(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=Non
     M, K = x.shape
     N = _check_weight(w_packed, sw, K, True)
     y = _out(y, M, N, x.device)
-    lid = smallm_fp8bs_weight_layout_id() if layout_id is None else layout_id
+    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_quant_gemm_e8m0(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
                                               y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
            "smallm_fp8bs_quant_gemm_e8m0")

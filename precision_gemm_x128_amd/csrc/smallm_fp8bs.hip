@@ -49,7 +49,6 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kLayoutId = 0x46384231u;  // "1B8F": 16x128 MFMA-B fragments, v1
 constexpr int kThreads = 512;                // 8 waves: 4 quantise, 4 MFMA
 constexpr int kRowStride = 144;              // LDS row pitch of the staged e4m3 rows (128 + 16 pad)
 
@@ -241,17 +240,26 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
 // ---------------------------------------------------------------------------------------------
 // weight (un)packing: one thread per 16-byte chunk of the packed layout
 // ---------------------------------------------------------------------------------------------
+//
+// Packed layout with C weight columns per group (C in {16, 8, 4, 2}, S = 16 / C K-blocks per
+// fragment): fragment f = cg * KG + h (KG = K / (128 S)) holds columns [cg C, cg C + C) and K-blocks
+// [h S, h S + S).  Its 16 MFMA B columns are j = c S + s (column c of the group, K-block s of the
+// fragment).  Lane l = 16 chunk + j of the fragment holds K bytes [32 chunk, 32 chunk + 32) of that
+// column and K-block: bytes 0..15 at l * 16, bytes 16..31 at 1024 + l * 16.
 
-template <bool PACK>
+template <bool PACK, int C>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                    int K, int64_t chunks) {
+  constexpr int S = 16 / C;
   const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (o >= chunks) return;
-  const int KB = K >> 7;
+  const int KG = (K >> 7) / S;
   const int64_t f = o >> 7;
-  const int within = (int)(o & 127), h = within >> 6, lane = within & 63;
-  const int64_t n = (f / KB) * 16 + (lane & 15);
-  const int64_t k = (f % KB) * 128 + (lane >> 4) * 32 + h * 16;
+  const int within = (int)(o & 127), half = within >> 6, lane = within & 63;
+  const int chunk = lane >> 4, j = lane & 15;
+  const int64_t cg = f / KG, h = f % KG;
+  const int64_t n = cg * C + j / S;
+  const int64_t k = (h * S + j % S) * 128 + chunk * 32 + half * 16;
   if (PACK)
     *(u32x4*)(dst + o * 16) = *(const u32x4*)(src + n * K + k);
   else
@@ -296,181 +304,252 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 
 enum Mode { kFusedF32 = 0, kFusedE8 = 1, kPreqF32 = 2, kPreqE8 = 3 };
 
-template <int MT, int NT, int MODE>
+constexpr int kKCMax = 32;      // K blocks staged per round
+constexpr int kMaxMfmaWaves = 12;  // MFMA waves per workgroup (the quantising waves come first)
+constexpr int kMaxQuantWaves = 8;
+
+template <int MT, int C, int FPW, int MODE>
 struct GemmCfg {
   static constexpr bool kE8 = (MODE & 1) != 0;
   static constexpr bool kPreq = (MODE & 2) != 0;
+  static constexpr int kS = 16 / C;                 // K blocks per weight fragment
   static constexpr int kMP = 16 * MT;               // rows per workgroup (M padded to the MFMA)
-  static constexpr int kBPW = (NT <= 2) ? 8 : 4;    // K blocks per MFMA wave per round
-  static constexpr int kKC = 4 * kBPW;              // K blocks per round
-  static constexpr int kStq = kKC * kMP * kRowStride;
-  static constexpr int kSts = kKC * kMP * (kE8 ? 1 : 4);
-  static constexpr int kRed = 4 * MT * NT * 4 * 64 * 4;
+  static constexpr int kStq = kKCMax * kMP * kRowStride;
+  static constexpr int kSts = kKCMax * kMP * (kE8 ? 1 : 4);
+  static constexpr int kRed = kMaxMfmaWaves * MT * 4 * 64 * 4;
   static constexpr int kSmem = ((kStq + kSts) > kRed ? (kStq + kSts) : kRed);
 };
 
-template <int MT, int NT, int MODE>
-__global__ __launch_bounds__(kThreads) void smallm_gemm_kernel(
+// Up to 16 waves per workgroup (4 per SIMD, 128 VGPRs each).
+constexpr int gemm_max_threads(int) { return 1024; }
+
+// One workgroup owns CGW consecutive column groups (C columns each) and all of K; with 256
+// workgroups every CU streams the same number of weight bytes.  The first QW waves quantise (or
+// stage) the activations of a round of K blocks into LDS, two passes of loads in flight per wave.
+// The CGW * WPG MFMA waves follow: MFMA wave
+// w works on column group w / WPG and on part w % WPG of each round's K groups, FPW weight
+// fragments per round at most.  Every weight load is unconditional (a buffer load whose offset
+// points past the workgroup's region when the slot is unused, so the hardware returns zeros
+// without touching memory); the code between the loads and the MFMAs is straight-line, which lets
+// each MFMA wait only for its own fragment.
+//
+// A fragment's S K blocks are S MFMAs chained into one accumulator.  MFMA s must only count in
+// the lanes whose B column belongs to K block s; the other lanes get the B-scale byte 0 (2^-127)
+// for it, so their share is scaled down by 2^-127 (below 2^-127 * 448^2 * 128 of that block's raw
+// dot product) instead of costing a masking operation per MFMA.  In the fp32-scale modes each
+// lane then multiplies the fragment's partial by x_scale * w_scale of its own K block (the pages'
+// 128x128 weight_scale_inv); in the e8m0 modes the scales are the MFMA's own e8m0 scale operands
+// and the accumulator runs over all of K.
+template <int MT, int C, int FPW, int MODE>
+__global__ __launch_bounds__(gemm_max_threads(FPW)) void smallm_gemm_kernel(
     const void* __restrict__ a_src, int64_t lda, const void* __restrict__ sa_src,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
-    int64_t ldy, int M, int K, uint8_t* __restrict__ q_dbg, void* __restrict__ sx_dbg) {
-  using C = GemmCfg<MT, NT, MODE>;
-  constexpr int MP = C::kMP, BPW = C::kBPW, KC = C::kKC;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
+    int64_t ldy, int M, int K, int CGW, int WPG, int QW, uint8_t* __restrict__ q_dbg,
+    void* __restrict__ sx_dbg) {
+  using Cfg = GemmCfg<MT, C, FPW, MODE>;
+  constexpr int S = Cfg::kS, MP = Cfg::kMP;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
   uint8_t* stq = smem;
-  float* sts_f = (float*)(smem + C::kStq);
-  uint8_t* sts_b = smem + C::kStq;
+  float* sts_f = (float*)(smem + Cfg::kStq);
+  uint8_t* sts_b = smem + Cfg::kStq;
   float* red = (float*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K >> 7;
-  const int n0 = blockIdx.x * (NT * 16);
+  const int KG = KB / S;
+  const int KC = FPW * S * WPG;     // K blocks per round
+  const int cg0 = blockIdx.x * CGW;
   const int m0 = blockIdx.y * MP;
   const int Mc = min(M - m0, MP);
+  const int s_l = (lane & 15) % S;  // K block (within a fragment) of this lane's B column
 
-  v4f acc[MT][NT];
+  const int mw = wave - QW;
+  const int cgl = (mw >= 0) ? mw / WPG : 0;
+  const int part = (mw >= 0) ? mw % WPG : 0;
+  const int nb = ((cg0 + cgl) * C) >> 7;  // 128-column block of the wave's column group
+  const uint32_t region = (uint32_t)CGW * (uint32_t)KG * 2048u;
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wp + (int64_t)cg0 * KG * 2048), 0, (int)region, 0x00020000);
+
+  v4f acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[mt][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int rounds = (KB + KC - 1) / KC;
   for (int rd = 0; rd < rounds; ++rd) {
     const int kb0 = rd * KC;
-    const int KBr = min(KC, KB - kb0);
-    if (wave >= 4) {
-      // ---- MFMA waves: stream this round's weight fragments, then multiply ----
-      const int mw = wave - 4;
-      u32x4 wr[NT][BPW][2];
+    const int KCr = min(KC, KB - kb0);
+    if (mw >= 0) {
+      // ---- MFMA waves ----
+      const int KGr = KCr / S;
+      const int kg_lo = part * KGr / WPG;
+      const int cnt = (part + 1) * KGr / WPG - kg_lo;
+      float swv[FPW];
+      int sbl[FPW];
+      u32x4 wr[FPW][2];
+      // block scales first (so that waiting for them never waits for the weight stream)
 #pragma unroll
-      for (int j = 0; j < BPW; ++j) {
-        const int kbl = mw + 4 * j;
-        if (kbl < KBr) {
+      for (int g = 0; g < FPW; ++g) {
+        const int kb = min(kb0 + (kg_lo + g) * S + s_l, KB - 1);
+        if (Cfg::kE8) sbl[g] = (int)((const uint8_t*)sw)[nb * KB + kb];
+        else swv[g] = ((const float*)sw)[nb * KB + kb];
+      }
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const u32x4* p = (const u32x4*)(wp + ((int64_t)(n0 / 16 + t) * KB + kb0 + kbl) * 2048) + lane;
-            wr[t][j][0] = __builtin_nontemporal_load(p);
-            wr[t][j][1] = __builtin_nontemporal_load(p + 64);
-          }
-        }
+      for (int g = 0; g < FPW; ++g) {
+        const uint32_t off = (g < cnt) ? ((uint32_t)(cgl * KG + kb0 / S + kg_lo + g) * 2048u + lane * 16u) : region;
+        wr[g][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 2));
+        wr[g][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 1024u, 0, 2));
       }
       __syncthreads();  // activation bytes and scales of this round are staged
 #pragma unroll
-      for (int j = 0; j < BPW; ++j) {
-        const int kbl = mw + 4 * j;
-        if (kbl < KBr) {
-          const int kb = kb0 + kbl;
+      for (int g = 0; g < FPW; ++g) {
+        const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wr[g][0], wr[g][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        v4f fa[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) fa[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int kbr = min((kg_lo + g) * S + s, KCr - 1);  // K block within the round
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const int row = mt * 16 + (lane & 15);
-            v8i a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            if (row < Mc) {
-              const u32x4* ap = (const u32x4*)(stq + (kbl * MP + row) * kRowStride + (lane >> 4) * 32);
-              const u32x4 a0 = ap[0], a1 = ap[1];
-              a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            }
-            if (C::kE8) {
-              const int sa = (row < Mc) ? (int)sts_b[kbl * MP + row] : 127;
-#pragma unroll
-              for (int t = 0; t < NT; ++t) {
-                const int nb = (n0 + 16 * t) >> 7;
-                const int sb = (int)((const uint8_t*)sw)[nb * KB + kb];
-                const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wr[t][j][0], wr[t][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[mt][t], 0, 0, 0, sa, 0, sb);
-              }
+            const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (lane >> 4) * 32);
+            const u32x4 a0 = ap[0], a1 = ap[1];
+            const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            if (Cfg::kE8) {
+              const int sa = (int)sts_b[kbr * MP + row];
+              const int sb = (S == 1 || s_l == s) ? sbl[g] : 0;
+              acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[mt], 0, 0, 0, sa, 0, sb);
+            } else if (S == 1) {
+              fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 0, 0, 0);
             } else {
-              const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
-#pragma unroll
-              for (int t = 0; t < NT; ++t) {
-                const int nb = (n0 + 16 * t) >> 7;
-                const float swv = ((const float*)sw)[nb * KB + kb];
-                const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wr[t][j][0], wr[t][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mt][t][i] = __builtin_fmaf(sx4[i] * swv, p[i], acc[mt][t][i]);
-              }
+              const int sb = (s_l == s) ? 127 : 0;
+              fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 127, 0, sb);
             }
+          }
+        }
+        if (!Cfg::kE8) {
+          const int kbl = min((kg_lo + g) * S + s_l, KCr - 1);  // this lane's K block within the round
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(sx4[i] * swv[g], fa[mt][i], acc[mt][i]);
           }
         }
       }
       __syncthreads();  // staging buffer free for the next round
     } else {
-      // ---- quantising (or staging) waves: one DPP quad per 1x128 group ----
+      // ---- quantising (or staging) waves: one DPP quad per 1x128 group, two passes in flight ----
+      const int slots = QW * 16;
       const int slot = wave * 16 + (lane >> 2);
       const int c = lane & 3;
-      const int G = Mc * KBr;
-      for (int g0 = 0; g0 < G; g0 += 64) {
-        const int g = g0 + slot;
-        const bool valid = g < G;
-        const int kbl = valid ? g / Mc : 0;
-        const int m = valid ? g % Mc : 0;
-        const int kb = kb0 + kbl;
-        u32x4 qv[2];
-        float s = 0.0f;
-        uint32_t e = 0;
-        if (!C::kPreq) {
-          const u32x4* xp = (const u32x4*)((const uint16_t*)a_src + (int64_t)(m0 + m) * lda + kb * 128 + c * 32);
-          u32x4 xv[4];
+      const int G = Mc * KCr;
+      const int npass = (G + 2 * slots - 1) / (2 * slots) * 2;  // even: the loop body is straight-line
+      constexpr int NV = Cfg::kPreq ? 2 : 4;                    // 16-byte loads per lane per pass
+      const int rowb = Cfg::kPreq ? 1 : 2;                        // bytes per activation element
+      // the workgroup's activation rows as a bounds-checked buffer: idle lanes and passes past the
+      // work use an offset past its end and fetch nothing
+      const uint32_t abytes = (uint32_t)((int64_t)(Mc - 1) * lda * rowb + (int64_t)KB * 128 * rowb);
+      const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const uint8_t*)a_src + (int64_t)m0 * lda * rowb), 0, (int)abytes, 0x00020000);
+      u32x4 xa[4], xb[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) xv[i] = valid ? xp[i] : u32x4{0, 0, 0, 0};
-          if (C::kE8) e = quant32_e8m0(xv, qv);
-          else s = quant32_fp32(xv, qv);
-        } else {
-          const u32x4* qp = (const u32x4*)((const uint8_t*)a_src + (int64_t)(m0 + m) * lda + kb * 128 + c * 32);
-          qv[0] = valid ? qp[0] : u32x4{0, 0, 0, 0};
-          qv[1] = valid ? qp[1] : u32x4{0, 0, 0, 0};
-          if (valid && c == 0) {
-            if (C::kE8) e = ((const uint8_t*)sa_src)[(int64_t)(m0 + m) * KB + kb];
-            else s = ((const float*)sa_src)[(int64_t)(m0 + m) * KB + kb];
+      for (int i = 0; i < 4; ++i) { xa[i] = u32x4{0, 0, 0, 0}; xb[i] = u32x4{0, 0, 0, 0}; }
+#define SMALLM_QLOAD(v, p) do {                                                                   \
+      const int g_ = (p) * slots + slot;                                                         \
+      const uint32_t off_ = (g_ < G) ? (uint32_t)(((int64_t)(g_ % Mc) * lda + (kb0 + g_ / Mc) * 128 + c * 32) * rowb) \
+                                     : abytes;                                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < NV; ++i_)                                          \
+        v[i_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off_ + 16u * i_, 0, 0)); \
+    } while (0)
+#define SMALLM_QPROC(v, p) do {                                                                   \
+      const int g_ = (p) * slots + slot;                                                         \
+      const bool valid_ = g_ < G;                                                                \
+      const int kbl_ = valid_ ? g_ / Mc : 0;                                                     \
+      const int m_ = valid_ ? g_ % Mc : 0;                                                       \
+      u32x4 qv_[2];                                                                              \
+      float s_ = 0.0f;                                                                           \
+      uint32_t e_ = 0;                                                                           \
+      if (!Cfg::kPreq) {                                                                         \
+        if (Cfg::kE8) e_ = quant32_e8m0(v, qv_);                                                 \
+        else s_ = quant32_fp32(v, qv_);                                                          \
+      } else {                                                                                   \
+        qv_[0] = v[0];                                                                           \
+        qv_[1] = v[1];                                                                           \
+      }                                                                                          \
+      if (valid_) {                                                                              \
+        u32x4* dp_ = (u32x4*)(stq + (kbl_ * MP + m_) * kRowStride + c * 32);                    \
+        dp_[0] = qv_[0];                                                                         \
+        dp_[1] = qv_[1];                                                                         \
+        if (c == 0) {                                                                            \
+          if (Cfg::kPreq) {                                                                      \
+            if (Cfg::kE8) sts_b[kbl_ * MP + m_] = ((const uint8_t*)sa_src)[(int64_t)(m0 + m_) * KB + kb0 + kbl_]; \
+            else sts_f[kbl_ * MP + m_] = ((const float*)sa_src)[(int64_t)(m0 + m_) * KB + kb0 + kbl_];           \
+          } else {                                                                               \
+            if (Cfg::kE8) sts_b[kbl_ * MP + m_] = (uint8_t)e_;                                   \
+            else sts_f[kbl_ * MP + m_] = s_;                                                     \
+          }                                                                                      \
+        }                                                                                        \
+      }                                                                                          \
+    } while (0)
+      SMALLM_QLOAD(xa, 0);
+      SMALLM_QLOAD(xb, 1);
+      for (int p = 0; p < npass; p += 2) {
+        SMALLM_QPROC(xa, p);
+        SMALLM_QLOAD(xa, p + 2);
+        SMALLM_QPROC(xb, p + 1);
+        SMALLM_QLOAD(xb, p + 3);
+      }
+#undef SMALLM_QLOAD
+#undef SMALLM_QPROC
+      __syncthreads();  // staged: the MFMA waves read it now
+      if (!Cfg::kPreq && blockIdx.x == 0) {
+        // debug copy of the quantised bytes and scales this round used
+        const int qt = tid;  // 0 .. 64*QW-1
+        if (q_dbg != nullptr) {
+          for (int g = qt; g < Mc * KCr * 8; g += QW * 64) {
+            const int row = g / (KCr * 8), rem = g % (KCr * 8), kbl = rem / 8, part16 = rem % 8;
+            *(u32x4*)(q_dbg + (int64_t)(m0 + row) * K + (kb0 + kbl) * 128 + part16 * 16) =
+                *(const u32x4*)(stq + (kbl * MP + row) * kRowStride + part16 * 16);
           }
         }
-        if (valid) {
-          u32x4* dp = (u32x4*)(stq + (kbl * MP + m) * kRowStride + c * 32);
-          dp[0] = qv[0];
-          dp[1] = qv[1];
-          if (c == 0) {
-            if (C::kE8) sts_b[kbl * MP + m] = (uint8_t)e;
-            else sts_f[kbl * MP + m] = s;
-          }
-          if (!C::kPreq && q_dbg != nullptr && blockIdx.x == 0) {
-            u32x4* qd = (u32x4*)(q_dbg + (int64_t)(m0 + m) * K + kb * 128 + c * 32);
-            qd[0] = qv[0];
-            qd[1] = qv[1];
-          }
-          if (!C::kPreq && sx_dbg != nullptr && blockIdx.x == 0 && c == 0) {
-            if (C::kE8) ((uint8_t*)sx_dbg)[(int64_t)(m0 + m) * KB + kb] = (uint8_t)e;
-            else ((float*)sx_dbg)[(int64_t)(m0 + m) * KB + kb] = s;
+        if (sx_dbg != nullptr) {
+          for (int g = qt; g < Mc * KCr; g += QW * 64) {
+            const int row = g / KCr, kbl = g % KCr;
+            if (Cfg::kE8) ((uint8_t*)sx_dbg)[(int64_t)(m0 + row) * KB + kb0 + kbl] = sts_b[kbl * MP + row];
+            else ((float*)sx_dbg)[(int64_t)(m0 + row) * KB + kb0 + kbl] = sts_f[kbl * MP + row];
           }
         }
       }
       __syncthreads();
-      __syncthreads();
     }
   }
 
-  // ---- cross-wave reduction through LDS (staging space reused), fixed order, bf16 store ----
-  if (wave >= 4) {
-    const int mw = wave - 4;
+  // ---- cross-wave and cross-lane reduction through LDS (staging space reused), fixed order ----
+  if (mw >= 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[(((mw * MT + mt) * NT + t) * 4 + i) * 64 + lane] = acc[mt][t][i];
+      for (int i = 0; i < 4; ++i) red[((mw * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
   }
   __syncthreads();
-  constexpr int NCOL = NT * 16;
-  for (int o = tid; o < MP * NCOL; o += kThreads) {
-    const int row = o / NCOL, col = o % NCOL;
+  const int ncols = CGW * C;
+  const int nthreads = blockDim.x;
+  for (int o = tid; o < MP * ncols; o += nthreads) {
+    const int row = o / ncols, col = o % ncols;
     if (row < Mc) {
-      const int mt = row >> 4, i = row & 3, t = col >> 4;
-      const int l = ((row & 15) >> 2) * 16 + (col & 15);
+      const int cgw = col / C, cc = col % C;
+      const int mt = row >> 4, r = row & 15, i = r & 3;
+      const int lbase = (r >> 2) * 16 + cc * S;
       float sum = 0.0f;
+      for (int p = 0; p < WPG; ++p)
 #pragma unroll
-      for (int mw = 0; mw < 4; ++mw) sum += red[(((mw * MT + mt) * NT + t) * 4 + i) * 64 + l];
-      y[(int64_t)(m0 + row) * ldy + n0 + col] = bf16_rne(sum);
+        for (int s = 0; s < S; ++s) sum += red[(((cgw * WPG + p) * MT + mt) * 4 + i) * 64 + lbase + s];
+      y[(int64_t)(m0 + row) * ldy + (int64_t)(cg0 + cgw) * C + cc] = bf16_rne(sum);
     }
   }
 }
@@ -489,45 +568,87 @@ int check_mnk(int M, int N, int K) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SMALLM_OK : SMALLM_ERR_HIP; }
 
-int tile_override() {
-  static int v = [] {
-    const char* e = getenv("SMALLM_FP8BS_NT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+constexpr int kTargetWGs = 256;  // one workgroup per CU of the MI355X
+
+// MFMA waves that share one column group when a workgroup owns CGW of them.
+int waves_per_group(int CGW) { return CGW >= 3 ? 1 : 4 / CGW; }
+
+// Column groups per workgroup for C-column groups (1 when they do not split evenly over 256).
+int groups_per_wg(int N, int C) {
+  const int CG = N / C;
+  if (CG % kTargetWGs != 0) return 1;
+  int nwg = kTargetWGs, CGW = CG / nwg;
+  while (CGW > kMaxMfmaWaves && CG % (2 * nwg) == 0) { nwg *= 2; CGW = CG / nwg; }
+  return CGW > kMaxMfmaWaves ? 1 : CGW;
 }
 
-// Number of 16-column tiles per workgroup.
-int choose_nt(int N, int M) {
-  const int tiles = N / 16;
-  const int o = tile_override();
-  if ((o == 1 || o == 2 || o == 4) && tiles % o == 0) return o;
-  (void)M;
-  return (tiles % 2 == 0) ? 2 : 1;
+// Columns per group of the packed layout for an [N, K] weight: the widest C whose column-group
+// count is a multiple of 256 (equal weight bytes per CU), whose K-blocks per fragment divide
+// K / 128, and whose rounds fit the 32 staged K blocks; 16 when none is.
+int layout_columns(int N, int K) {
+  const int KB = K / 128;
+  for (int c : {16, 8, 4, 2}) {
+    const int S = 16 / c;
+    if (KB % S != 0 || (N / c) % kTargetWGs != 0) continue;
+    if (S * waves_per_group(groups_per_wg(N, c)) * 4 > kKCMax) continue;
+    return c;
+  }
+  return 16;
+}
+
+uint32_t layout_id_for(int N, int K) { return 0x46380200u | (uint32_t)layout_columns(N, K); }
+
+struct Plan {
+  int C, CGW, nwg, WPG, NWM, FPW, KC, QW;
+};
+
+Plan make_plan(int M, int N, int K) {
+  Plan p;
+  p.C = layout_columns(N, K);
+  const int S = 16 / p.C;
+  const int KG = (K / 128) / S;
+  p.CGW = groups_per_wg(N, p.C);
+  p.nwg = (N / p.C) / p.CGW;
+  p.WPG = waves_per_group(p.CGW);
+  p.NWM = p.CGW * p.WPG;
+  p.FPW = (S * p.WPG * 8 <= kKCMax && KG >= 8 * p.WPG) ? 8 : 4;
+  p.KC = p.FPW * S * p.WPG;
+  // quantising waves: about two 16-group passes each per round, between 2 and 8
+  const int groups = min(M, 32) * min(K / 128, p.KC);
+  p.QW = max(2, min((groups + 31) / 32, min(kMaxQuantWaves, 16 - p.NWM)));
+  return p;
+}
+
+template <int MODE, int MT, int C>
+void launch_c(const Plan& pl, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
+              const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K, uint8_t* q_dbg,
+              void* sx_dbg) {
+  const dim3 block(64 * (pl.QW + pl.NWM));
+  if (pl.FPW == 8)
+    hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, 8, MODE>), grid, block, 0, stream, a, lda, sa, wp, sw, y,
+                       ldy, M, K, pl.CGW, pl.WPG, pl.QW, q_dbg, sx_dbg);
+  else
+    hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, 4, MODE>), grid, block, 0, stream, a, lda, sa, wp, sw, y,
+                       ldy, M, K, pl.CGW, pl.WPG, pl.QW, q_dbg, sx_dbg);
 }
 
 template <int MODE>
 int launch_gemm(const void* a, int64_t lda, const void* sa, const uint8_t* wp, const void* sw,
                 uint16_t* y, int64_t ldy, int M, int N, int K, uint8_t* q_dbg, void* sx_dbg,
                 hipStream_t stream) {
+  const Plan pl = make_plan(M, N, K);
   const int MT = (M <= 16) ? 1 : 2;
-  const int NT = choose_nt(N, M);
   const int MP = 16 * MT;
-  dim3 grid(N / (16 * NT), (M + MP - 1) / MP);
-  dim3 block(kThreads);
-#define SMALLM_LAUNCH(mt, nt)                                                                   \
-  hipLaunchKernelGGL((smallm_gemm_kernel<mt, nt, MODE>), grid, block, 0, stream, a, lda, sa, wp, \
-                     sw, y, ldy, M, K, q_dbg, sx_dbg)
-  if (MT == 1) {
-    if (NT == 1) SMALLM_LAUNCH(1, 1);
-    else if (NT == 2) SMALLM_LAUNCH(1, 2);
-    else SMALLM_LAUNCH(1, 4);
-  } else {
-    if (NT == 1) SMALLM_LAUNCH(2, 1);
-    else if (NT == 2) SMALLM_LAUNCH(2, 2);
-    else SMALLM_LAUNCH(2, 4);
+  dim3 grid(pl.nwg, (M + MP - 1) / MP);
+#define SMALLM_C(mt)                                                                                  \
+  switch (pl.C) {                                                                                     \
+    case 16: launch_c<MODE, mt, 16>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break; \
+    case 8: launch_c<MODE, mt, 8>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break;   \
+    case 4: launch_c<MODE, mt, 4>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break;   \
+    default: launch_c<MODE, mt, 2>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break;  \
   }
-#undef SMALLM_LAUNCH
+  if (MT == 1) { SMALLM_C(1) } else { SMALLM_C(2) }
+#undef SMALLM_C
   return launch_status();
 }
 
@@ -538,10 +659,23 @@ int check_gemm_args(const void* a, int64_t lda, int a_elem_bytes, const void* sa
   int st = check_mnk(M, N, K);
   if (st) return st;
   if (lda < K || ldy < N) return SMALLM_ERR_SHAPE;
+  if ((lda * 31 + K) * a_elem_bytes >= ((int64_t)1 << 31)) return SMALLM_ERR_SHAPE;  // 32-row window
   if (!aligned16(a) || ((lda * a_elem_bytes) & 15) || !aligned16(wp) || ((uintptr_t)y & 1u))
     return SMALLM_ERR_ALIGN;
-  if (layout_id != kLayoutId) return SMALLM_ERR_LAYOUT;
+  if (layout_id != layout_id_for(N, K)) return SMALLM_ERR_LAYOUT;
   return SMALLM_OK;
+}
+
+template <bool PACK>
+void launch_pack(const uint8_t* src, uint8_t* dst, int N, int K, hipStream_t stream) {
+  const int64_t chunks = (int64_t)N * K / 16;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  switch (layout_columns(N, K)) {
+    case 16: hipLaunchKernelGGL((pack_kernel<PACK, 16>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
+    case 8: hipLaunchKernelGGL((pack_kernel<PACK, 8>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
+    case 4: hipLaunchKernelGGL((pack_kernel<PACK, 4>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
+    default: hipLaunchKernelGGL((pack_kernel<PACK, 2>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
+  }
 }
 
 }  // namespace
@@ -550,7 +684,10 @@ extern "C" {
 
 int smallm_fp8bs_abi_version(void) { return SMALLM_FP8BS_ABI_VERSION; }
 
-uint32_t smallm_fp8bs_weight_layout_id(void) { return kLayoutId; }
+uint32_t smallm_fp8bs_weight_layout_id(int N, int K) {
+  if (N <= 0 || K <= 0 || (N & 127) || (K & 127)) return 0;
+  return layout_id_for(N, K);
+}
 
 const char* smallm_fp8bs_strerror(int status) {
   switch (status) {
@@ -558,10 +695,21 @@ const char* smallm_fp8bs_strerror(int status) {
     case SMALLM_ERR_INVALID: return "a required pointer is NULL";
     case SMALLM_ERR_SHAPE: return "shape out of range (1 <= M <= 256, N and K multiples of 128, ld >= row length)";
     case SMALLM_ERR_ALIGN: return "pointer or row pitch not 16-byte aligned";
-    case SMALLM_ERR_LAYOUT: return "packed weight layout id does not match this library";
+    case SMALLM_ERR_LAYOUT: return "packed weight layout id does not match this library and shape";
     case SMALLM_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
+}
+
+int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan7) {
+  if (!plan7) return SMALLM_ERR_INVALID;
+  int st = check_mnk(M, N, K);
+  if (st) return st;
+  const Plan p = make_plan(M, N, K);
+  const int MT = (M <= 16) ? 1 : 2;
+  plan7[0] = p.C; plan7[1] = p.CGW; plan7[2] = p.nwg; plan7[3] = p.WPG;
+  plan7[4] = p.FPW; plan7[5] = p.KC; plan7[6] = MT;
+  return SMALLM_OK;
 }
 
 int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx) {
@@ -596,9 +744,7 @@ int smallm_fp8bs_pack_weight(const uint8_t* w8, uint8_t* w_packed, int N, int K,
   if (!w8 || !w_packed) return SMALLM_ERR_INVALID;
   if (N <= 0 || K <= 0 || (N & 127) || (K & 127)) return SMALLM_ERR_SHAPE;
   if (!aligned16(w8) || !aligned16(w_packed)) return SMALLM_ERR_ALIGN;
-  const int64_t chunks = (int64_t)N * K / 16;
-  hipLaunchKernelGGL((pack_kernel<true>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, w8, w_packed, K, chunks);
+  launch_pack<true>(w8, w_packed, N, K, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -606,9 +752,7 @@ int smallm_fp8bs_unpack_weight(const uint8_t* w_packed, uint8_t* w8, int N, int 
   if (!w8 || !w_packed) return SMALLM_ERR_INVALID;
   if (N <= 0 || K <= 0 || (N & 127) || (K & 127)) return SMALLM_ERR_SHAPE;
   if (!aligned16(w8) || !aligned16(w_packed)) return SMALLM_ERR_ALIGN;
-  const int64_t chunks = (int64_t)N * K / 16;
-  hipLaunchKernelGGL((pack_kernel<false>), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, w_packed, w8, K, chunks);
+  launch_pack<false>(w_packed, w8, N, K, (hipStream_t)stream);
   return launch_status();
 }
 

@@ -30,9 +30,33 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}\b", out), name
 
 
+def test_launch_plans_balance_the_cus():
+    # every CU streams the same weight bytes on the pages' shapes
+    for (N, K), (C, CGW) in {(5120, 4096): (4, 5), (4608, 4096): (2, 9), (4096, 2048): (16, 1),
+                             (2048, 4096): (8, 1)}.items():
+        p = P.smallm_fp8bs_launch_plan(16, N, K)
+        assert (p["C"], p["CGW"], p["nwg"]) == (C, CGW, 256)
+        assert p["CGW"] * p["WPG"] == 4 or p["WPG"] == 1
+    assert P.smallm_fp8bs_launch_plan(17, 4096, 2048)["MT"] == 2
+    assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["MT"] == 1
+    p = P.smallm_fp8bs_launch_plan(4, 36864, 128)
+    assert (p["CGW"], p["FPW"], p["WPG"]) == (9, 4, 1)
+    p = P.smallm_fp8bs_launch_plan(4, 5120, 4096)
+    assert (p["FPW"], p["KC"]) == (8, 32)
+    assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 4, 8, 0>"
+    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 2, 4, 0>"
+
+
 def test_version_layout_and_strerror():
     assert P.smallm_fp8bs_abi_version() == 1
-    assert P.smallm_fp8bs_weight_layout_id() == 0x46384231
+    # columns per group: the widest C in {16, 8, 4, 2} giving a multiple of 256 column groups
+    assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46380210
+    assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46380204
+    assert P.smallm_fp8bs_weight_layout_id(4608, 4096) == 0x46380202
+    assert P.smallm_fp8bs_weight_layout_id(2048, 4096) == 0x46380208
+    assert P.smallm_fp8bs_weight_layout_id(384, 640) == 0x46380210
+    assert P.smallm_fp8bs_weight_layout_id(4608, 640) == 0x46380210   # 5 K-blocks: only C=16 fits
+    assert P.smallm_fp8bs_weight_layout_id(100, 128) == 0
     for s in range(6):
         assert len(P.strerror(s)) > 0
     assert P.strerror(99) == "unknown status"
@@ -55,7 +79,7 @@ def _fake(addr=0x10000):
 def test_rejections_happen_before_any_launch():
     """Invalid arguments are refused on the host; these calls never reach HIP (no GPU here)."""
     L = P.lib()
-    lid = P.smallm_fp8bs_weight_layout_id()
+    lid = P.smallm_fp8bs_weight_layout_id(4096, 2048)
     f = _fake()
     # null pointers
     assert L.smallm_fp8bs_quant_gemm(None, 2048, f, lid, f, f, 4096, 4, 4096, 2048, None, None, None) == 1
@@ -83,6 +107,9 @@ def test_rejections_happen_before_any_launch():
     # layout id
     assert L.smallm_fp8bs_quant_gemm(f, 2048, f, lid ^ 1, f, f, 4096, 4, 4096, 2048, None, None, None) == 4
     assert L.smallm_fp8bs_gemm_e8m0(f, 2048, f, f, 0, f, f, 4096, 4, 4096, 2048, None) == 4
+    # a weight packed for another shape's layout is refused
+    lid5120 = P.smallm_fp8bs_weight_layout_id(5120, 4096)
+    assert L.smallm_fp8bs_quant_gemm(f, 4096, f, lid5120, f, f, 4608, 4, 4608, 4096, None, None, None) == 4
 
 
 def test_binding_rejects_wrong_dtypes_without_gpu():

@@ -102,10 +102,10 @@ def test_quant_weight_bitexact(e8m0):
                           sw_ref.view(np.uint8 if e8m0 else np.uint32))
 
 
-def test_pack_unpack_roundtrip_and_fragment_order():
-    note("pack/unpack")
-    N, K = 256, 384
-    rng = np.random.default_rng(0)
+@pytest.mark.parametrize("N,K", [(256, 384), (4096, 2048), (5120, 512), (4608, 1024), (2048, 512)])
+def test_pack_unpack_roundtrip_and_fragment_order(N, K):
+    note(f"pack/unpack N={N} K={K}")
+    rng = np.random.default_rng(N + K)
     w8 = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
     wd = to_dev(w8)
     wp = P.smallm_fp8bs_pack_weight(wd)
@@ -114,14 +114,20 @@ def test_pack_unpack_roundtrip_and_fragment_order():
     assert np.array_equal(back.cpu().numpy(), w8)
     packed = wp.cpu().numpy().reshape(-1)
     assert np.array_equal(np.sort(packed), np.sort(w8.reshape(-1)))
-    # fragment (n-tile 1, k-block 2): lane 16*c + j holds column 16 + j, K bytes 256 + 32c + [0, 32)
-    KB = K // 128
-    frag = packed[(1 * KB + 2) * 2048:(1 * KB + 2) * 2048 + 2048]
-    for c in range(4):
-        for j in (0, 7, 15):
-            lane = 16 * c + j
-            got = np.r_[frag[lane * 16:lane * 16 + 16], frag[1024 + lane * 16:1024 + lane * 16 + 16]]
-            assert np.array_equal(got, w8[16 + j, 256 + 32 * c:256 + 32 * c + 32])
+    # fragment f = cg * KG + h: lane 16*chunk + j holds column cg*C + j//S, K block h*S + j%S,
+    # bytes [32 chunk, 32 chunk + 32) of it (first 16 at lane*16, next 16 at 1024 + lane*16)
+    C = P.layout_columns(N, K)
+    S = 16 // C
+    KG = K // 128 // S
+    for cg, h in ((0, 0), (1, KG - 1), (N // C - 1, KG // 2)):
+        f = cg * KG + h
+        frag = packed[f * 2048:(f + 1) * 2048]
+        for chunk in range(4):
+            for j in (0, 5, 15):
+                lane = 16 * chunk + j
+                got = np.r_[frag[lane * 16:lane * 16 + 16], frag[1024 + lane * 16:1024 + lane * 16 + 16]]
+                k0 = (h * S + j % S) * 128 + 32 * chunk
+                assert np.array_equal(got, w8[cg * C + j // S, k0:k0 + 32])
 
 
 # ---------------------------------------------------------------------------------------------
@@ -242,6 +248,27 @@ def test_fused_full_shapes_all_m(N, K, e8m0):
     for M in M_LIST:
         note(f"fused full N={N} K={K} M={M} e8m0={e8m0}")
         x = synthgen.gen_x(M, K, seed=M, outliers=(M % 2 == 1))
+        _, _, ref = oracle_ref(x, w8, sw, e8m0, ranges)
+        y = fn(to_dev_bf16(x), wp, swd)
+        torch.cuda.synchronize()
+        assert_within_tol(y, ref, cols, what=f"N={N} K={K} M={M} e8m0={e8m0}")
+
+
+# Shapes that exercise every work split of the launch plan: column groups of C = 16, 8, 4, 2
+# columns; 1, 2, 3, 5, 9 and 12 column groups per workgroup; K shared by 4, 2 or 1 MFMA waves.
+PLAN_SHAPES = [(8192, 256), (12288, 256), (6144, 1024), (5120, 512), (4608, 1024), (2048, 512),
+               (36864, 128), (49152, 256)]
+
+
+@pytest.mark.parametrize("N,K", PLAN_SHAPES)
+@pytest.mark.parametrize("e8m0", [False, True])
+def test_fused_launch_plans(N, K, e8m0):
+    w8, sw, wp, swd = prepared_weight(N, K, seed=11, e8m0=e8m0)
+    cols, ranges = windows(N, 384)
+    fn = P.smallm_fp8bs_quant_gemm_e8m0 if e8m0 else P.smallm_fp8bs_quant_gemm
+    for M in (1, 7, 16, 32):
+        note(f"plan N={N} K={K} C={P.layout_columns(N, K)} M={M} e8m0={e8m0}")
+        x = special_x(M, K, seed=M + N) if K >= 512 else synthgen.gen_x(M, K, seed=M + N)
         _, _, ref = oracle_ref(x, w8, sw, e8m0, ranges)
         y = fn(to_dev_bf16(x), wp, swd)
         torch.cuda.synchronize()
