@@ -48,12 +48,13 @@ def source_hash():
 
 
 def load_traffic(kname):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_fused_5120x4096.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's counts), if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "fused_quant_gemm_5120x4096_traffic.md")
     try:
-        d = json.load(open(path))
-    except (OSError, ValueError):
+        text = open(path).read()
+        d = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, ValueError, IndexError):
         return None
     if d.get("source_hash") != source_hash():
         return None
@@ -71,6 +72,10 @@ def main():
     ap.add_argument("--K", type=int, default=K_DEFAULT)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="target seconds per CPU leg")
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per M for the per-M breakdown")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times): the "
+                         "reference kernel for scaling HBM byte counters, then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -86,6 +91,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     dev = torch.device("cuda:0")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.calib_copy_mib} MiB three times")
+        return
     N, K, copies = args.N, args.K, args.copies
     P.lib()
 
@@ -154,7 +169,7 @@ def main():
     value = step_bytes / (step_ms * 1e-3) / 1e9
 
     # ---- per-M breakdown (each M's graph timed on its own, same stream) ----
-    reps = max(args.steps, 20)
+    reps = max(1, args.reps)
     sweep = {}
     for M in M_SWEEP:
         graphs[M].replay()
@@ -220,11 +235,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": vs_baseline,
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 in/out",
+        "dtype": "fp8e4m3",
         "data": "synthetic (seeded N(0,1) x 2^U(-4,4) per 1x128 group activations; N(0,0.02) weights quantised per 128x128 block)",
         "config": {"workload": f"fused quant+fp8 block-scale GEMM N={N} K={K}, M sweep {list(M_SWEEP)}, "
                                f"{copies} cold weight copies rotated in a HIP graph",
                    "N": N, "K": K, "M": list(M_SWEEP), "weight_copies": copies,
+                   "arithmetic": "e4m3 x e4m3 products, fp32 accumulation, bf16 activations in, bf16 out",
                    "calls_per_step": copies * len(M_SWEEP), "parallelism": "single GPU"},
         "sweep": sweep,
         "launch_floor_us": round(floor_us, 3),
