@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SMALLM_FP8BS_ABI_VERSION 1
+#define SMALLM_FP8BS_ABI_VERSION 2
 #define SMALLM_FP8BS_MAX_M 256
 
 typedef enum {
@@ -75,10 +75,13 @@ const char* smallm_fp8bs_strerror(int status);
 int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx);
 
 /* Host-only description of the launch the GEMM entry points make for (M, N, K), for tools and
- * benchmarks: plan7 receives {C columns per group, column groups per workgroup, workgroups
- * along N, MFMA waves sharing one column group, weight fragments per MFMA wave per round, K
- * blocks per round, 16-row M tiles per workgroup}.  Returns SMALLM_OK or the shape error. */
-int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan7);
+ * benchmarks.  plan10 receives, in order: C (columns per group), CGW (column groups per
+ * workgroup), the number of workgroups along N, NWK and NWC (the MFMA waves form an NWK x NWC
+ * grid: NWK waves split each round's K groups, NWC waves split the column groups), NCG (column
+ * groups per MFMA wave, which share one read of each activation tile), NKG (K groups per MFMA
+ * wave per round), KC (K blocks per round), QW (quantising waves) and MT (16-row M tiles per
+ * workgroup).  Returns SMALLM_OK or the shape error. */
+int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan10);
 
 /* --------------------------------------------------------------------------------------------
  * Load-time weight preparation (not on the per-token path)

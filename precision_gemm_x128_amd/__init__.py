@@ -139,12 +139,12 @@ def smallm_fp8bs_supported(M: int, N: int, K: int, ldx: int) -> int:
     return int(lib().smallm_fp8bs_supported(M, N, K, ldx))
 
 
-PLAN_FIELDS = ("C", "CGW", "nwg", "WPG", "FPW", "KC", "MT")
+PLAN_FIELDS = ("C", "CGW", "nwg", "NWK", "NWC", "NCG", "NKG", "KC", "QW", "MT")
 
 
 def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
     """The launch the GEMM entry points make for (M, N, K) (host-only query)."""
-    buf = (ctypes.c_int * 7)()
+    buf = (ctypes.c_int * len(PLAN_FIELDS))()
     _check(lib().smallm_fp8bs_launch_plan(M, N, K, ctypes.cast(buf, ctypes.c_void_p)), "smallm_fp8bs_launch_plan")
     return dict(zip(PLAN_FIELDS, list(buf)))
 
@@ -152,7 +152,7 @@ def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
 def kernel_name(M: int, N: int, K: int, mode: int = 0) -> str:
     """Name of the GEMM kernel instantiation (mode 0 fused fp32, 1 fused e8m0, 2/3 pre-quantised)."""
     p = smallm_fp8bs_launch_plan(M, N, K)
-    return f"smallm_gemm_kernel<{p['MT']}, {p['C']}, {p['FPW']}, {mode}>"
+    return f"smallm_gemm_kernel<{p['MT']}, {p['C']}, {p['NCG']}, {p['NKG']}, {mode}>"
 
 
 # ---------------------------------------------------------------------------------------------

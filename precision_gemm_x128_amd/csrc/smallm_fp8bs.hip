@@ -68,6 +68,16 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   return v;
 }
 
+// Sum over the S consecutive lanes (S = 1, 2, 4 or 8, aligned) that hold one output column's K
+// blocks; every one of the S lanes gets the same total.
+template <int S>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if (S >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if (S >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (S >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -308,7 +318,7 @@ constexpr int kKCMax = 32;      // K blocks staged per round
 constexpr int kMaxMfmaWaves = 12;  // MFMA waves per workgroup (the quantising waves come first)
 constexpr int kMaxQuantWaves = 8;
 
-template <int MT, int C, int FPW, int MODE>
+template <int MT, int C, int NCG, int NKG, int MODE>
 struct GemmCfg {
   static constexpr bool kE8 = (MODE & 1) != 0;
   static constexpr bool kPreq = (MODE & 2) != 0;
@@ -316,20 +326,19 @@ struct GemmCfg {
   static constexpr int kMP = 16 * MT;               // rows per workgroup (M padded to the MFMA)
   static constexpr int kStq = kKCMax * kMP * kRowStride;
   static constexpr int kSts = kKCMax * kMP * (kE8 ? 1 : 4);
-  static constexpr int kRed = kMaxMfmaWaves * MT * 4 * 64 * 4;
+  static constexpr int kRed = kMaxMfmaWaves * NCG * MT * 4 * 64 * 4;
   static constexpr int kSmem = ((kStq + kSts) > kRed ? (kStq + kSts) : kRed);
 };
-
-// Up to 16 waves per workgroup (4 per SIMD, 128 VGPRs each).
-constexpr int gemm_max_threads(int) { return 1024; }
 
 // One workgroup owns CGW consecutive column groups (C columns each) and all of K; with 256
 // workgroups every CU streams the same number of weight bytes.  The first QW waves quantise (or
 // stage) the activations of a round of K blocks into LDS, two passes of loads in flight per wave.
-// The CGW * WPG MFMA waves follow: MFMA wave
-// w works on column group w / WPG and on part w % WPG of each round's K groups, FPW weight
-// fragments per round at most.  Every weight load is unconditional (a buffer load whose offset
-// points past the workgroup's region when the slot is unused, so the hardware returns zeros
+// The NWK * NWC MFMA waves follow.  MFMA wave (kq, cq) = (w % NWK, w / NWK) owns the column
+// groups cq, cq + NWC, ... (NCG at most) and, in every round, part kq of NWK contiguous parts of
+// that round's K groups (NKG at most): it reads each staged activation tile of its K groups once and
+// multiplies it into the weight fragments of all its column groups, so the activation bytes cross
+// the LDS once per NCG column groups.  Every weight load is unconditional (a buffer load whose
+// offset points past the workgroup's region when the slot is unused, so the hardware returns zeros
 // without touching memory); the code between the loads and the MFMAs is straight-line, which lets
 // each MFMA wait only for its own fragment.
 //
@@ -340,13 +349,13 @@ constexpr int gemm_max_threads(int) { return 1024; }
 // lane then multiplies the fragment's partial by x_scale * w_scale of its own K block (the pages'
 // 128x128 weight_scale_inv); in the e8m0 modes the scales are the MFMA's own e8m0 scale operands
 // and the accumulator runs over all of K.
-template <int MT, int C, int FPW, int MODE>
-__global__ __launch_bounds__(gemm_max_threads(FPW)) void smallm_gemm_kernel(
+template <int MT, int C, int NCG, int NKG, int MODE>
+__global__ __launch_bounds__(1024) void smallm_gemm_kernel(
     const void* __restrict__ a_src, int64_t lda, const void* __restrict__ sa_src,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
-    int64_t ldy, int M, int K, int CGW, int WPG, int QW, uint8_t* __restrict__ q_dbg,
+    int64_t ldy, int M, int K, int CGW, int NWK, int NWC, int QW, uint8_t* __restrict__ q_dbg,
     void* __restrict__ sx_dbg) {
-  using Cfg = GemmCfg<MT, C, FPW, MODE>;
+  using Cfg = GemmCfg<MT, C, NCG, NKG, MODE>;
   constexpr int S = Cfg::kS, MP = Cfg::kMP;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
   uint8_t* stq = smem;
@@ -359,23 +368,24 @@ __global__ __launch_bounds__(gemm_max_threads(FPW)) void smallm_gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K >> 7;
   const int KG = KB / S;
-  const int KC = FPW * S * WPG;     // K blocks per round
+  const int KC = NKG * NWK * S;     // K blocks per round
   const int cg0 = blockIdx.x * CGW;
   const int m0 = blockIdx.y * MP;
   const int Mc = min(M - m0, MP);
   const int s_l = (lane & 15) % S;  // K block (within a fragment) of this lane's B column
 
   const int mw = wave - QW;
-  const int cgl = (mw >= 0) ? mw / WPG : 0;
-  const int part = (mw >= 0) ? mw % WPG : 0;
-  const int nb = ((cg0 + cgl) * C) >> 7;  // 128-column block of the wave's column group
+  const int kq = (mw >= 0) ? mw % NWK : 0;
+  const int cq = (mw >= 0) ? mw / NWK : 0;
   const uint32_t region = (uint32_t)CGW * (uint32_t)KG * 2048u;
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(wp + (int64_t)cg0 * KG * 2048), 0, (int)region, 0x00020000);
 
-  v4f acc[MT];
+  v4f acc[NCG][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NCG; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int rounds = (KB + KC - 1) / KC;
   for (int rd = 0; rd < rounds; ++rd) {
@@ -384,60 +394,121 @@ __global__ __launch_bounds__(gemm_max_threads(FPW)) void smallm_gemm_kernel(
     if (mw >= 0) {
       // ---- MFMA waves ----
       const int KGr = KCr / S;
-      const int kg_lo = part * KGr / WPG;
-      const int cnt = (part + 1) * KGr / WPG - kg_lo;
-      float swv[FPW];
-      int sbl[FPW];
-      u32x4 wr[FPW][2];
+      // this wave's K groups of the round: a contiguous share [kg_lo, kg_lo + nkg)
+      const int kg_lo = kq * KGr / NWK;
+      const int nkg = (kq + 1) * KGr / NWK - kg_lo;
+      float swv[NKG][NCG];
+      int sbl[NKG][NCG];
+      u32x4 wr[NKG][NCG][2];
       // block scales first (so that waiting for them never waits for the weight stream)
 #pragma unroll
-      for (int g = 0; g < FPW; ++g) {
-        const int kb = min(kb0 + (kg_lo + g) * S + s_l, KB - 1);
-        if (Cfg::kE8) sbl[g] = (int)((const uint8_t*)sw)[nb * KB + kb];
-        else swv[g] = ((const float*)sw)[nb * KB + kb];
-      }
+      for (int i = 0; i < NKG; ++i)
 #pragma unroll
-      for (int g = 0; g < FPW; ++g) {
-        const uint32_t off = (g < cnt) ? ((uint32_t)(cgl * KG + kb0 / S + kg_lo + g) * 2048u + lane * 16u) : region;
-        wr[g][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 2));
-        wr[g][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 1024u, 0, 2));
-      }
+        for (int j = 0; j < NCG; ++j) {
+          const int cg = min(cq + j * NWC, CGW - 1);
+          const int nb = ((cg0 + cg) * C) >> 7;  // 128-column block of the column group
+          const int kb = min(kb0 + (kg_lo + i) * S + s_l, KB - 1);
+          if (Cfg::kE8) sbl[i][j] = (int)((const uint8_t*)sw)[nb * KB + kb];
+          else swv[i][j] = ((const float*)sw)[nb * KB + kb];
+        }
+#pragma unroll
+      for (int i = 0; i < NKG; ++i)
+#pragma unroll
+        for (int j = 0; j < NCG; ++j) {
+          const int cg = cq + j * NWC;
+          const uint32_t off = (i < nkg && cg < CGW)
+                                   ? ((uint32_t)(cg * KG + kb0 / S + kg_lo + i) * 2048u + lane * 16u)
+                                   : region;
+          wr[i][j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 2));
+          wr[i][j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 1024u, 0, 2));
+        }
       __syncthreads();  // activation bytes and scales of this round are staged
 #pragma unroll
-      for (int g = 0; g < FPW; ++g) {
-        const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wr[g][0], wr[g][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        v4f fa[MT];
+      for (int i = 0; i < NKG; ++i) {
+        // K group within the round; a slot past the wave's share has zero weights and reads a
+        // staged tile (finite bytes), so its products are exactly zero
+        const int kgr = min(kg_lo + i, KGr - 1);
+        if constexpr (NCG == 1) {
+          // one column group: each activation tile is read right before its MFMA
+          const v8i b = __builtin_bit_cast(
+              v8i, __builtin_shufflevector(wr[i][0][0], wr[i][0][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          v4f fa[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) fa[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int mt = 0; mt < MT; ++mt) fa[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int kbr = min((kg_lo + g) * S + s, KCr - 1);  // K block within the round
+          for (int s = 0; s < S; ++s) {
+            const int kbr = kgr * S + s;  // K block within the round
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int row = mt * 16 + (lane & 15);
-            const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (lane >> 4) * 32);
-            const u32x4 a0 = ap[0], a1 = ap[1];
-            const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            if (Cfg::kE8) {
-              const int sa = (int)sts_b[kbr * MP + row];
-              const int sb = (S == 1 || s_l == s) ? sbl[g] : 0;
-              acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[mt], 0, 0, 0, sa, 0, sb);
-            } else if (S == 1) {
-              fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 0, 0, 0);
-            } else {
-              const int sb = (s_l == s) ? 127 : 0;
-              fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 127, 0, sb);
+            for (int mt = 0; mt < MT; ++mt) {
+              const int row = mt * 16 + (lane & 15);
+              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (lane >> 4) * 32);
+              const u32x4 a0 = ap[0], a1 = ap[1];
+              const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+              if (Cfg::kE8) {
+                const int sa = (int)sts_b[kbr * MP + row];
+                const int sb = (S == 1 || s_l == s) ? sbl[i][0] : 0;
+                acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[0][mt], 0, 0, 0, sa, 0, sb);
+              } else if (S == 1) {
+                fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 0, 0, 0);
+              } else {
+                const int sb = (s_l == s) ? 127 : 0;
+                fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 127, 0, sb);
+              }
             }
           }
-        }
-        if (!Cfg::kE8) {
-          const int kbl = min((kg_lo + g) * S + s_l, KCr - 1);  // this lane's K block within the round
+          if (!Cfg::kE8) {
+            const int kbl = kgr * S + s_l;  // this lane's K block within the round
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[0][mt][e] = __builtin_fmaf(sx4[e] * swv[i][0], fa[mt][e], acc[0][mt][e]);
+            }
+          }
+        } else {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
+            // the K group's S activation tiles, read from LDS once for all NCG column groups
+            const int row = mt * 16 + (lane & 15);
+            v8i a[S];
+            int sa[S];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(sx4[i] * swv[g], fa[mt][i], acc[mt][i]);
+            for (int s = 0; s < S; ++s) {
+              const int kbr = kgr * S + s;  // K block within the round
+              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (lane >> 4) * 32);
+              const u32x4 a0 = ap[0], a1 = ap[1];
+              a[s] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+              sa[s] = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
+            }
+            v4f sx4 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            if (!Cfg::kE8) {
+              const int kbl = kgr * S + s_l;  // this lane's K block within the round
+              sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
+            }
+            // fragment by fragment, so that each one is consumed as soon as its loads land
+#pragma unroll
+            for (int j = 0; j < NCG; ++j) {
+              const v8i b = __builtin_bit_cast(
+                  v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+              v4f fa = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int s = 0; s < S; ++s) {
+                if (Cfg::kE8) {
+                  const int sb = (S == 1 || s_l == s) ? sbl[i][j] : 0;
+                  acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b, acc[j][mt], 0, 0, 0, sa[s], 0, sb);
+                } else if (S == 1) {
+                  fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b, fa, 0, 0, 0, 0, 0, 0);
+                } else {
+                  const int sb = (s_l == s) ? 127 : 0;
+                  fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b, fa, 0, 0, 0, 127, 0, sb);
+                }
+              }
+              if (!Cfg::kE8) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[e], acc[j][mt][e]);
+              }
+            }
           }
         }
       }
@@ -529,12 +600,16 @@ __global__ __launch_bounds__(gemm_max_threads(FPW)) void smallm_gemm_kernel(
     }
   }
 
-  // ---- cross-wave and cross-lane reduction through LDS (staging space reused), fixed order ----
+  // ---- reduction, fixed order: the S K-block lanes of a column in registers, then the NWK waves
+  // that split K through LDS (staging space reused) ----
   if (mw >= 0) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int j = 0; j < NCG; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[((mw * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          red[(((mw * NCG + j) * MT + mt) * 4 + e) * 64 + lane] = lane_group_sum<S>(acc[j][mt][e]);
   }
   __syncthreads();
   const int ncols = CGW * C;
@@ -543,12 +618,17 @@ __global__ __launch_bounds__(gemm_max_threads(FPW)) void smallm_gemm_kernel(
     const int row = o / ncols, col = o % ncols;
     if (row < Mc) {
       const int cgw = col / C, cc = col % C;
-      const int mt = row >> 4, r = row & 15, i = r & 3;
-      const int lbase = (r >> 2) * 16 + cc * S;
-      float sum = 0.0f;
-      for (int p = 0; p < WPG; ++p)
+      const int cqo = cgw % NWC, j = cgw / NWC;
+      const int mt = row >> 4, r = row & 15, e = r & 3;
+      const float* rp = red + (((cqo * NWK * NCG + j) * MT + mt) * 4 + e) * 64 + (r >> 2) * 16 + cc * S;
+      const int kstride = NCG * MT * 4 * 64;  // floats between the partials of consecutive K parts
+      float part[kMaxMfmaWaves];
 #pragma unroll
-        for (int s = 0; s < S; ++s) sum += red[(((cgw * WPG + p) * MT + mt) * 4 + i) * 64 + lbase + s];
+      for (int k = 0; k < kMaxMfmaWaves; ++k) part[k] = (k < NWK) ? rp[k * kstride] : 0.0f;
+      float sum = part[0];
+#pragma unroll
+      for (int k = 1; k < kMaxMfmaWaves; ++k)
+        if (k < NWK) sum += part[k];
       y[(int64_t)(m0 + row) * ldy + (int64_t)(cg0 + cgw) * C + cc] = bf16_rne(sum);
     }
   }
@@ -599,7 +679,7 @@ int layout_columns(int N, int K) {
 uint32_t layout_id_for(int N, int K) { return 0x46380200u | (uint32_t)layout_columns(N, K); }
 
 struct Plan {
-  int C, CGW, nwg, WPG, NWM, FPW, KC, QW;
+  int C, CGW, nwg, NWK, NWC, NCG, NKG, NWM, KC, QW;
 };
 
 Plan make_plan(int M, int N, int K) {
@@ -609,10 +689,30 @@ Plan make_plan(int M, int N, int K) {
   const int KG = (K / 128) / S;
   p.CGW = groups_per_wg(N, p.C);
   p.nwg = (N / p.C) / p.CGW;
-  p.WPG = waves_per_group(p.CGW);
-  p.NWM = p.CGW * p.WPG;
-  p.FPW = (S * p.WPG * 8 <= kKCMax && KG >= 8 * p.WPG) ? 8 : 4;
-  p.KC = p.FPW * S * p.WPG;
+  // One M tile: waves that share their activation tiles between NCG = 5 or 3 column groups, one
+  // K group per wave and round, when that still gives at least 4 MFMA waves; else (and for two M
+  // tiles, whose accumulators would not fit) one column group per wave.  NWK is the largest
+  // divisor of the K groups that fits, so that every round is full.
+  p.NCG = 0;
+  for (int ncg : {5, 3}) {
+    if (M > 16 || p.CGW % ncg != 0 || ncg * 8 + S * 8 + ncg * 4 > 100) continue;  // registers
+    const int nwc = p.CGW / ncg;
+    const int cap = min(kMaxMfmaWaves / nwc, kKCMax / S);
+    int nwk = 0;
+    for (int d = 1; d <= cap; ++d)
+      if (KG % d == 0) nwk = d;
+    if (nwk * nwc < 4) continue;
+    p.NCG = ncg; p.NKG = 1; p.NWC = nwc; p.NWK = nwk;
+    break;
+  }
+  if (p.NCG == 0) {
+    p.NCG = 1;
+    p.NWC = p.CGW;
+    p.NWK = waves_per_group(p.CGW);
+    p.NKG = (S * p.NWK * 8 <= kKCMax && KG >= 8 * p.NWK) ? 8 : 4;
+  }
+  p.NWM = p.NWK * p.NWC;
+  p.KC = p.NKG * p.NWK * S;
   // quantising waves: about two 16-group passes each per round, between 2 and 8
   const int groups = min(M, 32) * min(K / 128, p.KC);
   p.QW = max(2, min((groups + 31) / 32, min(kMaxQuantWaves, 16 - p.NWM)));
@@ -624,12 +724,18 @@ void launch_c(const Plan& pl, dim3 grid, hipStream_t stream, const void* a, int6
               const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K, uint8_t* q_dbg,
               void* sx_dbg) {
   const dim3 block(64 * (pl.QW + pl.NWM));
-  if (pl.FPW == 8)
-    hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, 8, MODE>), grid, block, 0, stream, a, lda, sa, wp, sw, y,
-                       ldy, M, K, pl.CGW, pl.WPG, pl.QW, q_dbg, sx_dbg);
-  else
-    hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, 4, MODE>), grid, block, 0, stream, a, lda, sa, wp, sw, y,
-                       ldy, M, K, pl.CGW, pl.WPG, pl.QW, q_dbg, sx_dbg);
+#define SMALLM_LAUNCH(ncg, nkg)                                                                          \
+  hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, ncg, nkg, MODE>), grid, block, 0, stream, a, lda, sa, wp, \
+                     sw, y, ldy, M, K, pl.CGW, pl.NWK, pl.NWC, pl.QW, q_dbg, sx_dbg)
+  if constexpr (MT == 1 && C != 2) {
+    if (pl.NCG == 5) { SMALLM_LAUNCH(5, 1); return; }
+  }
+  if constexpr (MT == 1) {
+    if (pl.NCG == 3) { SMALLM_LAUNCH(3, 1); return; }
+  }
+  if (pl.NKG == 8) SMALLM_LAUNCH(1, 8);
+  else SMALLM_LAUNCH(1, 4);
+#undef SMALLM_LAUNCH
 }
 
 template <int MODE>
@@ -701,14 +807,14 @@ const char* smallm_fp8bs_strerror(int status) {
   }
 }
 
-int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan7) {
-  if (!plan7) return SMALLM_ERR_INVALID;
+int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan10) {
+  if (!plan10) return SMALLM_ERR_INVALID;
   int st = check_mnk(M, N, K);
   if (st) return st;
   const Plan p = make_plan(M, N, K);
   const int MT = (M <= 16) ? 1 : 2;
-  plan7[0] = p.C; plan7[1] = p.CGW; plan7[2] = p.nwg; plan7[3] = p.WPG;
-  plan7[4] = p.FPW; plan7[5] = p.KC; plan7[6] = MT;
+  const int v[10] = {p.C, p.CGW, p.nwg, p.NWK, p.NWC, p.NCG, p.NKG, p.KC, p.QW, MT};
+  for (int i = 0; i < 10; ++i) plan10[i] = v[i];
   return SMALLM_OK;
 }
 

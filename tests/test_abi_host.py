@@ -36,19 +36,34 @@ def test_launch_plans_balance_the_cus():
                              (2048, 4096): (8, 1)}.items():
         p = P.smallm_fp8bs_launch_plan(16, N, K)
         assert (p["C"], p["CGW"], p["nwg"]) == (C, CGW, 256)
-        assert p["CGW"] * p["WPG"] == 4 or p["WPG"] == 1
+        # the MFMA wave grid covers every column group and, per round, every K group once
+        assert p["NCG"] * p["NWC"] == p["CGW"]
+        assert p["KC"] == p["NKG"] * p["NWK"] * (16 // p["C"])
+        assert 4 <= p["NWK"] * p["NWC"] <= 12 and p["NWK"] * p["NWC"] + p["QW"] <= 16
     assert P.smallm_fp8bs_launch_plan(17, 4096, 2048)["MT"] == 2
     assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["MT"] == 1
-    p = P.smallm_fp8bs_launch_plan(4, 36864, 128)
-    assert (p["CGW"], p["FPW"], p["WPG"]) == (9, 4, 1)
+    # activation tiles shared by 5 column groups: 8 waves, one K group of 4 blocks each
     p = P.smallm_fp8bs_launch_plan(4, 5120, 4096)
-    assert (p["FPW"], p["KC"]) == (8, 32)
-    assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 4, 8, 0>"
-    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 2, 4, 0>"
+    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (8, 1, 5, 1, 32)
+    # 9 column groups: 3 x 3 column groups per wave, 4 K groups of 8 blocks
+    p = P.smallm_fp8bs_launch_plan(16, 4608, 4096)
+    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (4, 3, 3, 1, 32, 4)
+    # two M tiles: one column group per wave
+    p = P.smallm_fp8bs_launch_plan(32, 4608, 4096)
+    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (1, 9, 1, 4, 32)
+    # one column group per workgroup: K split over 4 waves, 4 fragments each per round
+    p = P.smallm_fp8bs_launch_plan(4, 4096, 2048)
+    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (4, 1, 1, 4, 16)
+    # a single K group per round leaves one wave per column group
+    p = P.smallm_fp8bs_launch_plan(4, 36864, 128)
+    assert (p["CGW"], p["NWC"], p["NCG"], p["NWK"]) == (9, 9, 1, 1)
+    assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 4, 5, 1, 0>"
+    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 2, 1, 4, 0>"
+    assert P.kernel_name(8, 4096, 2048, 1) == "smallm_gemm_kernel<1, 16, 1, 4, 1>"
 
 
 def test_version_layout_and_strerror():
-    assert P.smallm_fp8bs_abi_version() == 1
+    assert P.smallm_fp8bs_abi_version() == 2
     # columns per group: the widest C in {16, 8, 4, 2} giving a multiple of 256 column groups
     assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46380210
     assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46380204
