@@ -68,16 +68,6 @@ __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   return v;
 }
 
-// Sum over the S consecutive lanes (S = 1, 2, 4 or 8, aligned) that hold one output column's K
-// blocks; every one of the S lanes gets the same total.
-template <int S>
-__device__ __forceinline__ float lane_group_sum(float v) {
-  if (S >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  if (S >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  if (S >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  return v;
-}
-
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -486,27 +476,45 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
               const int kbl = kgr * S + s_l;  // this lane's K block within the round
               sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
             }
-            // fragment by fragment, so that each one is consumed as soon as its loads land
+            // fragments in groups of up to three, whose MFMA chains interleave (a dependent chain
+            // would wait for each MFMA's result), each group consumed as soon as its loads land
+            constexpr int JG = NCG < 3 ? NCG : 3;
 #pragma unroll
-            for (int j = 0; j < NCG; ++j) {
-              const v8i b = __builtin_bit_cast(
-                  v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-              v4f fa = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int j0 = 0; j0 < NCG; j0 += JG) {
+              v8i b[JG];
+              v4f fa[JG];
 #pragma unroll
-              for (int s = 0; s < S; ++s) {
-                if (Cfg::kE8) {
-                  const int sb = (S == 1 || s_l == s) ? sbl[i][j] : 0;
-                  acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b, acc[j][mt], 0, 0, 0, sa[s], 0, sb);
-                } else if (S == 1) {
-                  fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b, fa, 0, 0, 0, 0, 0, 0);
-                } else {
-                  const int sb = (s_l == s) ? 127 : 0;
-                  fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b, fa, 0, 0, 0, 127, 0, sb);
-                }
+              for (int jj = 0; jj < JG; ++jj) {
+                const int j = min(j0 + jj, NCG - 1);
+                b[jj] = __builtin_bit_cast(
+                    v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                fa[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
               }
+#pragma unroll
+              for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int jj = 0; jj < JG; ++jj) {
+                  const int j = j0 + jj;
+                  if (j >= NCG) continue;
+                  if (Cfg::kE8) {
+                    const int sb = (S == 1 || s_l == s) ? sbl[i][j] : 0;
+                    acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], acc[j][mt], 0, 0, 0, sa[s], 0, sb);
+                  } else if (S == 1) {
+                    fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 0, 0, 0);
+                  } else {
+                    const int sb = (s_l == s) ? 127 : 0;
+                    fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 127, 0, sb);
+                  }
+                }
               if (!Cfg::kE8) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[e], acc[j][mt][e]);
+                for (int jj = 0; jj < JG; ++jj) {
+                  const int j = j0 + jj;
+                  if (j >= NCG) continue;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[jj][e], acc[j][mt][e]);
+                }
               }
             }
           }
@@ -600,16 +608,14 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
     }
   }
 
-  // ---- reduction, fixed order: the S K-block lanes of a column in registers, then the NWK waves
-  // that split K through LDS (staging space reused) ----
+  // ---- cross-wave and cross-lane reduction through LDS (staging space reused), fixed order ----
   if (mw >= 0) {
 #pragma unroll
     for (int j = 0; j < NCG; ++j)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          red[(((mw * NCG + j) * MT + mt) * 4 + e) * 64 + lane] = lane_group_sum<S>(acc[j][mt][e]);
+        for (int e = 0; e < 4; ++e) red[(((mw * NCG + j) * MT + mt) * 4 + e) * 64 + lane] = acc[j][mt][e];
   }
   __syncthreads();
   const int ncols = CGW * C;
@@ -620,15 +626,13 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       const int cgw = col / C, cc = col % C;
       const int cqo = cgw % NWC, j = cgw / NWC;
       const int mt = row >> 4, r = row & 15, e = r & 3;
-      const float* rp = red + (((cqo * NWK * NCG + j) * MT + mt) * 4 + e) * 64 + (r >> 2) * 16 + cc * S;
-      const int kstride = NCG * MT * 4 * 64;  // floats between the partials of consecutive K parts
-      float part[kMaxMfmaWaves];
+      const int lbase = (r >> 2) * 16 + cc * S;  // lanes of the column's S K blocks
+      float sum = 0.0f;
+      for (int k = 0; k < NWK; ++k) {
+        const float* rp = red + ((((cqo * NWK + k) * NCG + j) * MT + mt) * 4 + e) * 64 + lbase;
 #pragma unroll
-      for (int k = 0; k < kMaxMfmaWaves; ++k) part[k] = (k < NWK) ? rp[k * kstride] : 0.0f;
-      float sum = part[0];
-#pragma unroll
-      for (int k = 1; k < kMaxMfmaWaves; ++k)
-        if (k < NWK) sum += part[k];
+        for (int s = 0; s < S; ++s) sum += rp[s];
+      }
       y[(int64_t)(m0 + row) * ldy + (int64_t)(cg0 + cgw) * C + cc] = bf16_rne(sum);
     }
   }
