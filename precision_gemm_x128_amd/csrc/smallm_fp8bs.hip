@@ -56,12 +56,6 @@ constexpr int kRowStride = 144;              // LDS row pitch of the staged e4m3
 // small device helpers
 // ---------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ float quad_max_f32(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  return v;
-}
-
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
@@ -99,36 +93,40 @@ __device__ __forceinline__ int e8m0_round_exponent(float amax) {
 
 // Quantise 32 consecutive bf16 of one 1x128 group (this lane's quarter; the group is spread
 // over a DPP quad) with an fp32 group scale.  Returns the scale, writes 32 e4m3 bytes.
+//
+// x / s comes from Markstein's correction (q0 = x y, r = q0 s - x exact through the FMA,
+// q = q0 - r y, with y the correctly rounded 1/s), which needs y finite and r clear of the
+// subnormal range.  A group scale below 2^-64 is first rescaled by 2^64 (x 2^64 / (s 2^64) is the
+// same quotient; both products are exact, |x| <= 448 s keeping x 2^64 below 448), so every group
+// takes one straight-line path.  Over every pair of bf16 amax and bf16 x with |x| <= amax, q
+// equals RN(x / s) except for quotients far below 2^-10, which encode to zero either way: the
+// e4m3 codes are those of the exact division in all cases.
 __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[2]) {
-  float f[32];
+  // group amax on the bf16 bit patterns: with the sign cleared, integer order is magnitude order
+  u16x2 mx = u16x2{0, 0};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t d = xv[i >> 2][i & 3];
-    f[2 * i] = __uint_as_float(d << 16);
-    f[2 * i + 1] = __uint_as_float(d & 0xFFFF0000u);
-  }
-  float am = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(f[i]));
-  am = quad_max_f32(am);
-  const float s = am / 448.0f;                    // correctly rounded fp32 division
-  const float y = (am > 0.0f) ? 1.0f / s : 0.0f;  // correctly rounded reciprocal
-  float qf[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float q0 = f[i] * y;
-    const float r = __builtin_fmaf(q0, s, -f[i]);
-    qf[i] = __builtin_fmaf(-r, y, q0);
-  }
-  if (s > 0.0f && s < 0x1p-64f) {  // tiny group scale: plain IEEE division
-#pragma unroll
-    for (int i = 0; i < 32; ++i) qf[i] = f[i] / s;
-  }
+  for (int i = 0; i < 16; ++i)
+    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, xv[i >> 2][i & 3] & 0x7FFF7FFFu));
+  const uint32_t amb = quad_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1]));
+  const float am = __uint_as_float(amb << 16);
+  const float s = am / 448.0f;                          // correctly rounded fp32 division
+  const float k = (s < 0x1p-64f) ? 0x1p64f : 1.0f;      // rescaling of a tiny group
+  const float sk = s * k;
+  const float y = (am > 0.0f) ? 1.0f / sk : 0.0f;       // correctly rounded reciprocal
   uint32_t w[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(qf[4 * j], qf[4 * j + 1], 0, false);
-    p = __builtin_amdgcn_cvt_pk_fp8_f32(qf[4 * j + 2], qf[4 * j + 3], p, true);
+    float q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t d = xv[(2 * j + (t >> 1)) >> 2][(2 * j + (t >> 1)) & 3];
+      const float f = __uint_as_float((t & 1) ? (d & 0xFFFF0000u) : (d << 16)) * k;
+      const float q0 = f * y;
+      const float r = __builtin_fmaf(q0, sk, -f);
+      q[t] = __builtin_fmaf(-r, y, q0);
+    }
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
     w[j] = (uint32_t)p;
   }
   qv[0] = u32x4{w[0], w[1], w[2], w[3]};
@@ -377,12 +375,20 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Each role runs its own round loop (same number of barriers per round on both sides), so
+  // that values one role keeps across rounds take no registers in the other.
   const int rounds = (KB + KC - 1) / KC;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int kb0 = rd * KC;
-    const int KCr = min(KC, KB - kb0);
-    if (mw >= 0) {
+  if (mw >= 0) {
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int kb0 = rd * KC;
+      const int KCr = min(KC, KB - kb0);
       // ---- MFMA waves ----
+      // A per-round copy of the lane index that the compiler cannot see through, so that the
+      // lane-dependent addresses are formed inside the round instead of held in registers across
+      // the whole loop (which would spill: a spill reload waits for every load in flight).
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int s_lr = (ln & 15) % S;  // K block (within a fragment) of this lane's B column
       const int KGr = KCr / S;
       // this wave's K groups of the round: a contiguous share [kg_lo, kg_lo + nkg)
       const int kg_lo = kq * KGr / NWK;
@@ -390,16 +396,39 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       float swv[NKG][NCG];
       int sbl[NKG][NCG];
       u32x4 wr[NKG][NCG][2];
-      // block scales first (so that waiting for them never waits for the weight stream)
+      // Block scales: a fragment's S scales are contiguous and the same for the whole wave, so
+      // they are read with scalar loads (own counter: waiting for them never waits for the weight
+      // stream, and they take no vector registers); each lane then picks its own K block's.
 #pragma unroll
       for (int i = 0; i < NKG; ++i)
 #pragma unroll
         for (int j = 0; j < NCG; ++j) {
           const int cg = min(cq + j * NWC, CGW - 1);
           const int nb = ((cg0 + cg) * C) >> 7;  // 128-column block of the column group
-          const int kb = min(kb0 + (kg_lo + i) * S + s_l, KB - 1);
-          if (Cfg::kE8) sbl[i][j] = (int)((const uint8_t*)sw)[nb * KB + kb];
-          else swv[i][j] = ((const float*)sw)[nb * KB + kb];
+          const int kbs = __builtin_amdgcn_readfirstlane(min(kb0 + (kg_lo + i) * S, KB - S));
+          const int base = __builtin_amdgcn_readfirstlane(nb * KB + kbs);
+          if (Cfg::kE8) {
+            const uint8_t* sp = (const uint8_t*)sw + base;
+            uint32_t word = 0;
+#pragma unroll
+            for (int t = 0; t < (S < 4 ? S : 4); ++t) word |= (uint32_t)sp[t] << (8 * t);
+            if (S == 8) {
+              uint32_t hi = 0;
+#pragma unroll
+              for (int t = 4; t < 8; ++t) hi |= (uint32_t)sp[t] << (8 * (t - 4));
+              word = (s_lr < 4) ? word : hi;
+            }
+            sbl[i][j] = (int)((word >> (8 * (s_lr & 3))) & 0xFFu);
+          } else {
+            const float* sp = (const float*)sw + base;
+            float sc[S];
+#pragma unroll
+            for (int t = 0; t < S; ++t) sc[t] = sp[t];
+            float v = sc[0];
+#pragma unroll
+            for (int t = 1; t < S; ++t) v = (s_lr == t) ? sc[t] : v;
+            swv[i][j] = v;
+          }
         }
 #pragma unroll
       for (int i = 0; i < NKG; ++i)
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         for (int j = 0; j < NCG; ++j) {
           const int cg = cq + j * NWC;
           const uint32_t off = (i < nkg && cg < CGW)
-                                   ? ((uint32_t)(cg * KG + kb0 / S + kg_lo + i) * 2048u + lane * 16u)
+                                   ? ((uint32_t)(cg * KG + kb0 / S + kg_lo + i) * 2048u + ln * 16u)
                                    : region;
           wr[i][j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 2));
           wr[i][j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 1024u, 0, 2));
@@ -418,6 +447,9 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         // K group within the round; a slot past the wave's share has zero weights and reads a
         // staged tile (finite bytes), so its products are exactly zero
         const int kgr = min(kg_lo + i, KGr - 1);
+        // keep the scheduler from hoisting the next K group's LDS reads over this one (their
+        // registers would not fit, and a spill reload waits for every load in flight)
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (NCG == 1) {
           // one column group: each activation tile is read right before its MFMA
           const v8i b = __builtin_bit_cast(
@@ -430,28 +462,28 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
             const int kbr = kgr * S + s;  // K block within the round
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-              const int row = mt * 16 + (lane & 15);
-              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (lane >> 4) * 32);
+              const int row = mt * 16 + (ln & 15);
+              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
               const u32x4 a0 = ap[0], a1 = ap[1];
               const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
               if (Cfg::kE8) {
                 const int sa = (int)sts_b[kbr * MP + row];
-                const int sb = (S == 1 || s_l == s) ? sbl[i][0] : 0;
+                const int sb = (S == 1 || s_lr == s) ? sbl[i][0] : 0;
                 acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[0][mt], 0, 0, 0, sa, 0, sb);
               } else if (S == 1) {
                 fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 0, 0, 0);
               } else {
-                const int sb = (s_l == s) ? 127 : 0;
+                const int sb = (s_lr == s) ? 127 : 0;
                 fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 127, 0, sb);
               }
             }
           }
           if (!Cfg::kE8) {
-            const int kbl = kgr * S + s_l;  // this lane's K block within the round
+            const int kbl = kgr * S + s_lr;  // this ln's K block within the round
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-              const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
+              const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
 #pragma unroll
               for (int e = 0; e < 4; ++e) acc[0][mt][e] = __builtin_fmaf(sx4[e] * swv[i][0], fa[mt][e], acc[0][mt][e]);
             }
@@ -460,21 +492,21 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             // the K group's S activation tiles, read from LDS once for all NCG column groups
-            const int row = mt * 16 + (lane & 15);
+            const int row = mt * 16 + (ln & 15);
             v8i a[S];
             int sa[S];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
               const int kbr = kgr * S + s;  // K block within the round
-              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (lane >> 4) * 32);
+              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
               const u32x4 a0 = ap[0], a1 = ap[1];
               a[s] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
               sa[s] = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
             }
             v4f sx4 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
             if (!Cfg::kE8) {
-              const int kbl = kgr * S + s_l;  // this lane's K block within the round
-              sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (lane >> 4));
+              const int kbl = kgr * S + s_lr;  // this ln's K block within the round
+              sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
             }
             // fragments in groups of up to three, whose MFMA chains interleave (a dependent chain
             // would wait for each MFMA's result), each group consumed as soon as its loads land
@@ -497,12 +529,12 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
                   const int j = j0 + jj;
                   if (j >= NCG) continue;
                   if (Cfg::kE8) {
-                    const int sb = (S == 1 || s_l == s) ? sbl[i][j] : 0;
+                    const int sb = (S == 1 || s_lr == s) ? sbl[i][j] : 0;
                     acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], acc[j][mt], 0, 0, 0, sa[s], 0, sb);
                   } else if (S == 1) {
                     fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 0, 0, 0);
                   } else {
-                    const int sb = (s_l == s) ? 127 : 0;
+                    const int sb = (s_lr == s) ? 127 : 0;
                     fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 127, 0, sb);
                   }
                 }
@@ -521,7 +553,11 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         }
       }
       __syncthreads();  // staging buffer free for the next round
-    } else {
+    }
+  } else {
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int kb0 = rd * KC;
+      const int KCr = min(KC, KB - kb0);
       // ---- quantising (or staging) waves: one DPP quad per 1x128 group, two passes in flight ----
       const int slots = QW * 16;
       const int slot = wave * 16 + (lane >> 2);
