@@ -383,11 +383,12 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       const int kb0 = rd * KC;
       const int KCr = min(KC, KB - kb0);
       // ---- MFMA waves ----
-      // A per-round copy of the lane index that the compiler cannot see through, so that the
-      // lane-dependent addresses are formed inside the round instead of held in registers across
-      // the whole loop (which would spill: a spill reload waits for every load in flight).
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
+      // The lane index, formed afresh in every round where the compiler cannot see through it, so
+      // that the lane-dependent addresses are computed inside the round instead of held in
+      // registers across the whole loop (which would spill: a spill reload waits for every load
+      // in flight).
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
       const int s_lr = (ln & 15) % S;  // K block (within a fragment) of this lane's B column
       const int KGr = KCr / S;
       // this wave's K groups of the round: a contiguous share [kg_lo, kg_lo + nkg)
@@ -447,9 +448,10 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         // K group within the round; a slot past the wave's share has zero weights and reads a
         // staged tile (finite bytes), so its products are exactly zero
         const int kgr = min(kg_lo + i, KGr - 1);
-        // keep the scheduler from hoisting the next K group's LDS reads over this one (their
-        // registers would not fit, and a spill reload waits for every load in flight)
-        __builtin_amdgcn_sched_barrier(0);
+        // with eight fragments (or eight K blocks of two M tiles) in flight, keep the scheduler from hoisting the next K group's LDS
+        // reads over this one (their registers would not fit, and a spill reload waits for every
+        // load in flight)
+        if (NKG >= 8 || (MT == 2 && S >= 8)) __builtin_amdgcn_sched_barrier(0);
         if constexpr (NCG == 1) {
           // one column group: each activation tile is read right before its MFMA
           const v8i b = __builtin_bit_cast(
@@ -489,64 +491,109 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
             }
           }
         } else {
+          if constexpr (MT == 1) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            // the K group's S activation tiles, read from LDS once for all NCG column groups
-            const int row = mt * 16 + (ln & 15);
-            v8i a[S];
-            int sa[S];
+            for (int mt = 0; mt < MT; ++mt) {
+              // the K group's S activation tiles, read from LDS once for all NCG column groups
+              const int row = mt * 16 + (ln & 15);
+              v8i a[S];
+              int sa[S];
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-              const int kbr = kgr * S + s;  // K block within the round
-              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
-              const u32x4 a0 = ap[0], a1 = ap[1];
-              a[s] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-              sa[s] = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
-            }
-            v4f sx4 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-            if (!Cfg::kE8) {
-              const int kbl = kgr * S + s_lr;  // this ln's K block within the round
-              sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
-            }
-            // fragments in groups of up to three, whose MFMA chains interleave (a dependent chain
-            // would wait for each MFMA's result), each group consumed as soon as its loads land
-            constexpr int JG = NCG < 3 ? NCG : 3;
-#pragma unroll
-            for (int j0 = 0; j0 < NCG; j0 += JG) {
-              v8i b[JG];
-              v4f fa[JG];
-#pragma unroll
-              for (int jj = 0; jj < JG; ++jj) {
-                const int j = min(j0 + jj, NCG - 1);
-                b[jj] = __builtin_bit_cast(
-                    v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                fa[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+              for (int s = 0; s < S; ++s) {
+                const int kbr = kgr * S + s;  // K block within the round
+                const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
+                const u32x4 a0 = ap[0], a1 = ap[1];
+                a[s] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                sa[s] = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
               }
+              v4f sx4 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+              if (!Cfg::kE8) {
+                const int kbl = kgr * S + s_lr;  // this ln's K block within the round
+                sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
+              }
+              // fragments in groups of up to three, whose MFMA chains interleave (a dependent chain
+              // would wait for each MFMA's result), each group consumed as soon as its loads land
+              constexpr int JG = NCG < 3 ? NCG : 3;
 #pragma unroll
-              for (int s = 0; s < S; ++s)
+              for (int j0 = 0; j0 < NCG; j0 += JG) {
+                v8i b[JG];
+                v4f fa[JG];
 #pragma unroll
                 for (int jj = 0; jj < JG; ++jj) {
-                  const int j = j0 + jj;
-                  if (j >= NCG) continue;
-                  if (Cfg::kE8) {
-                    const int sb = (S == 1 || s_lr == s) ? sbl[i][j] : 0;
-                    acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], acc[j][mt], 0, 0, 0, sa[s], 0, sb);
-                  } else if (S == 1) {
-                    fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 0, 0, 0);
-                  } else {
-                    const int sb = (s_lr == s) ? 127 : 0;
-                    fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 127, 0, sb);
+                  const int j = min(j0 + jj, NCG - 1);
+                  b[jj] = __builtin_bit_cast(
+                      v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                  fa[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                  for (int jj = 0; jj < JG; ++jj) {
+                    const int j = j0 + jj;
+                    if (j >= NCG) continue;
+                    if (Cfg::kE8) {
+                      const int sb = (S == 1 || s_lr == s) ? sbl[i][j] : 0;
+                      acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], acc[j][mt], 0, 0, 0, sa[s], 0, sb);
+                    } else if (S == 1) {
+                      fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 0, 0, 0);
+                    } else {
+                      const int sb = (s_lr == s) ? 127 : 0;
+                      fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 127, 0, sb);
+                    }
+                  }
+                if (!Cfg::kE8) {
+#pragma unroll
+                  for (int jj = 0; jj < JG; ++jj) {
+                    const int j = j0 + jj;
+                    if (j >= NCG) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                      acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[jj][e], acc[j][mt][e]);
                   }
                 }
-              if (!Cfg::kE8) {
+              }
+            }
+          } else {
+            // two M tiles: one activation tile at a time (the accumulators of both tiles are
+            // live), the NCG independent MFMA chains interleaved
 #pragma unroll
-                for (int jj = 0; jj < JG; ++jj) {
-                  const int j = j0 + jj;
-                  if (j >= NCG) continue;
+            for (int mt = 0; mt < MT; ++mt) {
+              const int row = mt * 16 + (ln & 15);
+              v4f fa[NCG];
+#pragma unroll
+              for (int j = 0; j < NCG; ++j) fa[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int s = 0; s < S; ++s) {
+                const int kbr = kgr * S + s;  // K block within the round
+                const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
+                const u32x4 a0 = ap[0], a1 = ap[1];
+                const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                  (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                const int sa = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
+#pragma unroll
+                for (int j = 0; j < NCG; ++j) {
+                  const v8i b = __builtin_bit_cast(
+                      v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                  if (Cfg::kE8) {
+                    const int sb = (S == 1 || s_lr == s) ? sbl[i][j] : 0;
+                    acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j][mt], 0, 0, 0, sa, 0, sb);
+                  } else if (S == 1) {
+                    fa[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[j], 0, 0, 0, 0, 0, 0);
+                  } else {
+                    const int sb = (s_lr == s) ? 127 : 0;
+                    fa[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[j], 0, 0, 0, 127, 0, sb);
+                  }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              if (!Cfg::kE8) {
+                const int kbl = kgr * S + s_lr;  // this lane's K block within the round
+                const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
+#pragma unroll
+                for (int j = 0; j < NCG; ++j)
 #pragma unroll
                   for (int e = 0; e < 4; ++e)
-                    acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[jj][e], acc[j][mt][e]);
-                }
+                    acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[j][e], acc[j][mt][e]);
               }
             }
           }
@@ -735,7 +782,7 @@ Plan make_plan(int M, int N, int K) {
   // divisor of the K groups that fits, so that every round is full.
   p.NCG = 0;
   for (int ncg : {5, 3}) {
-    if (M > 16 || p.CGW % ncg != 0 || ncg * 8 + S * 8 + ncg * 4 > 100) continue;  // registers
+    if (p.CGW % ncg != 0 || ncg * 8 + S * 8 + ncg * 4 > 100) continue;  // registers
     const int nwc = p.CGW / ncg;
     const int cap = min(kMaxMfmaWaves / nwc, kKCMax / S);
     int nwk = 0;
@@ -767,12 +814,10 @@ void launch_c(const Plan& pl, dim3 grid, hipStream_t stream, const void* a, int6
 #define SMALLM_LAUNCH(ncg, nkg)                                                                          \
   hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, ncg, nkg, MODE>), grid, block, 0, stream, a, lda, sa, wp, \
                      sw, y, ldy, M, K, pl.CGW, pl.NWK, pl.NWC, pl.QW, q_dbg, sx_dbg)
-  if constexpr (MT == 1 && C != 2) {
+  if constexpr (C != 2) {
     if (pl.NCG == 5) { SMALLM_LAUNCH(5, 1); return; }
   }
-  if constexpr (MT == 1) {
-    if (pl.NCG == 3) { SMALLM_LAUNCH(3, 1); return; }
-  }
+  if (pl.NCG == 3) { SMALLM_LAUNCH(3, 1); return; }
   if (pl.NKG == 8) SMALLM_LAUNCH(1, 8);
   else SMALLM_LAUNCH(1, 4);
 #undef SMALLM_LAUNCH
