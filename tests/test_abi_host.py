@@ -48,9 +48,9 @@ def test_launch_plans_balance_the_cus():
     # 9 column groups: 3 x 3 column groups per wave, 4 K groups of 8 blocks
     p = P.smallm_fp8bs_launch_plan(16, 4608, 4096)
     assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (4, 3, 3, 1, 32, 4)
-    # two M tiles: one column group per wave
+    # two M tiles keep the same wave grid
     p = P.smallm_fp8bs_launch_plan(32, 4608, 4096)
-    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (1, 9, 1, 4, 32)
+    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (4, 3, 3, 1, 32)
     # one column group per workgroup: K split over 4 waves, 4 fragments each per round
     p = P.smallm_fp8bs_launch_plan(4, 4096, 2048)
     assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (4, 1, 1, 4, 16)
@@ -58,7 +58,7 @@ def test_launch_plans_balance_the_cus():
     p = P.smallm_fp8bs_launch_plan(4, 36864, 128)
     assert (p["CGW"], p["NWC"], p["NCG"], p["NWK"]) == (9, 9, 1, 1)
     assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 4, 5, 1, 0>"
-    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 2, 1, 4, 0>"
+    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 2, 3, 1, 0>"
     assert P.kernel_name(8, 4096, 2048, 1) == "smallm_gemm_kernel<1, 16, 1, 4, 1>"
 
 
