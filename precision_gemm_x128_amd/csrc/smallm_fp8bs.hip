@@ -448,10 +448,10 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         // K group within the round; a slot past the wave's share has zero weights and reads a
         // staged tile (finite bytes), so its products are exactly zero
         const int kgr = min(kg_lo + i, KGr - 1);
-        // with eight fragments (or eight K blocks of two M tiles) in flight, keep the scheduler from hoisting the next K group's LDS
-        // reads over this one (their registers would not fit, and a spill reload waits for every
-        // load in flight)
-        if (NKG >= 8 || (MT == 2 && S >= 8)) __builtin_amdgcn_sched_barrier(0);
+        // with eight fragments, shared tiles or two M tiles of multi-block fragments, keep the
+        // scheduler from hoisting the next K group's LDS reads over this one (their registers
+        // would not fit, and a spill reload waits for every load in flight)
+        if (NKG >= 8 || NCG > 1 || (MT == 2 && S >= 2)) __builtin_amdgcn_sched_barrier(0);
         if constexpr (NCG == 1) {
           // one column group: each activation tile is read right before its MFMA
           const v8i b = __builtin_bit_cast(
@@ -692,18 +692,22 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
   }
 
   // ---- cross-wave and cross-lane reduction through LDS (staging space reused), fixed order ----
+  // (lane and thread index formed again here rather than held across the rounds)
+  int lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int tid_e = wave * 64 + lane_e;
   if (mw >= 0) {
 #pragma unroll
     for (int j = 0; j < NCG; ++j)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(((mw * NCG + j) * MT + mt) * 4 + e) * 64 + lane] = acc[j][mt][e];
+        for (int e = 0; e < 4; ++e) red[(((mw * NCG + j) * MT + mt) * 4 + e) * 64 + lane_e] = acc[j][mt][e];
   }
   __syncthreads();
   const int ncols = CGW * C;
   const int nthreads = blockDim.x;
-  for (int o = tid; o < MP * ncols; o += nthreads) {
+  for (int o = tid_e; o < MP * ncols; o += nthreads) {
     const int row = o / ncols, col = o % ncols;
     if (row < Mc) {
       const int cgw = col / C, cc = col % C;
