@@ -91,6 +91,29 @@ __device__ __forceinline__ int e8m0_round_exponent(float amax) {
   return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
+// x / s for the 32 elements as described below, then e4m3 with round to nearest even, four at a
+// time; RESCALE multiplies x by k first.
+template <bool RESCALE>
+__device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float sk, float y, float k,
+                                              uint32_t (&w)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t d = xv[(2 * j + (t >> 1)) >> 2][(2 * j + (t >> 1)) & 3];
+      float f = __uint_as_float((t & 1) ? (d & 0xFFFF0000u) : (d << 16));
+      if (RESCALE) f *= k;
+      const float q0 = f * y;
+      const float r = __builtin_fmaf(q0, sk, -f);
+      q[t] = __builtin_fmaf(-r, y, q0);
+    }
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
+    w[j] = (uint32_t)p;
+  }
+}
+
 // Quantise 32 consecutive bf16 of one 1x128 group (this lane's quarter; the group is spread
 // over a DPP quad) with an fp32 group scale.  Returns the scale, writes 32 e4m3 bytes.
 //
@@ -110,25 +133,14 @@ __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[
   const uint32_t amb = quad_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1]));
   const float am = __uint_as_float(amb << 16);
   const float s = am / 448.0f;                          // correctly rounded fp32 division
-  const float k = (s < 0x1p-64f) ? 0x1p64f : 1.0f;      // rescaling of a tiny group
+  const bool tiny = s > 0.0f && s < 0x1p-64f;       // (an all-zero group needs no rescaling)
+  const float k = tiny ? 0x1p64f : 1.0f;                // rescaling of a tiny group
   const float sk = s * k;
   const float y = (am > 0.0f) ? 1.0f / sk : 0.0f;       // correctly rounded reciprocal
   uint32_t w[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float q[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t d = xv[(2 * j + (t >> 1)) >> 2][(2 * j + (t >> 1)) & 3];
-      const float f = __uint_as_float((t & 1) ? (d & 0xFFFF0000u) : (d << 16)) * k;
-      const float q0 = f * y;
-      const float r = __builtin_fmaf(q0, sk, -f);
-      q[t] = __builtin_fmaf(-r, y, q0);
-    }
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
-    w[j] = (uint32_t)p;
-  }
+  // the rescaling multiply only runs when some group of the wave needs it (a wave-wide vote)
+  if (__builtin_amdgcn_ballot_w64(tiny) != 0) quant32_codes<true>(xv, sk, y, k, w);
+  else quant32_codes<false>(xv, sk, y, k, w);
   qv[0] = u32x4{w[0], w[1], w[2], w[3]};
   qv[1] = u32x4{w[4], w[5], w[6], w[7]};
   return s;
@@ -715,6 +727,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       const int mt = row >> 4, r = row & 15, e = r & 3;
       const int lbase = (r >> 2) * 16 + cc * S;  // lanes of the column's S K blocks
       float sum = 0.0f;
+#pragma unroll 4
       for (int k = 0; k < NWK; ++k) {
         const float* rp = red + ((((cqo * NWK + k) * NCG + j) * MT + mt) * 4 + e) * 64 + lbase;
 #pragma unroll
