@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "µs/call + achieved HBM GB/s (% of MI355X peak), fused quant+FP8 GEMM, M=1–32"
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 N_DEFAULT, K_DEFAULT = 5120, 4096
 M_SWEEP = (1, 4, 8, 16, 32)
 COPIES = 24
@@ -62,6 +63,93 @@ def load_traffic(kname):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def time_config(P, torch, np, synthgen, dev, N, K, Ms, copies, reps, e8m0=False, outliers=False):
+    """us/call of the fused path at each M on N x K: a HIP graph of `copies` calls on distinct
+    weight copies (cold), replayed `reps` times, timed with HIP events on the replay stream.
+    Returns {M: us}, plus the outputs of the last call at each M (for cross-checks)."""
+    qw = P.smallm_fp8bs_quant_weight_e8m0 if e8m0 else P.smallm_fp8bs_quant_weight
+    fn = P.smallm_fp8bs_quant_gemm_e8m0 if e8m0 else P.smallm_fp8bs_quant_gemm
+    wps, sws = [], []
+    for i in range(copies):
+        w = torch.from_numpy(synthgen.gen_w(N, K, seed=0, copy=i)).to(dev)
+        w8, sw = qw(w)
+        wps.append(P.smallm_fp8bs_pack_weight(w8))
+        sws.append(sw)
+        del w, w8
+    out, ys = {}, {}
+    for M in Ms:
+        x = torch.from_numpy(synthgen.gen_x(M, K, seed=0, outliers=outliers).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(copies):
+                fn(x, wps[i], sws[i], y=y)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(copies):
+                fn(x, wps[i], sws[i], y=y)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out[M] = a.elapsed_time(b) * 1e3 / (reps * copies)
+        ys[M] = y.float().cpu()
+    del wps, sws
+    torch.cuda.empty_cache()
+    return out, ys
+
+
+def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
+    """The other workloads of the method, timed the same way (per-M us/call, GB/s, % of peak):
+    the single 4096x2048 call at M=4; the M sweeps on 4608x4096 and 4096x2048 with outlier rows;
+    M = 33..256 on 4096x2048 with the MFMA rate beside the bandwidth; and the e8m0-scale path on
+    4096x2048 and 2048x4096 beside the fp32-scale path on the same data."""
+    res = {}
+
+    def entry(N, K, M, us, e8m0=False):
+        b = P.algorithmic_bytes(M, N, K, e8m0)
+        gbs = b / (us * 1e-6) / 1e9
+        return {"us_per_call": round(us, 3), "GB_s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                "kernel": P.kernel_name(M, N, K, 1 if e8m0 else 0)}
+
+    t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, [4], copies, reps)
+    res["single_4096x2048_m4"] = entry(4096, 2048, 4, t[4])
+    for N, K in ((4608, 4096), (4096, 2048)):
+        t, _ = time_config(P, torch, np, synthgen, dev, N, K, list(M_SWEEP), copies, reps, outliers=True)
+        res[f"sweep_{N}x{K}_outliers"] = {str(M): entry(N, K, M, t[M]) for M in M_SWEEP}
+        log(f"[bench] {N}x{K} outliers: " + " ".join(f"M={M} {t[M]:.2f}us" for M in M_SWEEP))
+    big = (33, 48, 64, 128, 256)
+    t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, list(big), copies, reps)
+    d = {}
+    for M in big:
+        e = entry(4096, 2048, M, t[M])
+        tf = 2.0 * M * 4096 * 2048 / (t[M] * 1e-6) / 1e12
+        e.update({"TFLOP_s": round(tf, 2), "pct_fp8_mfma_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)})
+        d[str(M)] = e
+    res["beyond_small_m_4096x2048"] = d
+    log("[bench] 4096x2048 M>32: " + " ".join(f"M={M} {t[M]:.2f}us" for M in big))
+    for N, K in ((4096, 2048), (2048, 4096)):
+        ms = [1, 8, 32]
+        tf, yf = time_config(P, torch, np, synthgen, dev, N, K, ms, copies, reps)
+        te, ye = time_config(P, torch, np, synthgen, dev, N, K, ms, copies, reps, e8m0=True)
+        d = {}
+        for M in ms:
+            rel = float(((ye[M] - yf[M]).abs().max() / yf[M].abs().max()).item())
+            d[str(M)] = {"fp32_scales": entry(N, K, M, tf[M]), "e8m0_scales": entry(N, K, M, te[M], True),
+                         "max_abs_diff_over_max_abs": round(rel, 5)}
+        res[f"e8m0_vs_fp32_{N}x{K}"] = d
+        log(f"[bench] {N}x{K} e8m0 vs fp32: " + " ".join(f"M={M} {te[M]:.2f}/{tf[M]:.2f}us" for M in ms))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,6 +159,7 @@ def main():
     ap.add_argument("--N", type=int, default=N_DEFAULT)
     ap.add_argument("--K", type=int, default=K_DEFAULT)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' timings")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="target seconds per CPU leg")
     ap.add_argument("--reps", type=int, default=20, help="graph replays per M for the per-M breakdown")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -219,6 +308,13 @@ def main():
     pages_gbs = sum(bytes_per_call.values()) / (pages_step_us * 1e-6) / 1e9
     vs_baseline = round(value / pages_gbs, 3) if (N, K) == (5120, 4096) else None
 
+    # ---- the other workloads (after the timed region; not part of `value`) ----
+    configs = None
+    if not args.no_configs:
+        del graphs, wps, sws
+        torch.cuda.empty_cache()
+        configs = config_sweeps(P, torch, np, synthgen, dev, min(copies, COPIES), 10)
+
     # ---- CPU oracle baseline (rank 0, N=1 only), bounded sample ----
     cpu = None
     if not args.no_cpu:
@@ -246,6 +342,7 @@ def main():
         "launch_floor_us": round(floor_us, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "configs": configs,
         "gpu": torch.cuda.get_device_name(0),
         "hip": torch.version.hip,
     }

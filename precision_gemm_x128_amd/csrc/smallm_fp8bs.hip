@@ -386,6 +386,11 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
   for (int j = 0; j < NCG; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // e8m0 with one column group: odd fragments accumulate separately, so that the MFMA chain of
+  // consecutive fragments is two independent chains (added once at the end)
+  v4f acc_odd[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc_odd[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Each role runs its own round loop (same number of barriers per round on both sides), so
   // that values one role keeps across rounds take no registers in the other.
@@ -484,7 +489,8 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
               if (Cfg::kE8) {
                 const int sa = (int)sts_b[kbr * MP + row];
                 const int sb = (S == 1 || s_lr == s) ? sbl[i][0] : 0;
-                acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[0][mt], 0, 0, 0, sa, 0, sb);
+                v4f& dst = (i & 1) ? acc_odd[mt] : acc[0][mt];
+                dst = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, dst, 0, 0, 0, sa, 0, sb);
               } else if (S == 1) {
                 fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 0, 0, 0);
               } else {
@@ -612,6 +618,10 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         }
       }
       __syncthreads();  // staging buffer free for the next round
+    }
+    if (Cfg::kE8 && NCG == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[0][mt] += acc_odd[mt];
     }
   } else {
     for (int rd = 0; rd < rounds; ++rd) {
