@@ -94,7 +94,7 @@ __device__ __forceinline__ int e8m0_round_exponent(float amax) {
 // x / s for the 32 elements as described below, then e4m3 with round to nearest even, four at a
 // time; RESCALE multiplies x by k first.
 template <bool RESCALE>
-__device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float sk, float y, float k,
+__device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float yh, float yl, float k,
                                               uint32_t (&w)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -104,9 +104,7 @@ __device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float sk, fl
       const uint32_t d = xv[(2 * j + (t >> 1)) >> 2][(2 * j + (t >> 1)) & 3];
       float f = __uint_as_float((t & 1) ? (d & 0xFFFF0000u) : (d << 16));
       if (RESCALE) f *= k;
-      const float q0 = f * y;
-      const float r = __builtin_fmaf(q0, sk, -f);
-      q[t] = __builtin_fmaf(-r, y, q0);
+      q[t] = __builtin_fmaf(f, yh, f * yl);
     }
     int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
     p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
@@ -117,13 +115,14 @@ __device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float sk, fl
 // Quantise 32 consecutive bf16 of one 1x128 group (this lane's quarter; the group is spread
 // over a DPP quad) with an fp32 group scale.  Returns the scale, writes 32 e4m3 bytes.
 //
-// x / s comes from Markstein's correction (q0 = x y, r = q0 s - x exact through the FMA,
-// q = q0 - r y, with y the correctly rounded 1/s), which needs y finite and r clear of the
-// subnormal range.  A group scale below 2^-64 is first rescaled by 2^64 (x 2^64 / (s 2^64) is the
-// same quotient; both products are exact, |x| <= 448 s keeping x 2^64 below 448), so every group
-// takes one straight-line path.  Over every pair of bf16 amax and bf16 x with |x| <= amax, q
-// equals RN(x / s) except for quotients far below 2^-10, which encode to zero either way: the
-// e4m3 codes are those of the exact division in all cases.
+// x / s is formed with a two-term reciprocal, 1/s ~ yh + yl: yh is 1/s rounded toward zero (the
+// correctly rounded reciprocal, stepped down one unit when the residual 1 - s yh comes out
+// negative) and yl = (1 - s yh) yh >= 0 its remainder, so that q = fma(x, yh, x yl) costs a
+// multiply and an FMA per element and keeps the sign of a zero x.  A group scale below 2^-64 is
+// first rescaled by 2^64 (x 2^64 / (s 2^64) is the same quotient; both products are exact,
+// |x| <= 448 s keeping x 2^64 below 448) so that 1/s stays finite.  Over every pair of bf16 amax
+// and bf16 x with |x| <= amax, the e4m3 code of q equals that of the correctly rounded division
+// RN(x / s): q differs from RN(x / s) only by quotients that no e4m3 rounding boundary separates.
 __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[2]) {
   // group amax on the bf16 bit patterns: with the sign cleared, integer order is magnitude order
   u16x2 mx = u16x2{0, 0};
@@ -136,11 +135,17 @@ __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[
   const bool tiny = s > 0.0f && s < 0x1p-64f;       // (an all-zero group needs no rescaling)
   const float k = tiny ? 0x1p64f : 1.0f;                // rescaling of a tiny group
   const float sk = s * k;
-  const float y = (am > 0.0f) ? 1.0f / sk : 0.0f;       // correctly rounded reciprocal
+  float yh = (am > 0.0f) ? 1.0f / sk : 0.0f;            // correctly rounded reciprocal
+  float e = __builtin_fmaf(-sk, yh, 1.0f);               // its residual, exact
+  if (e < 0.0f) {                                        // rounded up: one unit toward zero
+    yh = __uint_as_float(__float_as_uint(yh) - 1u);
+    e = __builtin_fmaf(-sk, yh, 1.0f);
+  }
+  const float yl = e * yh;                               // all-zero group: yh = yl = 0
   uint32_t w[8];
   // the rescaling multiply only runs when some group of the wave needs it (a wave-wide vote)
-  if (__builtin_amdgcn_ballot_w64(tiny) != 0) quant32_codes<true>(xv, sk, y, k, w);
-  else quant32_codes<false>(xv, sk, y, k, w);
+  if (__builtin_amdgcn_ballot_w64(tiny) != 0) quant32_codes<true>(xv, yh, yl, k, w);
+  else quant32_codes<false>(xv, yh, yl, k, w);
   qv[0] = u32x4{w[0], w[1], w[2], w[3]};
   qv[1] = u32x4{w[4], w[5], w[6], w[7]};
   return s;

@@ -1,7 +1,9 @@
 // Exhaustive CPU check of the fused kernel's activation-quotient recipe.
 //
-// The kernel forms x / s, s = RN(amax / 448), as q0 = x y, r = fma(q0, s, -x), q = fma(-r, y, q0)
-// with y = RN(1 / s) (Markstein's correction), after rescaling x and s by 2^64 when 0 < s < 2^-64.
+// The kernel forms x / s, s = RN(amax / 448), as q = fma(x, yh, x yl) with a two-term reciprocal:
+// yh = 1 / s rounded toward zero (RN(1 / s), stepped down one unit when the residual
+// e = fma(-s, yh, 1) is negative) and yl = e yh >= 0, after rescaling x and s by 2^64 when
+// 0 < s < 2^-64.
 // For every positive bf16 amax and every bf16 x with |x| <= amax (both signs), this program checks
 // that the e4m3 code (round to nearest even, saturating at 448) of that q equals the code of the
 // correctly rounded IEEE division x / s.  It counts fp32 quotient mismatches separately (they may
@@ -37,14 +39,18 @@ int main(void) {
     const float s = am / 448.0f;
     const float k = (s > 0.0f && s < 0x1p-64f) ? 0x1p64f : 1.0f;
     const float sk = s * k;
-    const float y = 1.0f / sk;
+    float yh = 1.0f / sk;
+    float e = fmaf(-sk, yh, 1.0f);
+    if (e < 0.0f) {
+      uint32_t u; memcpy(&u, &yh, 4); --u; memcpy(&yh, &u, 4);
+      e = fmaf(-sk, yh, 1.0f);
+    }
+    const float yl = e * yh;
     for (int xb = 0; xb <= ab; ++xb) {
       for (int sg = 0; sg < 2; ++sg) {
         const float x = sg ? -bf((uint16_t)xb) : bf((uint16_t)xb);
         const float f = x * k;
-        const float q0 = f * y;
-        const float r = fmaf(q0, sk, -f);
-        const float q = fmaf(-r, y, q0);
+        const float q = fmaf(f, yh, f * yl);
         const float ref = x / s;
         ++checked;
         if (q != ref || signbit(q) != signbit(ref)) ++fbad;

@@ -198,6 +198,57 @@ def test_quant_exhaustive_bf16_values():
                               sx_ref.view(np.uint8 if e8m0 else np.uint32))
 
 
+def every_amax_groups(seed=7):
+    """One 1x128 group per positive finite bf16 amax (0x0001 .. 0x7F7F): the amax itself plus 127
+    random bf16 of magnitude <= amax with random signs, as rows of 32 groups (K = 4096).  Covers
+    the tiny-scale rescaling, subnormal scales and reciprocals, and the largest scales."""
+    rng = np.random.default_rng([seed, 11])
+    amax = np.arange(1, 0x7F80, dtype=np.uint32)
+    mag = (rng.random((len(amax), 127)) * (amax[:, None] + 1)).astype(np.uint32)
+    mag = np.minimum(mag, amax[:, None])
+    sgn = rng.integers(0, 2, (len(amax), 127), dtype=np.uint32) << 15
+    g = np.c_[(mag | sgn), amax].astype(np.uint16)
+    g = np.take_along_axis(g, rng.permuted(np.tile(np.arange(128), (len(amax), 1)), axis=1), axis=1)
+    pad = (-len(amax)) % 32
+    g = np.r_[g, np.zeros((pad, 128), dtype=np.uint16)]
+    return g.reshape(-1, 4096)
+
+
+def test_quant_every_bf16_amax():
+    note("quant every bf16 amax")
+    x = every_amax_groups()
+    for e8m0 in (False, True):
+        q_ref, sx_ref = oracle.quant_act(x, e8m0=e8m0)
+        fn = P.smallm_fp8bs_quant_e8m0 if e8m0 else P.smallm_fp8bs_quant
+        for r0 in range(0, x.shape[0], 256):                # at most 256 rows per call
+            q, sx = fn(to_dev_bf16(x[r0:r0 + 256]))
+            torch.cuda.synchronize()
+            assert np.array_equal(q.cpu().numpy(), q_ref[r0:r0 + 256]), f"e8m0={e8m0} rows {r0}.."
+            assert np.array_equal(sx.cpu().numpy().view(np.uint8 if e8m0 else np.uint32),
+                                  sx_ref[r0:r0 + 256].view(np.uint8 if e8m0 else np.uint32))
+
+
+@pytest.mark.parametrize("e8m0", [False, True])
+def test_fused_debug_quant_every_bf16_amax(e8m0):
+    """The fused kernel's quantiser on the same groups, 32 rows (1024 groups) per call."""
+    note(f"fused debug quant every bf16 amax e8m0={e8m0}")
+    x = every_amax_groups()
+    q_ref, sx_ref = oracle.quant_act(x, e8m0=e8m0)
+    N, K = 256, 4096
+    w8, sw, wp, swd = prepared_weight(N, K, seed=3, e8m0=e8m0)
+    fn = P.smallm_fp8bs_quant_gemm_e8m0 if e8m0 else P.smallm_fp8bs_quant_gemm
+    for r0 in range(0, x.shape[0], 32):
+        xs = x[r0:r0 + 32]
+        M = xs.shape[0]
+        q_dbg = torch.zeros((M, K), dtype=torch.uint8, device=DEV)
+        sx_dbg = torch.zeros((M, K // 128), dtype=torch.uint8 if e8m0 else torch.float32, device=DEV)
+        fn(to_dev_bf16(xs), wp, swd, q_dbg=q_dbg, sx_dbg=sx_dbg)
+        torch.cuda.synchronize()
+        assert np.array_equal(q_dbg.cpu().numpy(), q_ref[r0:r0 + M]), f"rows {r0}.."
+        assert np.array_equal(sx_dbg.cpu().numpy().view(np.uint8 if e8m0 else np.uint32),
+                              sx_ref[r0:r0 + M].view(np.uint8 if e8m0 else np.uint32)), f"rows {r0}.."
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 32, 48])
 @pytest.mark.parametrize("e8m0", [False, True])
 def test_fused_debug_quant_bitexact(M, e8m0):

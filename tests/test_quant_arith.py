@@ -1,4 +1,4 @@
-"""The fused kernel forms each activation quotient with Markstein's correction (and a power-of-two
+"""The fused kernel forms each activation quotient from a two-term reciprocal (and a power-of-two
 rescaling below 2^-64) instead of a division.  tests/native/quant_arith_check.c restates that recipe
 in C and checks, over every pair of bf16 amax and bf16 x with |x| <= amax, that the resulting e4m3
 code equals the code of the correctly rounded division.  Runs on the CPU in a few seconds."""
