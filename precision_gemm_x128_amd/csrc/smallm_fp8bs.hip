@@ -45,6 +45,7 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -331,7 +332,10 @@ struct GemmCfg {
   static constexpr int kMP = 16 * MT;               // rows per workgroup (M padded to the MFMA)
   static constexpr int kStq = kKCMax * kMP * kRowStride;
   static constexpr int kSts = kKCMax * kMP * (kE8 ? 1 : 4);
-  static constexpr int kRed = kMaxMfmaWaves * NCG * MT * 4 * 64 * 4;
+  // partial-sum block of one (MFMA wave, column group, M tile): 4 x 64 floats, padded so that
+  // consecutive column groups start 16 floats apart modulo the 64 LDS banks
+  static constexpr int kRedPitch = 4 * 64 + 16 / MT;
+  static constexpr int kRed = kMaxMfmaWaves * NCG * MT * kRedPitch * 4;
   static constexpr int kSmem = ((kStq + kSts) > kRed ? (kStq + kSts) : kRed);
 };
 
@@ -723,33 +727,51 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
   int lane_e;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
   const int tid_e = wave * 64 + lane_e;
+  constexpr int RP = Cfg::kRedPitch;
   if (mw >= 0) {
 #pragma unroll
     for (int j = 0; j < NCG; ++j)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(((mw * NCG + j) * MT + mt) * 4 + e) * 64 + lane_e] = acc[j][mt][e];
+        for (int e = 0; e < 4; ++e) red[((mw * NCG + j) * MT + mt) * RP + e * 64 + lane_e] = acc[j][mt][e];
   }
+  // One output per thread and pass, consecutive threads on consecutive columns of a row.  A
+  // column's S K-block partials sit in S consecutive lanes, read as one vector per MFMA wave.
+  // The first output's indices are formed before the barrier, off the critical path.
+  const unsigned ncols = (unsigned)(CGW * C);
+  const unsigned nthreads = blockDim.x;  // > ncols
+  unsigned row = (unsigned)tid_e / ncols;
+  unsigned col = (unsigned)tid_e - row * ncols;
+  const unsigned drow = nthreads / ncols, dcol = nthreads - drow * ncols;
+  const int kstride = NCG * MT * RP;
   __syncthreads();
-  const int ncols = CGW * C;
-  const int nthreads = blockDim.x;
-  for (int o = tid_e; o < MP * ncols; o += nthreads) {
-    const int row = o / ncols, col = o % ncols;
-    if (row < Mc) {
-      const int cgw = col / C, cc = col % C;
-      const int cqo = cgw % NWC, j = cgw / NWC;
-      const int mt = row >> 4, r = row & 15, e = r & 3;
-      const int lbase = (r >> 2) * 16 + cc * S;  // lanes of the column's S K blocks
-      float sum = 0.0f;
+  while (row < (unsigned)Mc) {
+    const unsigned cgw = col / C, cc = col % C;
+    const unsigned j = cgw / (unsigned)NWC, cqo = cgw - j * (unsigned)NWC;
+    const unsigned mt = row >> 4, r = row & 15, e = r & 3;
+    const unsigned lbase = (r >> 2) * 16 + cc * S;  // lanes of the column's S K blocks
+    const float* rp = red + ((cqo * NWK * NCG + j) * MT + mt) * RP + e * 64 + lbase;
+    float sum = 0.0f;
 #pragma unroll 4
-      for (int k = 0; k < NWK; ++k) {
-        const float* rp = red + ((((cqo * NWK + k) * NCG + j) * MT + mt) * 4 + e) * 64 + lbase;
+    for (int k = 0; k < NWK; ++k, rp += kstride) {
+      if constexpr (S >= 4) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) sum += rp[s];
+        for (int s4 = 0; s4 < S; s4 += 4) {
+          const v4f v = *(const v4f*)(rp + s4);
+          sum += v[0]; sum += v[1]; sum += v[2]; sum += v[3];
+        }
+      } else if constexpr (S == 2) {
+        const v2f v = *(const v2f*)rp;
+        sum += v[0]; sum += v[1];
+      } else {
+        sum += rp[0];
       }
-      y[(int64_t)(m0 + row) * ldy + (int64_t)(cg0 + cgw) * C + cc] = bf16_rne(sum);
     }
+    y[(int64_t)(m0 + row) * ldy + (int64_t)(cg0 + cgw) * C + cc] = bf16_rne(sum);
+    row += drow;
+    col += dcol;
+    if (col >= ncols) { col -= ncols; ++row; }
   }
 }
 
