@@ -322,7 +322,6 @@ enum Mode { kFusedF32 = 0, kFusedE8 = 1, kPreqF32 = 2, kPreqE8 = 3 };
 
 constexpr int kKCMax = 32;      // K blocks staged per round
 constexpr int kMaxMfmaWaves = 12;  // MFMA waves per workgroup (the quantising waves come first)
-constexpr int kMaxQuantWaves = 8;
 
 template <int MT, int C, int NCG, int NKG, int MODE>
 struct GemmCfg {
@@ -637,11 +636,9 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       const int kb0 = rd * KC;
       const int KCr = min(KC, KB - kb0);
       // ---- quantising (or staging) waves: one DPP quad per 1x128 group, two passes in flight ----
-      const int slots = QW * 16;
-      const int slot = wave * 16 + (lane >> 2);
+      const int grp = lane >> 2;  // this lane's group within a block of 16
       const int c = lane & 3;
       const int G = Mc * KCr;
-      const int npass = (G + 2 * slots - 1) / (2 * slots) * 2;  // even: the loop body is straight-line
       constexpr int NV = Cfg::kPreq ? 2 : 4;                    // 16-byte loads per lane per pass
       const int rowb = Cfg::kPreq ? 1 : 2;                        // bytes per activation element
       // the workgroup's activation rows as a bounds-checked buffer: idle lanes and passes past the
@@ -652,15 +649,15 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       u32x4 xa[4], xb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) { xa[i] = u32x4{0, 0, 0, 0}; xb[i] = u32x4{0, 0, 0, 0}; }
-#define SMALLM_QLOAD(v, p) do {                                                                   \
-      const int g_ = (p) * slots + slot;                                                         \
+#define SMALLM_QLOAD(v, b) do {                                                                   \
+      const int g_ = (b) * 16 + grp;                                                             \
       const uint32_t off_ = (g_ < G) ? (uint32_t)(((int64_t)(g_ % Mc) * lda + (kb0 + g_ / Mc) * 128 + c * 32) * rowb) \
                                      : abytes;                                                   \
       _Pragma("unroll") for (int i_ = 0; i_ < NV; ++i_)                                          \
         v[i_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off_ + 16u * i_, 0, 0)); \
     } while (0)
-#define SMALLM_QPROC(v, p) do {                                                                   \
-      const int g_ = (p) * slots + slot;                                                         \
+#define SMALLM_QPROC(v, b) do {                                                                   \
+      const int g_ = (b) * 16 + grp;                                                             \
       const bool valid_ = g_ < G;                                                                \
       const int kbl_ = valid_ ? g_ / Mc : 0;                                                     \
       const int m_ = valid_ ? g_ % Mc : 0;                                                       \
@@ -689,13 +686,21 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
         }                                                                                        \
       }                                                                                          \
     } while (0)
-      SMALLM_QLOAD(xa, 0);
-      SMALLM_QLOAD(xb, 1);
-      for (int p = 0; p < npass; p += 2) {
-        SMALLM_QPROC(xa, p);
-        SMALLM_QLOAD(xa, p + 2);
-        SMALLM_QPROC(xb, p + 1);
-        SMALLM_QLOAD(xb, p + 3);
+      // Block b of 16 groups: groups 16 b .. 16 b + 15, one per DPP quad of a wave.  Wave w takes
+      // blocks w, QW + w, 2 QW + w, ... alternating between its two buffers; the buffer processed
+      // next holds the smaller block index, so once it is past the end the other one is too.
+      const int nblk = (G + 15) >> 4;
+      int b0 = wave, b1 = QW + wave;
+      SMALLM_QLOAD(xa, b0);
+      SMALLM_QLOAD(xb, b1);
+      while (b0 < nblk) {
+        SMALLM_QPROC(xa, b0);
+        b0 += 2 * QW;
+        SMALLM_QLOAD(xa, b0);
+        if (b1 >= nblk) break;
+        SMALLM_QPROC(xb, b1);
+        b1 += 2 * QW;
+        SMALLM_QLOAD(xb, b1);
       }
 #undef SMALLM_QLOAD
 #undef SMALLM_QPROC
@@ -823,11 +828,23 @@ struct Plan {
   int C, CGW, nwg, NWK, NWC, NCG, NKG, NWM, KC, QW;
 };
 
+// Quantising waves for a round of `groups` 1x128 groups next to nwm MFMA waves: about two
+// 16-group passes per wave, as 2, 4, 8 or 12 waves, and a multiple of 4 when more than 2 so that
+// every SIMD (wave w runs on SIMD w % 4) carries the same share of the quantiser's VALU work.
+int quant_waves(int groups, int nwm) {
+  const int need = (groups + 31) / 32;
+  const int qw = need <= 2 ? 2 : (need <= 4 ? 4 : (need <= 8 ? 8 : 12));
+  const int room = 16 - nwm;
+  return min(qw, room >= 4 ? room / 4 * 4 : 2);
+}
+
 Plan make_plan(int M, int N, int K) {
   Plan p;
   p.C = layout_columns(N, K);
   const int S = 16 / p.C;
-  const int KG = (K / 128) / S;
+  const int KB = K / 128;
+  const int KG = KB / S;
+  const int Mr = min(M, 32);  // rows per workgroup
   p.CGW = groups_per_wg(N, p.C);
   p.nwg = (N / p.C) / p.CGW;
   // One M tile: waves that share their activation tiles between NCG = 5 or 3 column groups, one
@@ -843,6 +860,17 @@ Plan make_plan(int M, int N, int K) {
     for (int d = 1; d <= cap; ++d)
       if (KG % d == 0) nwk = d;
     if (nwk * nwc < 4) continue;
+    // When the quantising waves that fit beside nwk * nwc MFMA waves would still take five or
+    // more passes each, the next smaller divisor (as long as it needs at most two rounds) frees
+    // waves for the quantiser: its VALU work, not the weight stream, is then what the kernel waits for.
+    const int g = Mr * min(KB, nwk * S);
+    const int qw = quant_waves(g, nwk * nwc);
+    const int passes = (g + 16 * qw - 1) / (16 * qw) * ((KB + nwk * S - 1) / (nwk * S));
+    if (passes >= 5) {
+      int d = nwk - 1;
+      while (d >= 1 && KG % d != 0) --d;
+      if (d >= 1 && (KB + d * S - 1) / (d * S) <= 2) nwk = d;
+    }
     p.NCG = ncg; p.NKG = 1; p.NWC = nwc; p.NWK = nwk;
     break;
   }
@@ -854,9 +882,7 @@ Plan make_plan(int M, int N, int K) {
   }
   p.NWM = p.NWK * p.NWC;
   p.KC = p.NKG * p.NWK * S;
-  // quantising waves: about two 16-group passes each per round, between 2 and 8
-  const int groups = min(M, 32) * min(K / 128, p.KC);
-  p.QW = max(2, min((groups + 31) / 32, min(kMaxQuantWaves, 16 - p.NWM)));
+  p.QW = quant_waves(Mr * min(KB, p.KC), p.NWM);
   return p;
 }
 

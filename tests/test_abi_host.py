@@ -40,17 +40,30 @@ def test_launch_plans_balance_the_cus():
         assert p["NCG"] * p["NWC"] == p["CGW"]
         assert p["KC"] == p["NKG"] * p["NWK"] * (16 // p["C"])
         assert 4 <= p["NWK"] * p["NWC"] <= 12 and p["NWK"] * p["NWC"] + p["QW"] <= 16
+        # quantising waves: 2, or a multiple of 4 (the same number on every SIMD)
+        assert p["QW"] == 2 or p["QW"] % 4 == 0
     assert P.smallm_fp8bs_launch_plan(17, 4096, 2048)["MT"] == 2
     assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["MT"] == 1
     # activation tiles shared by 5 column groups: 8 waves, one K group of 4 blocks each
     p = P.smallm_fp8bs_launch_plan(4, 5120, 4096)
-    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (8, 1, 5, 1, 32)
+    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (8, 1, 5, 1, 32, 4)
+    # quantising waves follow the groups of a round: two 16-group passes each, 8 at most here
+    assert P.smallm_fp8bs_launch_plan(1, 5120, 4096)["QW"] == 2
+    assert P.smallm_fp8bs_launch_plan(16, 5120, 4096)["QW"] == 8
+    # from 24 rows, half the K split (two rounds) leaves room for 12 quantising waves
+    p = P.smallm_fp8bs_launch_plan(32, 5120, 4096)
+    assert (p["NWK"], p["NWC"], p["KC"], p["QW"]) == (4, 1, 16, 12)
     # 9 column groups: 3 x 3 column groups per wave, 4 K groups of 8 blocks
-    p = P.smallm_fp8bs_launch_plan(16, 4608, 4096)
+    p = P.smallm_fp8bs_launch_plan(8, 4608, 4096)
     assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (4, 3, 3, 1, 32, 4)
-    # two M tiles keep the same wave grid
-    p = P.smallm_fp8bs_launch_plan(32, 4608, 4096)
-    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (4, 3, 3, 1, 32)
+    # from 12 rows: 2 K groups per round (two rounds) and 8 quantising waves
+    for M in (12, 16, 32):
+        p = P.smallm_fp8bs_launch_plan(M, 4608, 4096)
+        assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (2, 3, 3, 1, 16, 8)
+    # one column group per workgroup: 12 quantising waves when a round holds 384 groups or more
+    assert P.smallm_fp8bs_launch_plan(16, 2048, 4096)["QW"] == 12
+    assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["QW"] == 8
+    assert P.smallm_fp8bs_launch_plan(32, 4096, 2048)["QW"] == 12
     # one column group per workgroup: K split over 4 waves, 4 fragments each per round
     p = P.smallm_fp8bs_launch_plan(4, 4096, 2048)
     assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (4, 1, 1, 4, 16)
