@@ -44,12 +44,14 @@
 extern "C" {
 #endif
 
-#define SMALLM_FP8BS_ABI_VERSION 2
+#define SMALLM_FP8BS_ABI_VERSION 3
 #define SMALLM_FP8BS_MAX_M 256
+#define SMALLM_FP8BS_RMS_MAX_M (1 << 20) /* rows of one producer call */
+#define SMALLM_FP8BS_RMS_MAX_H 16384     /* values per row of one producer call */
 
 typedef enum {
   SMALLM_OK = 0,
-  SMALLM_ERR_INVALID = 1, /* a required pointer is NULL */
+  SMALLM_ERR_INVALID = 1, /* a required pointer is NULL, or an invalid scalar argument */
   SMALLM_ERR_SHAPE = 2,   /* M, N, K or a leading dimension out of range */
   SMALLM_ERR_ALIGN = 3,   /* pointer or row pitch misaligned */
   SMALLM_ERR_LAYOUT = 4,  /* packed-weight layout id does not match this library */
@@ -141,6 +143,34 @@ int smallm_fp8bs_gemm(const uint8_t* q, int64_t ldq, const float* sx, const uint
 int smallm_fp8bs_gemm_e8m0(const uint8_t* q, int64_t ldq, const uint8_t* sx_e8m0,
                            const uint8_t* w_packed, uint32_t layout_id, const uint8_t* sw_e8m0,
                            uint16_t* y, int64_t ldy, int M, int N, int K, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * Producer: RMSNorm with the per-1x128 quantisation of its output
+ * ------------------------------------------------------------------------------------------ */
+
+/* The step before the GEMM, emitting the activation bytes and scales once for every consumer
+ * ("[Perf] [AMD] dsv4: optional e8m0 mxscale GEMM for dense 128x128 fp8 linears",
+ * Modifications and commit message: the fused input_norm / q_norm producers emit the
+ * activation scales, so no launch is added).  The page names the fusion, not its arithmetic;
+ * this library's reading, per row of H values:
+ *   ms = mean of x^2 taken exactly and rounded once to fp32;  v = RN32(ms + eps);
+ *   r  = RN32(1 / sqrt(v)), correctly rounded;  y = RNE_bf16(RN32(RN32(x * r) * w));
+ *   q, sx = exactly what smallm_fp8bs_quant gives for y (fp32 group scales).
+ * x: bf16 [M, ldx]; w: bf16 norm weight [H]; eps: positive finite fp32 (else
+ * SMALLM_ERR_INVALID); y: bf16 [M, ldy] or NULL (not written); q: e4m3 [M, ldq] or NULL, in
+ * which case sx is not written and the call is a plain RMSNorm (y must then be non-NULL);
+ * sx: fp32 [M, H/128].  1 <= M <= SMALLM_FP8BS_RMS_MAX_M; H a multiple of 128 in
+ * [128, SMALLM_FP8BS_RMS_MAX_H].  A row whose mean square exceeds the fp32 range is outside the
+ * contract (it normalises to zeros).  The mean is exact except when it lies within about 2^-48
+ * (relative) of an fp32 rounding boundary, where the per-lane fp64 sums may decide it. */
+int smallm_fp8bs_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* w, float eps,
+                               uint16_t* y, int64_t ldy, uint8_t* q, int64_t ldq, float* sx,
+                               int M, int H, void* stream);
+
+/* Same with ue8m0 group scales (q, sx as smallm_fp8bs_quant_e8m0 gives for y). */
+int smallm_fp8bs_rmsnorm_quant_e8m0(const uint16_t* x, int64_t ldx, const uint16_t* w, float eps,
+                                    uint16_t* y, int64_t ldy, uint8_t* q, int64_t ldq,
+                                    uint8_t* sx_e8m0, int M, int H, void* stream);
 
 /* The fused path (one launch): quantise x exactly as smallm_fp8bs_quant does, then the GEMM,
  * without writing q to memory.  If q_dbg / sx_dbg are non-NULL the kernel also writes the q

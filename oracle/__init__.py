@@ -17,8 +17,10 @@ passage of the pages it follows in the C source:
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
+from fractions import Fraction
 
 import numpy as np
 
@@ -206,3 +208,104 @@ def quant_gemm(x_bits: np.ndarray, w8: np.ndarray, sw: np.ndarray, e8m0: bool = 
 
 def max_threads() -> int:
     return int(lib().oracle_max_threads())
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm producer with per-1x128 quantisation (the step before the GEMM)
+# ---------------------------------------------------------------------------------------------
+# sglang "[Perf] [AMD] dsv4: optional e8m0 mxscale GEMM for dense 128x128 fp8 linears",
+# Modifications and commit message: the fused input_norm / q_norm producers emit the activation
+# quantisation (ue8m0 scales when every consumer uses the e8m0 GEMM) so that no launch is added.
+# The pages name the fusion but not its arithmetic; the reading taken here, per row of H values:
+#   ms = mean of x^2, taken exactly and rounded once to fp32;
+#   v  = RN32(ms + eps);  r = RN32(1 / sqrt(v)), correctly rounded;
+#   y  = RNE_bf16(RN32(RN32(x * r) * w))   (w: the bf16 norm weight);
+#   q, sx = the 1x128 activation quantisation of y (quant_act), fp32 or ue8m0 scales.
+# So the quantised bytes are those the separate RMSNorm then quant launches would give.
+
+def _rn32_ratio(p: int, d: int) -> float:
+    """IEEE binary32 round-to-nearest-even of the positive rational p / d (inf above the range)."""
+    assert p >= 0 and d > 0
+    if p == 0:
+        return 0.0
+    e = p.bit_length() - d.bit_length()          # p / d in [2^(e-1), 2^(e+1))
+    if (p << max(0, -e)) < (d << max(0, e)):     # p / d < 2^e
+        e -= 1
+    e = max(e, -126)                              # subnormals share the 2^-149 quantum
+    sh = 23 - e                                   # quantum 2^(e - 23)
+    num, den = (p << sh, d) if sh >= 0 else (p, d << -sh)
+    fl, rem = divmod(num, den)
+    if 2 * rem > den or (2 * rem == den and fl & 1):
+        fl += 1
+    if fl.bit_length() + (e - 23) > 128:          # fl * 2^(e-23) >= 2^128
+        return math.inf
+    return math.ldexp(fl, e - 23)
+
+
+def _bf16_parts(bits: np.ndarray):
+    """bf16 patterns -> (integer significand, power of two): |value| = sig * 2^p2."""
+    bits = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    ef = (bits >> 7) & 0xFF
+    fr = bits & 0x7F
+    sig = np.where(ef == 0, fr, fr | 0x80)
+    p2 = np.where(ef == 0, -133, ef - 134)
+    return sig, p2
+
+
+def mean_square_f32(x_row_bits: np.ndarray) -> float:
+    """RN32(sum x^2 / H) for one bf16 row, the sum taken exactly (integers scaled by 2^-266)."""
+    sig, p2 = _bf16_parts(x_row_bits)
+    total = 0
+    for s, e in zip(sig.tolist(), p2.tolist()):
+        if s:
+            total += (s * s) << (2 * e + 266)
+    return _rn32_ratio(total, len(sig) << 266)
+
+
+def rsqrt_f32(v: float) -> float:
+    """RN32(1 / sqrt(v)) for a positive finite fp32 v, correctly rounded: a candidate from the
+    double-precision formula, then moved until 1/sqrt(v) lies between the midpoints with its
+    fp32 neighbours (compared exactly as rationals: m^2 v against 1)."""
+    assert v > 0 and math.isfinite(v)
+    V = Fraction(v)
+    r = np.float32(1.0 / math.sqrt(v))
+    for _ in range(8):
+        up = np.nextafter(r, np.float32(np.inf))
+        dn = np.nextafter(r, np.float32(0))
+        mu = (Fraction(float(r)) + Fraction(float(up))) / 2
+        ml = (Fraction(float(r)) + Fraction(float(dn))) / 2
+        if mu * mu * V < 1:
+            r = up
+        elif ml * ml * V > 1:
+            r = dn
+        else:
+            assert mu * mu * V != 1 and ml * ml * V != 1   # no ties: 1/sqrt(v) is never a midpoint
+            return float(r)
+    raise AssertionError("rsqrt_f32 did not settle")
+
+
+def rmsnorm(x_bits: np.ndarray, w_bits: np.ndarray, eps: float):
+    """x_bits bf16 [M, H], w_bits bf16 [H], eps > 0 (fp32).  Returns (y bf16 bits [M, H],
+    r float32 [M]) with the reading stated above."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, H = x_bits.shape
+    eps32 = np.float32(eps)
+    assert eps32 > 0
+    r = np.empty(M, dtype=np.float32)
+    for m in range(M):
+        ms = np.float32(mean_square_f32(x_bits[m]))
+        v = np.float32(ms + eps32)                 # one fp32 addition
+        r[m] = np.float32(rsqrt_f32(float(v)))
+    xf = bf16_to_f32(x_bits)
+    wf = bf16_to_f32(np.asarray(w_bits, dtype=np.uint16))
+    t = (xf * r[:, None]).astype(np.float32)       # RN32(x * r)
+    yf = (t * wf[None, :]).astype(np.float32)       # RN32(t * w)
+    y = round_bf16(yf.astype(np.float64))
+    return y, r
+
+
+def rmsnorm_quant(x_bits: np.ndarray, w_bits: np.ndarray, eps: float, e8m0: bool = False):
+    """Producer: (y bf16 bits [M, H], q e4m3 [M, H], sx fp32 or e8m0 [M, H/128])."""
+    y, _ = rmsnorm(x_bits, w_bits, eps)
+    q, sx = quant_act(y, e8m0=e8m0)
+    return y, q, sx

@@ -45,6 +45,8 @@ EXPORTS = (
     "smallm_fp8bs_gemm_e8m0",
     "smallm_fp8bs_quant_gemm",
     "smallm_fp8bs_quant_gemm_e8m0",
+    "smallm_fp8bs_rmsnorm_quant",
+    "smallm_fp8bs_rmsnorm_quant_e8m0",
 )
 
 
@@ -101,6 +103,8 @@ def lib():
         "smallm_fp8bs_gemm_e8m0": (I, [P, I64, P, P, U32, P, P, I64, I, I, I, P]),
         "smallm_fp8bs_quant_gemm": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
         "smallm_fp8bs_quant_gemm_e8m0": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
+        "smallm_fp8bs_rmsnorm_quant": (I, [P, I64, P, ctypes.c_float, P, I64, P, I64, P, I, I, P]),
+        "smallm_fp8bs_rmsnorm_quant_e8m0": (I, [P, I64, P, ctypes.c_float, P, I64, P, I64, P, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -266,6 +270,44 @@ def smallm_fp8bs_quant_e8m0(x, q=None, sx=None, stream=None):
     _check(lib().smallm_fp8bs_quant_e8m0(_ptr(x), x.stride(0), _ptr(q), q.stride(0), _ptr(sx), M, K,
                                          _stream(stream)), "smallm_fp8bs_quant_e8m0")
     return q, sx
+
+
+def _rmsnorm_quant(x, w, eps, y, q, sx, emit_y, emit_q, e8m0, stream):
+    _need(x, _BF, "x")
+    M, H = x.shape
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or not w.is_cuda:
+        raise TypeError("w must be a bf16 device tensor")
+    if w.dim() != 1 or w.shape[0] != H or not w.is_contiguous():
+        raise ValueError(f"w must be contiguous of shape [{H}]")
+    if emit_y and y is None:
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    if emit_q:
+        q = torch.empty((M, H), dtype=torch.uint8, device=x.device) if q is None else q
+        sdt = torch.uint8 if e8m0 else torch.float32
+        sx = torch.empty((M, H // 128), dtype=sdt, device=x.device) if sx is None else sx
+    else:
+        q = sx = None
+    if y is not None:
+        _need(y, _BF, "y")
+    if q is not None:
+        _need(q, _F8, "q")
+        _contig(sx, "sx")
+    fn = lib().smallm_fp8bs_rmsnorm_quant_e8m0 if e8m0 else lib().smallm_fp8bs_rmsnorm_quant
+    _check(fn(_ptr(x), x.stride(0), _ptr(w), ctypes.c_float(eps), _ptr(y), y.stride(0) if y is not None else 0,
+              _ptr(q), q.stride(0) if q is not None else 0, _ptr(sx), M, H, _stream(stream)),
+           "smallm_fp8bs_rmsnorm_quant" + ("_e8m0" if e8m0 else ""))
+    return y, q, sx
+
+
+def smallm_fp8bs_rmsnorm_quant(x, w, eps, y=None, q=None, sx=None, emit_y=True, emit_q=True, stream=None):
+    """RMSNorm of bf16 x [M, H] with bf16 weight w [H], then the 1x128 quantisation of the bf16
+    output with fp32 group scales.  Returns (y or None, q or None, sx or None)."""
+    return _rmsnorm_quant(x, w, eps, y, q, sx, emit_y, emit_q, False, stream)
+
+
+def smallm_fp8bs_rmsnorm_quant_e8m0(x, w, eps, y=None, q=None, sx=None, emit_y=True, emit_q=True, stream=None):
+    """As smallm_fp8bs_rmsnorm_quant with ue8m0 group scales."""
+    return _rmsnorm_quant(x, w, eps, y, q, sx, emit_y, emit_q, True, stream)
 
 
 def _check_weight(w_packed, sw, K, e8m0):

@@ -315,6 +315,149 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
+// producer: RMSNorm of a row, then the 1x128 quantisation of its bf16 output
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kRmsChunks = 2;  // 32 values per lane and chunk: rows of up to 2 * 32 * 256 values
+
+// Knuth's TwoSum: a + b = t + e exactly, t = RN(a + b).
+__device__ __forceinline__ void two_sum(double a, double b, double& t, double& e) {
+  t = a + b;
+  const double bp = t - a;
+  e = (a - (t - bp)) + (b - bp);
+}
+
+// (s, c) += (s2, c2) as unevaluated sums; symmetric in its two operands.
+__device__ __forceinline__ void dd_add(double& s, double& c, double s2, double c2) {
+  double t, e;
+  two_sum(s, s2, t, e);
+  s = t;
+  c = (c + c2) + e;
+}
+
+__device__ __forceinline__ float next_up_pos(float f) { return __uint_as_float(__float_as_uint(f) + 1u); }
+__device__ __forceinline__ float next_dn_pos(float f) {
+  return f > 0.0f ? __uint_as_float(__float_as_uint(f) - 1u) : 0.0f;
+}
+
+// RN32((S + C) / H) for a non-negative double-double S + C: the fp64 candidate, then compared with
+// the midpoints to its fp32 neighbours exactly (mid * H is exact in fp64 and, being within a
+// factor of two of S, so is mid * H - S; subtracting C keeps the sign), ties to even.
+__device__ __forceinline__ float rn32_dd_over(double S, double C, int H) {
+  float f = (float)((S + C) / (double)H);
+  if (!(f <= 3.40282347e38f)) return f;  // beyond the fp32 range: +inf
+  const double dh = (double)H;
+  const float up = next_up_pos(f), dn = next_dn_pos(f);
+  const double du = __builtin_fma(0.5 * ((double)f + (double)up), dh, -S) - C;
+  const double dl = __builtin_fma(0.5 * ((double)f + (double)dn), dh, -S) - C;
+  const bool odd = (__float_as_uint(f) & 1u) != 0;
+  if (du < 0.0 || (du == 0.0 && odd)) return up;
+  if (f > 0.0f && (dl > 0.0 || (dl == 0.0 && odd))) return dn;
+  return f;
+}
+
+// RN32(1 / sqrt(v)) for a positive fp32 v, correctly rounded: the fp64 candidate, then the
+// midpoint m to each fp32 neighbour is tested exactly through the sign of m^2 v - 1 (m^2 is exact
+// in fp64, the FMA rounds once).  1 / sqrt(v) is never a midpoint, so there are no ties.
+__device__ __forceinline__ float rsqrt_rn32(float v) {
+  if (!(v <= 3.40282347e38f)) return 0.0f;
+  float r = (float)(1.0 / __builtin_sqrt((double)v));
+  const double mu = 0.5 * ((double)r + (double)next_up_pos(r));
+  const double ml = 0.5 * ((double)r + (double)next_dn_pos(r));
+  if (__builtin_fma(mu * mu, (double)v, -1.0) < 0.0) return next_up_pos(r);
+  if (__builtin_fma(ml * ml, (double)v, -1.0) > 0.0) return next_dn_pos(r);
+  return r;
+}
+
+// One workgroup per row; lane l of the row holds values 32 l .. 32 l + 31 (a DPP quad per 1x128
+// group).  Mean square: exact squares summed in fp64 per lane, then across lanes and waves as
+// double-double sums in a fixed order, rounded once to fp32.  y = RN32(RN32(x r) w) rounded to
+// bf16; q and sx are then exactly those of the standalone quantisation of y.  y and q may be
+// null (not written); with q null, sx is not written either.
+template <bool E8M0>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, float eps,
+    uint16_t* __restrict__ y, int64_t ldy, uint8_t* __restrict__ q, int64_t ldq,
+    void* __restrict__ sx, int H) {
+  __shared__ double red[2][4];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int nt = blockDim.x, nw = nt >> 6;
+  const int nl = H >> 5;
+  const uint16_t* xr = x + (int64_t)m * ldx;
+  u32x4 xv[kRmsChunks][4];
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kRmsChunks; ++k) {
+    const int l = tid + k * nt;
+    const bool valid = l < nl;
+    const u32x4* xp = (const u32x4*)(xr + (int64_t)(valid ? l : 0) * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[k][i] = valid ? xp[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t d = xv[k][i >> 2][i & 3];
+      const double a = (double)__uint_as_float(d << 16), b = (double)__uint_as_float(d & 0xFFFF0000u);
+      s = __builtin_fma(a, a, s);
+      s = __builtin_fma(b, b, s);
+    }
+  }
+  // across the wave (xor butterfly: every lane ends with the same sum), then across the waves
+  double c = 0.0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double s2 = __shfl_xor(s, off), c2 = __shfl_xor(c, off);
+    dd_add(s, c, s2, c2);
+  }
+  if ((tid & 63) == 0) { red[0][wave] = s; red[1][wave] = c; }
+  __syncthreads();
+  double S = red[0][0], C = red[1][0];
+  for (int i = 1; i < nw; ++i) dd_add(S, C, red[0][i], red[1][i]);
+  const float ms = rn32_dd_over(S, C, H);
+  const float r = rsqrt_rn32(ms + eps);
+
+#pragma unroll
+  for (int k = 0; k < kRmsChunks; ++k) {
+    const int l = tid + k * nt;
+    if (k * nt >= nl) break;  // no lane of this chunk holds values (uniform)
+    const bool valid = l < nl;
+    u32x4 wv[4], yv[4];
+    const u32x4* wp = (const u32x4*)(w + (valid ? l : 0) * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = valid ? wp[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t d = xv[k][i >> 2][i & 3], e = wv[i >> 2][i & 3];
+      const float y0 = (__uint_as_float(d << 16) * r) * __uint_as_float(e << 16);
+      const float y1 = (__uint_as_float(d & 0xFFFF0000u) * r) * __uint_as_float(e & 0xFFFF0000u);
+      yv[i >> 2][i & 3] = (uint32_t)bf16_rne(y0) | ((uint32_t)bf16_rne(y1) << 16);
+    }
+    if (y != nullptr && valid) {
+      u32x4* yp = (u32x4*)(y + (int64_t)m * ldy + l * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yp[i] = yv[i];
+    }
+    if (q != nullptr) {
+      // every lane of the wave takes part in the group reductions; invalid quads are whole groups
+      u32x4 qv[2];
+      const int g = l >> 2, KB = H >> 7;
+      if (!E8M0) {
+        const float sc = quant32_fp32(yv, qv);
+        if (valid && (l & 3) == 0) ((float*)sx)[(int64_t)m * KB + g] = sc;
+      } else {
+        const uint32_t e = quant32_e8m0(yv, qv);
+        if (valid && (l & 3) == 0) ((uint8_t*)sx)[(int64_t)m * KB + g] = (uint8_t)e;
+      }
+      if (valid) {
+        u32x4* qp = (u32x4*)(q + (int64_t)m * ldq + l * 32);
+        qp[0] = qv[0];
+        qp[1] = qv[1];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // the GEMM (fused quant or pre-quantised input; fp32 or e8m0 scales)
 // ---------------------------------------------------------------------------------------------
 
@@ -1052,6 +1195,40 @@ int smallm_fp8bs_quant(const uint16_t* x, int64_t ldx, uint8_t* q, int64_t ldq, 
 int smallm_fp8bs_quant_e8m0(const uint16_t* x, int64_t ldx, uint8_t* q, int64_t ldq,
                             uint8_t* sx_e8m0, int M, int K, void* stream) {
   return quant_common(x, ldx, q, ldq, (void*)sx_e8m0, M, K, true, stream);
+}
+
+static int rmsnorm_quant_common(const uint16_t* x, int64_t ldx, const uint16_t* w, float eps,
+                                uint16_t* y, int64_t ldy, uint8_t* q, int64_t ldq, void* sx, int M,
+                                int H, bool e8, void* stream) {
+  if (!x || !w || (q && !sx) || (!q && !y)) return SMALLM_ERR_INVALID;
+  if (!(eps > 0.0f) || !(eps <= 3.40282347e38f)) return SMALLM_ERR_INVALID;
+  if (M < 1 || M > SMALLM_FP8BS_RMS_MAX_M || H < 128 || (H & 127) || H > SMALLM_FP8BS_RMS_MAX_H ||
+      ldx < H || (y && ldy < H) || (q && ldq < H))
+    return SMALLM_ERR_SHAPE;
+  if (!aligned16(x) || ((ldx * 2) & 15) || !aligned16(w) || (y && (!aligned16(y) || ((ldy * 2) & 15))) ||
+      (q && (!aligned16(q) || (ldq & 15))))
+    return SMALLM_ERR_ALIGN;
+  const int nl = H / 32;
+  const int nt = nl >= 256 ? 256 : (nl + 63) / 64 * 64;
+  if (e8)
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<true>), dim3(M), dim3(nt), 0, (hipStream_t)stream, x,
+                       ldx, w, eps, y, ldy, q, ldq, sx, H);
+  else
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<false>), dim3(M), dim3(nt), 0, (hipStream_t)stream, x,
+                       ldx, w, eps, y, ldy, q, ldq, sx, H);
+  return launch_status();
+}
+
+int smallm_fp8bs_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* w, float eps,
+                               uint16_t* y, int64_t ldy, uint8_t* q, int64_t ldq, float* sx, int M,
+                               int H, void* stream) {
+  return rmsnorm_quant_common(x, ldx, w, eps, y, ldy, q, ldq, (void*)sx, M, H, false, stream);
+}
+
+int smallm_fp8bs_rmsnorm_quant_e8m0(const uint16_t* x, int64_t ldx, const uint16_t* w, float eps,
+                                    uint16_t* y, int64_t ldy, uint8_t* q, int64_t ldq,
+                                    uint8_t* sx_e8m0, int M, int H, void* stream) {
+  return rmsnorm_quant_common(x, ldx, w, eps, y, ldy, q, ldq, (void*)sx_e8m0, M, H, true, stream);
 }
 
 int smallm_fp8bs_gemm(const uint8_t* q, int64_t ldq, const float* sx, const uint8_t* w_packed,

@@ -76,7 +76,7 @@ def test_launch_plans_balance_the_cus():
 
 
 def test_version_layout_and_strerror():
-    assert P.smallm_fp8bs_abi_version() == 2
+    assert P.smallm_fp8bs_abi_version() == 3
     # columns per group: the widest C in {16, 8, 4, 2} giving a multiple of 256 column groups
     assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46380210
     assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46380204
@@ -138,6 +138,33 @@ def test_rejections_happen_before_any_launch():
     # a weight packed for another shape's layout is refused
     lid5120 = P.smallm_fp8bs_weight_layout_id(5120, 4096)
     assert L.smallm_fp8bs_quant_gemm(f, 4096, f, lid5120, f, f, 4608, 4, 4608, 4096, None, None, None) == 4
+
+
+def test_producer_rejections_happen_before_any_launch():
+    """smallm_fp8bs_rmsnorm_quant(_e8m0): bad pointers, eps, shapes and alignment are refused on
+    the host (argument order: x, ldx, w, eps, y, ldy, q, ldq, sx, M, H, stream)."""
+    L = P.lib()
+    f = _fake()
+    for fn in (L.smallm_fp8bs_rmsnorm_quant, L.smallm_fp8bs_rmsnorm_quant_e8m0):
+        assert fn(None, 4096, f, 1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 1      # no x
+        assert fn(f, 4096, None, 1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 1      # no w
+        assert fn(f, 4096, f, 1e-6, None, 0, None, 0, None, 4, 4096, None) == 1      # no output
+        assert fn(f, 4096, f, 1e-6, f, 4096, f, 4096, None, 4, 4096, None) == 1      # q without sx
+        assert fn(f, 4096, f, 0.0, f, 4096, f, 4096, f, 4, 4096, None) == 1          # eps <= 0
+        assert fn(f, 4096, f, -1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 1
+        assert fn(f, 4096, f, float("inf"), f, 4096, f, 4096, f, 4, 4096, None) == 1
+        assert fn(f, 4096, f, float("nan"), f, 4096, f, 4096, f, 4, 4096, None) == 1
+        assert fn(f, 4096, f, 1e-6, f, 4096, f, 4096, f, 0, 4096, None) == 2         # M = 0
+        assert fn(f, 4096, f, 1e-6, f, 4096, f, 4096, f, 4, 4000, None) == 2         # H % 128
+        assert fn(f, 32768, f, 1e-6, f, 32768, f, 32768, f, 4, 32768, None) == 2    # H too long
+        assert fn(f, 4000, f, 1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 2         # ldx < H
+        assert fn(f, 4096, f, 1e-6, f, 4000, f, 4096, f, 4, 4096, None) == 2         # ldy < H
+        assert fn(f, 4096, f, 1e-6, f, 4096, f, 4000, f, 4, 4096, None) == 2         # ldq < H
+        assert fn(_fake(0x10008), 4096, f, 1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 3
+        assert fn(f, 4100, f, 1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 3         # x pitch
+        assert fn(f, 4096, _fake(0x10002), 1e-6, f, 4096, f, 4096, f, 4, 4096, None) == 3
+        assert fn(f, 4096, f, 1e-6, f, 4100, f, 4096, f, 4, 4096, None) == 3         # y pitch
+        assert fn(f, 4096, f, 1e-6, f, 4096, f, 4104, f, 4, 4096, None) == 3         # q pitch
 
 
 def test_binding_rejects_wrong_dtypes_without_gpu():

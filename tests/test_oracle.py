@@ -475,3 +475,136 @@ def test_quant_gemm_column_window_and_bf16(oracle_lib):
     y2, ref2, _, _ = oracle.quant_gemm(x, w8, sw, n0=128, n1=256, threads=2)
     assert np.array_equal(ref2[:, 128:256], full[:, 128:256])
     assert np.all(ref2[:, :128] == 0) and np.all(ref2[:, 256:] == 0)
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm producer (mean square exact then rounded to fp32, correctly rounded fp32 rsqrt,
+# fp32 products, bf16 output, then the 1x128 quantisation)
+# ---------------------------------------------------------------------------------------------
+
+def round_fraction_to_bf16_bits(v: Fraction) -> int:
+    """Exact bf16 round-to-nearest-even of a rational (8 significant bits, quantum 2^-133 at the
+    bottom), as a bit pattern; independent of the oracle's bf16 rounding."""
+    neg = v < 0
+    a = -v if neg else v
+    if a == 0:
+        return 0x8000 if neg else 0
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 7)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * quantum
+    bits = int(np.array([np.float32(float(r))], dtype=np.float32).view(np.uint32)[0]) >> 16
+    return bits | (0x8000 if neg else 0)
+
+
+def decimal_rsqrt_f32(v: float) -> Fraction:
+    """RN32(1 / sqrt(v)) from an 80-digit decimal square root and exact rational rounding."""
+    getcontext().prec = 80
+    d = Decimal(1) / Decimal(v).sqrt()
+    return round_fraction_to_f32(Fraction(d))
+
+
+def rmsnorm_by_fractions(x_bits, w_bits, eps32):
+    """The producer's RMSNorm in exact rationals, row by row (slow; small shapes only)."""
+    M, H = x_bits.shape
+    xs = synthgen.bf16_bits_to_f32(x_bits)
+    ws = synthgen.bf16_bits_to_f32(w_bits)
+    y = np.zeros((M, H), dtype=np.uint16)
+    for m in range(M):
+        ss = sum(Fraction(float(a)) ** 2 for a in xs[m])
+        ms = round_fraction_to_f32(ss / H)
+        v = round_fraction_to_f32(ms + Fraction(float(eps32)))
+        r = decimal_rsqrt_f32(float(v))
+        for i in range(H):
+            t = round_fraction_to_f32(Fraction(float(xs[m, i])) * r)
+            u = round_fraction_to_f32(t * Fraction(float(ws[i])))
+            y[m, i] = round_fraction_to_bf16_bits(u)
+            if u == 0 and math.copysign(1.0, float(xs[m, i])) * math.copysign(1.0, float(ws[i])) < 0:
+                y[m, i] = 0x8000
+    return y
+
+
+def test_rmsnorm_unit_row_returns_the_weight(oracle_lib):
+    # all-ones row: mean square 1, eps far below half an ulp of 1, so r = 1 and y = w exactly
+    rng = np.random.default_rng([5, 1])
+    w = synthgen.f32_to_bf16_bits(rng.normal(0.0, 2.0, 256).astype(np.float32))
+    x = np.full((2, 256), 0x3F80, dtype=np.uint16)
+    y, r = oracle.rmsnorm(x, w, 2.0 ** -40)
+    assert np.all(r == 1.0)
+    assert np.array_equal(y, np.stack([w, w]))
+
+
+def test_rmsnorm_hand_worked_3_4_row(oracle_lib):
+    # x = (3, 4, 0, ..., 0), H = 128: sum of squares 25, mean 25/128 = 0.1953125 exactly;
+    # eps = 2^-30 is below half an ulp (2^-27) of it, so v = 25/128 and r = RN32(sqrt(5.12))
+    x = np.zeros((1, 128), dtype=np.uint16)
+    x[0, 0] = 0x4040   # 3.0
+    x[0, 1] = 0x4080   # 4.0
+    w = np.full(128, 0x3F80, dtype=np.uint16)
+    assert oracle.mean_square_f32(x[0]) == 0.1953125
+    y, r = oracle.rmsnorm(x, w, 2.0 ** -30)
+    getcontext().prec = 80
+    r_ref = round_fraction_to_f32(Fraction(Decimal("5.12").sqrt()))
+    assert Fraction(float(r[0])) == r_ref
+    assert float(r[0]) == pytest.approx(2.2627417, abs=3e-7)
+    assert y[0, 0] == round_fraction_to_bf16_bits(round_fraction_to_f32(3 * r_ref))
+    assert y[0, 1] == round_fraction_to_bf16_bits(round_fraction_to_f32(4 * r_ref))
+    assert y[0, 0] == 0x40D9 and y[0, 1] == 0x4111   # 6.78125 and 9.0625
+    assert np.all(y[0, 2:] == 0)
+
+
+@pytest.mark.parametrize("H", [128, 384])
+def test_rmsnorm_matches_exact_rational_reference(oracle_lib, H):
+    rng = np.random.default_rng([7, H])
+    x = synthgen.gen_x(3, H, seed=H, outliers=True)
+    x[2, :] = synthgen.f32_to_bf16_bits(synthgen.bf16_bits_to_f32(x[2, :]) * np.float32(1e-20))
+    w = synthgen.f32_to_bf16_bits(rng.normal(1.0, 0.3, H).astype(np.float32))
+    eps = np.float32(1e-6)
+    y, _ = oracle.rmsnorm(x, w, float(eps))
+    assert np.array_equal(y, rmsnorm_by_fractions(x, w, eps))
+
+
+def test_rmsnorm_rsqrt_against_decimal_on_edge_values(oracle_lib):
+    vals = [2.0 ** -126, 2.0 ** -20, 0.1953125, 1.0, 2.0, 3.0, 1e-6, 12345.678, 2.0 ** 100,
+            float(np.float32(3.4e38))]
+    rng = np.random.default_rng([9, 9])
+    vals += [float(np.float32(v)) for v in rng.uniform(1e-7, 1e7, 40)]
+    for v in vals:
+        v = float(np.float32(v))
+        assert Fraction(oracle.rsqrt_f32(v)) == decimal_rsqrt_f32(v), v
+
+
+def test_rmsnorm_permutation_and_power_of_two_scale_invariance(oracle_lib):
+    rng = np.random.default_rng([11, 2])
+    x = synthgen.gen_x(4, 512, seed=3)
+    w = synthgen.f32_to_bf16_bits(rng.normal(1.0, 0.5, 512).astype(np.float32))
+    y, _ = oracle.rmsnorm(x, w, 1e-6)
+    perm = rng.permutation(512)
+    yp, _ = oracle.rmsnorm(np.ascontiguousarray(x[:, perm]), w[perm], 1e-6)
+    assert np.array_equal(yp, y[:, perm])            # the mean is exact: order does not matter
+    xs = synthgen.f32_to_bf16_bits(synthgen.bf16_bits_to_f32(x) * np.float32(32.0))
+    ys, _ = oracle.rmsnorm(xs, w, 1e-6 * 1024.0)
+    assert np.array_equal(ys, y)                      # x * 2^5 with eps * 2^10: same output
+
+
+def test_rmsnorm_quant_zero_row_keeps_signs(oracle_lib):
+    x = np.zeros((1, 256), dtype=np.uint16)
+    x[0, 1::2] = 0x8000                               # -0.0 at odd positions
+    w = np.full(256, 0x3F80, dtype=np.uint16)
+    w[::4] = 0xBF80                                   # -1.0 at every fourth position
+    y, q, sx = oracle.rmsnorm_quant(x, w, 1e-6)
+    sign = (np.arange(256) % 2 == 1) ^ (np.arange(256) % 4 == 0)
+    assert np.array_equal(y[0], np.where(sign, 0x8000, 0).astype(np.uint16))
+    assert np.array_equal(q[0], np.where(sign, 0x80, 0).astype(np.uint8))
+    assert np.all(sx == 0)
+    _, q8, sx8 = oracle.rmsnorm_quant(x, w, 1e-6, e8m0=True)
+    assert np.array_equal(q8[0], q[0]) and np.all(sx8 == 0)   # E = -127 for an all-zero group
