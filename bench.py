@@ -107,11 +107,84 @@ def time_config(P, torch, np, synthgen, dev, N, K, Ms, copies, reps, e8m0=False,
     return out, ys
 
 
+def graph_us(torch, fn, copies, reps):
+    """us per layer of a HIP graph of `copies` layers, layer i issued by fn(i), replayed `reps`
+    times after warm-up, timed with HIP events on the replay stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(copies):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            fn(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * copies)
+
+
+def producer_pipeline(P, torch, np, synthgen, dev, copies, reps, N=5120, K=4096):
+    """The producer-side fusion: per layer, (a) a plain RMSNorm then the fused quant+GEMM, and
+    (b) RMSNorm with the 1x128 quantisation then the GEMM on pre-quantised input, each kernel
+    also timed alone; 24 layers on distinct weight copies in one graph, both scale types."""
+    res = {}
+    rng = np.random.default_rng([3, 3])
+    wn_bits = synthgen.f32_to_bf16_bits(rng.normal(1.0, 0.2, K).astype(np.float32))
+    wn = torch.from_numpy(wn_bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    for e8m0 in (False, True):
+        qw = P.smallm_fp8bs_quant_weight_e8m0 if e8m0 else P.smallm_fp8bs_quant_weight
+        prod = P.smallm_fp8bs_rmsnorm_quant_e8m0 if e8m0 else P.smallm_fp8bs_rmsnorm_quant
+        fused = P.smallm_fp8bs_quant_gemm_e8m0 if e8m0 else P.smallm_fp8bs_quant_gemm
+        preq = P.smallm_fp8bs_gemm_e8m0 if e8m0 else P.smallm_fp8bs_gemm
+        wps, sws = [], []
+        for i in range(copies):
+            w = torch.from_numpy(synthgen.gen_w(N, K, seed=0, copy=i)).to(dev)
+            w8, sw = qw(w)
+            wps.append(P.smallm_fp8bs_pack_weight(w8))
+            sws.append(sw)
+            del w, w8
+        d = {}
+        for M in M_SWEEP:
+            x = torch.from_numpy(synthgen.gen_x(M, K, seed=0).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+            y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            sx = torch.empty((M, K // 128), dtype=torch.uint8 if e8m0 else torch.float32, device=dev)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            t = {
+                "rmsnorm_us": graph_us(torch, lambda i: prod(x, wn, 1e-6, y=y, emit_q=False), copies, reps),
+                "rmsnorm_quant_us": graph_us(torch, lambda i: prod(x, wn, 1e-6, q=q, sx=sx, emit_y=False), copies, reps),
+                "fused_gemm_us": graph_us(torch, lambda i: fused(y, wps[i], sws[i], y=out), copies, reps),
+                "prequantised_gemm_us": graph_us(torch, lambda i: preq(q, sx, wps[i], sws[i], y=out), copies, reps),
+                "rmsnorm_then_fused_us": graph_us(torch, lambda i: (prod(x, wn, 1e-6, y=y, emit_q=False),
+                                                                     fused(y, wps[i], sws[i], y=out)), copies, reps),
+                "rmsnorm_quant_then_prequantised_us": graph_us(torch, lambda i: (prod(x, wn, 1e-6, q=q, sx=sx, emit_y=False),
+                                                                                  preq(q, sx, wps[i], sws[i], y=out)), copies, reps),
+            }
+            d[str(M)] = {k: round(v, 3) for k, v in t.items()}
+            log(f"[bench] producer {'e8m0' if e8m0 else 'fp32'} M={M}: norm+fused {t['rmsnorm_then_fused_us']:.2f} "
+                f"producer+prequantised {t['rmsnorm_quant_then_prequantised_us']:.2f} us/layer")
+        res[f"producer_pipeline_{N}x{K}_{'e8m0' if e8m0 else 'fp32'}"] = d
+        del wps, sws
+        torch.cuda.empty_cache()
+    return res
+
+
 def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
     """The other workloads of the method, timed the same way (per-M us/call, GB/s, % of peak):
     the single 4096x2048 call at M=4; the M sweeps on 4608x4096 and 4096x2048 with outlier rows;
-    M = 33..256 on 4096x2048 with the MFMA rate beside the bandwidth; and the e8m0-scale path on
-    4096x2048 and 2048x4096 beside the fp32-scale path on the same data."""
+    M = 33..256 on 4096x2048 with the MFMA rate beside the bandwidth; the e8m0-scale path on
+    4096x2048 and 2048x4096 beside the fp32-scale path on the same data; and the producer-side
+    fusion (RMSNorm with the quantisation, then the GEMM on pre-quantised input) on 5120x4096."""
     res = {}
 
     def entry(N, K, M, us, e8m0=False):
@@ -147,6 +220,7 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
                          "max_abs_diff_over_max_abs": round(rel, 5)}
         res[f"e8m0_vs_fp32_{N}x{K}"] = d
         log(f"[bench] {N}x{K} e8m0 vs fp32: " + " ".join(f"M={M} {te[M]:.2f}/{tf[M]:.2f}us" for M in ms))
+    res.update(producer_pipeline(P, torch, np, synthgen, dev, copies, reps))
     return res
 
 

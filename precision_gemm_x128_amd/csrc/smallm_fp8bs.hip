@@ -335,6 +335,28 @@ __device__ __forceinline__ void dd_add(double& s, double& c, double s2, double c
   c = (c + c2) + e;
 }
 
+// An fp64 value from another lane of the same row of 16 (DPP), as two 32-bit moves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dd_add_dpp(double& s, double& c) {
+  const double s2 = dpp_f64<CTRL>(s), c2 = dpp_f64<CTRL>(c);
+  dd_add(s, c, s2, c2);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ float next_up_pos(float f) { return __uint_as_float(__float_as_uint(f) + 1u); }
 __device__ __forceinline__ float next_dn_pos(float f) {
   return f > 0.0f ? __uint_as_float(__float_as_uint(f) - 1u) : 0.0f;
@@ -385,15 +407,21 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   const int nt = blockDim.x, nw = nt >> 6;
   const int nl = H >> 5;
   const uint16_t* xr = x + (int64_t)m * ldx;
-  u32x4 xv[kRmsChunks][4];
-  double s = 0.0;
+  u32x4 xv[kRmsChunks][4], wv[kRmsChunks][4];
 #pragma unroll
-  for (int k = 0; k < kRmsChunks; ++k) {
+  for (int k = 0; k < kRmsChunks; ++k) {  // the row and the weight, both loaded up front
     const int l = tid + k * nt;
     const bool valid = l < nl;
     const u32x4* xp = (const u32x4*)(xr + (int64_t)(valid ? l : 0) * 32);
+    const u32x4* wp = (const u32x4*)(w + (valid ? l : 0) * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) xv[k][i] = valid ? xp[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[k][i] = valid ? wp[i] : u32x4{0, 0, 0, 0};
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kRmsChunks; ++k) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t d = xv[k][i >> 2][i & 3];
@@ -402,14 +430,19 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
       s = __builtin_fma(b, b, s);
     }
   }
-  // across the wave (xor butterfly: every lane ends with the same sum), then across the waves
+  // within each row of 16 lanes by DPP (lane pairs 1, 2, then the half and full row mirrors:
+  // every lane of the row ends with the same sum), the four rows from lanes 0, 16, 32, 48 in a
+  // fixed order, then across the waves through LDS
   double c = 0.0;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double s2 = __shfl_xor(s, off), c2 = __shfl_xor(c, off);
-    dd_add(s, c, s2, c2);
-  }
-  if ((tid & 63) == 0) { red[0][wave] = s; red[1][wave] = c; }
+  dd_add_dpp<0xB1>(s, c);   // quad_perm [1, 0, 3, 2]
+  dd_add_dpp<0x4E>(s, c);   // quad_perm [2, 3, 0, 1]
+  dd_add_dpp<0x141>(s, c);  // row_half_mirror
+  dd_add_dpp<0x140>(s, c);  // row_mirror
+  double ws = readlane_f64(s, 0), wc = readlane_f64(c, 0);
+  dd_add(ws, wc, readlane_f64(s, 16), readlane_f64(c, 16));
+  dd_add(ws, wc, readlane_f64(s, 32), readlane_f64(c, 32));
+  dd_add(ws, wc, readlane_f64(s, 48), readlane_f64(c, 48));
+  if ((tid & 63) == 0) { red[0][wave] = ws; red[1][wave] = wc; }
   __syncthreads();
   double S = red[0][0], C = red[1][0];
   for (int i = 1; i < nw; ++i) dd_add(S, C, red[0][i], red[1][i]);
@@ -421,16 +454,14 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     const int l = tid + k * nt;
     if (k * nt >= nl) break;  // no lane of this chunk holds values (uniform)
     const bool valid = l < nl;
-    u32x4 wv[4], yv[4];
-    const u32x4* wp = (const u32x4*)(w + (valid ? l : 0) * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = valid ? wp[i] : u32x4{0, 0, 0, 0};
+    u32x4 yv[4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t d = xv[k][i >> 2][i & 3], e = wv[i >> 2][i & 3];
+      const uint32_t d = xv[k][i >> 2][i & 3], e = wv[k][i >> 2][i & 3];
       const float y0 = (__uint_as_float(d << 16) * r) * __uint_as_float(e << 16);
       const float y1 = (__uint_as_float(d & 0xFFFF0000u) * r) * __uint_as_float(e & 0xFFFF0000u);
-      yv[i >> 2][i & 3] = (uint32_t)bf16_rne(y0) | ((uint32_t)bf16_rne(y1) << 16);
+      // fp32 -> bf16 with round to nearest even, both halves in one conversion
+      yv[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){y0, y1}, v2bf));
     }
     if (y != nullptr && valid) {
       u32x4* yp = (u32x4*)(y + (int64_t)m * ldy + l * 32);
