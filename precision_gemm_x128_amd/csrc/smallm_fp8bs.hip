@@ -509,7 +509,12 @@ struct GemmCfg {
   // consecutive column groups start 16 floats apart modulo the 64 LDS banks
   static constexpr int kRedPitch = 4 * 64 + 16 / MT;
   static constexpr int kRed = kMaxMfmaWaves * NCG * MT * kRedPitch * 4;
-  static constexpr int kSmem = ((kStq + kSts) > kRed ? (kStq + kSts) : kRed);
+  // One M tile with shared activation tiles (NCG > 1): the partial sums get their own LDS space
+  // after the staging area, so the last round needs no barrier between the MFMAs and the
+  // partial-sum writes.  Otherwise they reuse the staging space.
+  static constexpr bool kRedOwn = (MT == 1 && NCG > 1);
+  static constexpr int kRedOff = kRedOwn ? (kStq + kSts + 15) / 16 * 16 : 0;
+  static constexpr int kSmem = kRedOwn ? kRedOff + kRed : ((kStq + kSts) > kRed ? (kStq + kSts) : kRed);
 };
 
 // One workgroup owns CGW consecutive column groups (C columns each) and all of K; with 256
@@ -543,7 +548,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
   uint8_t* stq = smem;
   float* sts_f = (float*)(smem + Cfg::kStq);
   uint8_t* sts_b = smem + Cfg::kStq;
-  float* red = (float*)smem;
+  float* red = (float*)(smem + Cfg::kRedOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -799,7 +804,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
           }
         }
       }
-      __syncthreads();  // staging buffer free for the next round
+      if (!Cfg::kRedOwn || rd + 1 < rounds) __syncthreads();  // staging buffer free for the next round
     }
     if (Cfg::kE8 && NCG == 1) {
 #pragma unroll
@@ -897,11 +902,11 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
           }
         }
       }
-      __syncthreads();
+      if (!Cfg::kRedOwn || rd + 1 < rounds) __syncthreads();
     }
   }
 
-  // ---- cross-wave and cross-lane reduction through LDS (staging space reused), fixed order ----
+  // ---- cross-wave and cross-lane reduction through LDS, fixed order ----
   // (lane and thread index formed again here rather than held across the rounds)
   int lane_e;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
