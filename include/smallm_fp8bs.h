@@ -134,7 +134,10 @@ int smallm_fp8bs_quant_e8m0(const uint16_t* x, int64_t ldx, uint8_t* q, int64_t 
                             uint8_t* sx_e8m0, int M, int K, void* stream);
 
 /* GEMM on pre-quantised activations (the second of the two launches): q e4m3 [M, ldq],
- * sx fp32 [M, K/128], packed weight, sw fp32 [N/128, K/128]  ->  y bf16 [M, ldy] (RNE). */
+ * sx fp32 [M, K/128], packed weight, sw fp32 [N/128, K/128]  ->  y bf16 [M, ldy] (RNE).
+ * Beyond M = 32, with a weight packed in 16-column groups and K <= 16384, it runs an
+ * MFMA-tiled kernel (32 x 64 output tiles, no cross-wave reduction): the continuation past the
+ * small-M range, where the pages' path falls back to a tiled library GEMM (P1 Modifications). */
 int smallm_fp8bs_gemm(const uint8_t* q, int64_t ldq, const float* sx, const uint8_t* w_packed,
                       uint32_t layout_id, const float* sw, uint16_t* y, int64_t ldy,
                       int M, int N, int K, void* stream);

@@ -153,8 +153,14 @@ def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
     return dict(zip(PLAN_FIELDS, list(buf)))
 
 
+TILED_FROM_M = 32   # the pre-quantised GEMM is MFMA-tiled above this M with 16-column layouts
+TILED_ROWS = 32
+
+
 def kernel_name(M: int, N: int, K: int, mode: int = 0) -> str:
     """Name of the GEMM kernel instantiation (mode 0 fused fp32, 1 fused e8m0, 2/3 pre-quantised)."""
+    if mode >= 2 and M > TILED_FROM_M and layout_columns(N, K) == 16 and K // 128 <= 128:
+        return f"tiled_gemm_kernel<{TILED_ROWS}, {'true' if mode == 3 else 'false'}>"
     p = smallm_fp8bs_launch_plan(M, N, K)
     return f"smallm_gemm_kernel<{p['MT']}, {p['C']}, {p['NCG']}, {p['NKG']}, {mode}>"
 

@@ -960,6 +960,160 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// GEMM on pre-quantised input beyond the small-M range: MFMA-tiled, for 16-column layouts
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kTiledFromM = 32;  // M above which the pre-quantised GEMM is tiled
+constexpr int kTM = 32;          // rows per workgroup tile of the tiled kernel
+constexpr int kTiledMaxKB = 128;  // K blocks the tiled kernel takes (e8m0 weight scales in two registers)
+constexpr int kTD = 8;        // weight fragments in flight per wave (K blocks ahead)
+constexpr int kTPitch = 144;  // LDS pitch of a staged 128-byte activation row (conflict-free reads)
+
+// Workgroup tile: TM rows x 64 columns, four waves, wave w owning column group 4 x + w (16
+// columns) for all TM rows.  Per K block the tile's TM x 128 activation bytes and their scales
+// are staged in LDS by the 256 threads (TM / 2 bytes each; two buffers, one barrier per K block);
+// each wave streams its own fragments kTD K blocks ahead and runs one
+// 16x16x128 MFMA per 16-row subtile (the activation bytes are fetched kTD K blocks ahead too).
+// fp32 scales: each K block's partial is multiplied by
+// sx[row, kb] * sw[n/128, kb] into the accumulator; e8m0: the scales are the MFMA's scale
+// operands and one accumulator runs over K.  Every wave owns whole outputs: no reduction.
+template <int TM, bool E8>
+__global__ __launch_bounds__(256) void tiled_gemm_kernel(
+    const uint8_t* __restrict__ q, int64_t ldq, const void* __restrict__ sa,
+    const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
+    int64_t ldy, int M, int K) {
+  constexpr int NSUB = TM / 16;   // 16-row MFMA subtiles
+  constexpr int TPR = 256 / TM;   // staging threads per row
+  constexpr int BPT = 128 / TPR;  // staged bytes per thread
+  constexpr int NLA = BPT / 16;   // 16-byte loads per thread
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * kTPitch];
+  __shared__ uint32_t sS[2][TM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = K >> 7;
+  const int cg = blockIdx.x * 4 + wave;
+  const int m0 = blockIdx.y * TM;
+  const int Mt = min(TM, M - m0);
+  const int nb = (cg * 16) >> 7;
+
+  // the tile's activation rows as a bounds-checked buffer; rows past M and K blocks past the end
+  // use an offset beyond it and read zeros without touching memory
+  const uint32_t abytes = (uint32_t)((int64_t)(Mt - 1) * ldq + K);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(q + (int64_t)m0 * ldq), 0, (int)abytes, 0x00020000);
+  const uint32_t wbytes = (uint32_t)KB * 2048u;
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wp + (int64_t)cg * KB * 2048), 0, (int)wbytes, 0x00020000);
+  const int srow = tid / TPR, sch = tid % TPR;  // staging: row and chunk of this thread
+  // per-thread bases: a row past the tile starts beyond the buffers, so every K block of it
+  // reads zeros; the weight offsets of K blocks past the end are beyond their buffer too
+  const uint32_t arow = (srow < Mt) ? (uint32_t)((int64_t)srow * ldq + sch * BPT) : abytes;
+  const uint32_t sbytes = (uint32_t)(Mt * KB) * (E8 ? 1u : 4u);
+  const uint32_t srowb = (srow < Mt) ? (uint32_t)(srow * KB) * (E8 ? 1u : 4u) : sbytes;
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)sa + (int64_t)m0 * KB * (E8 ? 1 : 4)), 0, (int)sbytes, 0x00020000);
+
+  u32x4 ab[kTD][NLA];
+  uint32_t asc[kTD];
+  u32x4 wb[kTD][2];
+#define TILED_LOAD_A(slot, kb) do {                                                               \
+    const uint32_t o_ = arow + (uint32_t)(kb) * 128u;                                              \
+    _Pragma("unroll") for (int l_ = 0; l_ < NLA; ++l_)                                             \
+      ab[slot][l_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o_ + 16u * l_, 0, 0)); \
+    const uint32_t so_ = srowb + (uint32_t)(kb) * (E8 ? 1u : 4u);                                 \
+    if (E8) asc[slot] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(srsrc, so_, 0, 0);             \
+    else asc[slot] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, so_, 0, 0);                          \
+  } while (0)
+#define TILED_LOAD_W(slot, kb) do {                                                               \
+    const uint32_t o_ = (uint32_t)(kb) * 2048u + (uint32_t)lane * 16u;                              \
+    wb[slot][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, o_, 0, 2)); \
+    wb[slot][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, o_ + 1024u, 0, 2)); \
+  } while (0)
+
+  // e8m0 weight scales of the column group's row of blocks, one byte per lane (K blocks 0..63 and
+  // 64..127; past the row: zeros), loaded before everything else and taken per K block with
+  // readlane, so no load sits on the MFMA's path
+  uint32_t swb0 = 0u, swb1 = 0u;
+  if (E8) {
+    const __amdgpu_buffer_rsrc_t swsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)sw + (int64_t)nb * KB), 0, KB, 0x00020000);
+    swb0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsrc, (uint32_t)lane, 0, 0);
+    swb1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsrc, (uint32_t)lane + 64u, 0, 0);
+  }
+  // prologue in the loop's own issue order (per K block: activation bytes, scale, weights), so
+  // that every wait in the loop counts the same loads behind it
+#pragma unroll
+  for (int d = 0; d < kTD; ++d) {
+    TILED_LOAD_A(d, d);
+    TILED_LOAD_W(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  v4f acc[NSUB];
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kb0 = 0; kb0 < KB; kb0 += kTD) {
+#pragma unroll
+    for (int u = 0; u < kTD; ++u) {
+      const int kb = kb0 + u;
+      if (kb >= KB) break;  // uniform
+      const int buf = u & 1;  // kb0 is a multiple of kTD (even): buffer and slots follow u
+      // stage K block kb (its rows' last readers, at kb - 2, are past the previous barrier)
+      u32x4* dst = (u32x4*)(&sA[buf][srow * kTPitch + sch * BPT]);
+#pragma unroll
+      for (int l = 0; l < NLA; ++l) dst[l] = ab[u][l];
+      sS[buf][srow] = asc[u];  // the threads of a row store the same value
+      __syncthreads();
+      TILED_LOAD_A(u, kb + kTD);
+      const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[u][0], wb[u][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (E8) {
+        const int sb = (kb < 64) ? __builtin_amdgcn_readlane((int)swb0, kb) : __builtin_amdgcn_readlane((int)swb1, kb - 64);
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i) {
+          const int r = i * 16 + (lane & 15);
+          const u32x4* ap = (const u32x4*)(&sA[buf][r * kTPitch + (lane >> 4) * 32]);
+          const u32x4 a0 = ap[0], a1 = ap[1];
+          const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i], 0, 0, 0, (int)sS[buf][r], 0, sb);
+        }
+      } else {
+        const float swv = ((const float*)sw)[nb * KB + kb];
+        v4f fa[NSUB];
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i) {
+          const int r = i * 16 + (lane & 15);
+          const u32x4* ap = (const u32x4*)(&sA[buf][r * kTPitch + (lane >> 4) * 32]);
+          const u32x4 a0 = ap[0], a1 = ap[1];
+          const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          fa[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i) {
+          const v4f sx4 = v4f{__uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 0]),
+                              __uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 1]),
+                              __uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 2]),
+                              __uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 3])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(sx4[e] * swv, fa[i][e], acc[i][e]);
+        }
+      }
+      TILED_LOAD_W(u, kb + kTD);
+    }
+  }
+#undef TILED_LOAD_A
+#undef TILED_LOAD_W
+  // output: lane l holds column l % 16 of the wave's group, rows 4 (l / 16) + e of each subtile
+  const int col = cg * 16 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = i * 16 + 4 * (lane >> 4) + e;
+      if (r < Mt) y[(int64_t)(m0 + r) * ldy + col] = bf16_rne(acc[i][e]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------------
 
@@ -1099,6 +1253,23 @@ int launch_gemm(const void* a, int64_t lda, const void* sa, const uint8_t* wp, c
   }
   if (MT == 1) { SMALLM_C(1) } else { SMALLM_C(2) }
 #undef SMALLM_C
+  return launch_status();
+}
+
+// The pre-quantised GEMM takes the MFMA-tiled kernel beyond the small-M range when the weight
+// is packed in 16-column groups (one fragment per MFMA B operand) and a 64-row tile of q spans
+// less than 2 GiB.
+bool use_tiled(int M, int N, int K, int64_t ldq) {
+  return M > kTiledFromM && layout_columns(N, K) == 16 && K / 128 <= kTiledMaxKB &&
+         ldq * (kTM - 1) + K < ((int64_t)1 << 31);
+}
+
+template <bool E8>
+int launch_tiled(const uint8_t* q, int64_t ldq, const void* sa, const uint8_t* wp, const void* sw,
+                 uint16_t* y, int64_t ldy, int M, int N, int K, hipStream_t stream) {
+  const dim3 grid(N / 64, (M + kTM - 1) / kTM);
+  hipLaunchKernelGGL((tiled_gemm_kernel<kTM, E8>), grid, dim3(256), 0, stream, q, ldq, sa, wp, sw,
+                     y, ldy, M, K);
   return launch_status();
 }
 
@@ -1272,6 +1443,7 @@ int smallm_fp8bs_gemm(const uint8_t* q, int64_t ldq, const float* sx, const uint
                       int K, void* stream) {
   int st = check_gemm_args(q, ldq, 1, sx, true, w_packed, layout_id, sw, y, ldy, M, N, K);
   if (st) return st;
+  if (use_tiled(M, N, K, ldq)) return launch_tiled<false>(q, ldq, sx, w_packed, sw, y, ldy, M, N, K, (hipStream_t)stream);
   return launch_gemm<kPreqF32>(q, ldq, sx, w_packed, sw, y, ldy, M, N, K, nullptr, nullptr,
                                (hipStream_t)stream);
 }
@@ -1281,6 +1453,7 @@ int smallm_fp8bs_gemm_e8m0(const uint8_t* q, int64_t ldq, const uint8_t* sx_e8m0
                            uint16_t* y, int64_t ldy, int M, int N, int K, void* stream) {
   int st = check_gemm_args(q, ldq, 1, sx_e8m0, true, w_packed, layout_id, sw_e8m0, y, ldy, M, N, K);
   if (st) return st;
+  if (use_tiled(M, N, K, ldq)) return launch_tiled<true>(q, ldq, sx_e8m0, w_packed, sw_e8m0, y, ldy, M, N, K, (hipStream_t)stream);
   return launch_gemm<kPreqE8>(q, ldq, sx_e8m0, w_packed, sw_e8m0, y, ldy, M, N, K, nullptr,
                               nullptr, (hipStream_t)stream);
 }

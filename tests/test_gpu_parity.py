@@ -360,6 +360,46 @@ def test_two_kernel_path(M, e8m0):
     assert torch.equal(y.view(torch.int16), yf.view(torch.int16))
 
 
+TILED_CASES = [
+    # (N, K, M, full output?) -- 16-column layouts, M beyond 32: the MFMA-tiled kernel
+    (384, 640, 33, True),     # 6 column tiles, 5 K blocks (not a multiple of the prefetch depth)
+    (384, 640, 100, True),    # two row tiles, the second ragged
+    (4096, 128, 64, True),    # a single K block
+    (4096, 2048, 48, False),
+    (4096, 2048, 256, False),  # four full row tiles
+    (4096, 4736, 77, False),   # 37 K blocks
+]
+
+
+@pytest.mark.parametrize("N,K,M,full", TILED_CASES)
+@pytest.mark.parametrize("e8m0", [False, True])
+def test_prequantised_gemm_tiled(N, K, M, full, e8m0):
+    """GEMM on pre-quantised input beyond the small-M range with a 16-column weight layout: the
+    MFMA-tiled kernel, against the oracle GEMM on the oracle's quantised bytes."""
+    note(f"tiled prequantised N={N} K={K} M={M} e8m0={e8m0}")
+    assert P.layout_columns(N, K) == 16
+    w8, sw, wp, swd = prepared_weight(N, K, seed=6, e8m0=e8m0)
+    cols, ranges = (np.arange(N), [(0, N)]) if full else windows(N)
+    x = special_x(M, K, seed=M + N)
+    q_ref, sx_ref, ref = oracle_ref(x, w8, sw, e8m0, ranges)
+    qf = P.smallm_fp8bs_quant_e8m0 if e8m0 else P.smallm_fp8bs_quant
+    gf = P.smallm_fp8bs_gemm_e8m0 if e8m0 else P.smallm_fp8bs_gemm
+    q, sx = qf(to_dev_bf16(x))
+    y = torch.full((M, N), 3.0, dtype=torch.bfloat16, device=DEV)
+    gf(q, sx, wp, swd, y=y)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert_within_tol(y, ref, cols, what=f"tiled N={N} K={K} M={M}")
+    # padded row pitches: only the M x N outputs are written
+    qp = torch.zeros((M, K + 16), dtype=torch.uint8, device=DEV)
+    qp[:, :K] = q
+    yp = torch.full((M + 3, N + 8), 5.0, dtype=torch.bfloat16, device=DEV)
+    gf(qp[:, :K], sx, wp, swd, y=yp[:M, :N])
+    torch.cuda.synchronize()
+    assert torch.equal(yp[:M, :N].view(torch.int16), y.view(torch.int16))
+    assert torch.all(yp[M:] == 5.0) and torch.all(yp[:, N:] == 5.0)
+
+
 def test_padded_leading_dimensions():
     note("padded ld")
     M, N, K = 5, 384, 640

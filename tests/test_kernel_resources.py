@@ -1,4 +1,4 @@
-"""The GEMM kernels must not spill: a scratch reload shares the in-order vector-memory counter with
+"""The GEMM and producer kernels must not spill: a scratch reload shares the in-order vector-memory counter with
 the weight and activation loads, so a single spill would make a wave wait for every load in flight
 (and the spill stores are HBM traffic).  Compiles the device code (no GPU needed) and reads the
 per-kernel resource summary the compiler writes into the assembly."""
@@ -22,6 +22,9 @@ def test_gemm_kernels_use_no_scratch(tmp_path):
     text = out.read_text()
     kernels = re.findall(r"^(_Z\S*smallm_gemm_kernel\S*):", text, re.M)
     assert len(kernels) >= 64
+    others = re.findall(r"^(_Z\S*(?:tiled_gemm_kernel|rmsnorm_quant_kernel)\S*):", text, re.M)
+    assert len(others) == 4
+    kernels += others
     spills = []
     for k in kernels:
         seg = text[text.index(k + ":"):]
