@@ -179,10 +179,41 @@ def producer_pipeline(P, torch, np, synthgen, dev, copies, reps, N=5120, K=4096)
     return res
 
 
+def two_launch_beyond(P, torch, np, synthgen, dev, copies, reps, Ms, N=4096, K=2048):
+    """Beyond the small-M range: the standalone quantisation, then the GEMM on pre-quantised
+    input (the MFMA-tiled kernel for this 16-column layout), each alone and back to back."""
+    wps, sws = [], []
+    for i in range(copies):
+        w = torch.from_numpy(synthgen.gen_w(N, K, seed=0, copy=i)).to(dev)
+        w8, sw = P.smallm_fp8bs_quant_weight(w)
+        wps.append(P.smallm_fp8bs_pack_weight(w8))
+        sws.append(sw)
+        del w, w8
+    d = {}
+    for M in Ms:
+        x = torch.from_numpy(synthgen.gen_x(M, K, seed=0).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sx = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        tq = graph_us(torch, lambda i: P.smallm_fp8bs_quant(x, q=q, sx=sx), copies, reps)
+        tg = graph_us(torch, lambda i: P.smallm_fp8bs_gemm(q, sx, wps[i], sws[i], y=y), copies, reps)
+        t2 = graph_us(torch, lambda i: (P.smallm_fp8bs_quant(x, q=q, sx=sx),
+                                        P.smallm_fp8bs_gemm(q, sx, wps[i], sws[i], y=y)), copies, reps)
+        tf = 2.0 * M * N * K / (tg * 1e-6) / 1e12
+        d[str(M)] = {"quant_us": round(tq, 3), "gemm_us": round(tg, 3), "two_launch_us": round(t2, 3),
+                     "gemm_TFLOP_s": round(tf, 2), "gemm_pct_fp8_mfma_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+                     "gemm_kernel": P.kernel_name(M, N, K, 2)}
+    log("[bench] 4096x2048 M>32 two launches: " + " ".join(f"M={M} {d[str(M)]['two_launch_us']:.2f}us" for M in Ms))
+    del wps, sws
+    torch.cuda.empty_cache()
+    return d
+
+
 def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
     """The other workloads of the method, timed the same way (per-M us/call, GB/s, % of peak):
     the single 4096x2048 call at M=4; the M sweeps on 4608x4096 and 4096x2048 with outlier rows;
-    M = 33..256 on 4096x2048 with the MFMA rate beside the bandwidth; the e8m0-scale path on
+    M = 33..256 on 4096x2048 with the MFMA rate beside the bandwidth (fused, and quant then the
+    tiled GEMM on pre-quantised input); the e8m0-scale path on
     4096x2048 and 2048x4096 beside the fp32-scale path on the same data; and the producer-side
     fusion (RMSNorm with the quantisation, then the GEMM on pre-quantised input) on 5120x4096."""
     res = {}
@@ -209,6 +240,7 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
         d[str(M)] = e
     res["beyond_small_m_4096x2048"] = d
     log("[bench] 4096x2048 M>32: " + " ".join(f"M={M} {t[M]:.2f}us" for M in big))
+    res["beyond_small_m_4096x2048_two_launch"] = two_launch_beyond(P, torch, np, synthgen, dev, copies, reps, big)
     for N, K in ((4096, 2048), (2048, 4096)):
         ms = [1, 8, 32]
         tf, yf = time_config(P, torch, np, synthgen, dev, N, K, ms, copies, reps)
