@@ -13,6 +13,11 @@ passage of the pages it follows in the C source:
   applied per 128-wide K block, bf16 output);
 * sglang "[Perf] [AMD] dsv4: optional e8m0 mxscale GEMM for dense 128x128 fp8 linears",
   Modifications and commit message (power-of-two scales stored as e8m0 bytes).
+
+The FP8 block-scale MoE layer (dequantised fp64 reference in numpy, at the end of this module)
+follows sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small sort and FP8
+block-scale small-M kernel", Modifications, and the phase structure of sglang "[AMD] Small-M
+MXFP4 fused-MoE kernel for gfx950 (Qwen)", Modifications.
 """
 from __future__ import annotations
 
@@ -309,3 +314,91 @@ def rmsnorm_quant(x_bits: np.ndarray, w_bits: np.ndarray, eps: float, e8m0: bool
     y, _ = rmsnorm(x_bits, w_bits, eps)
     q, sx = quant_act(y, e8m0=e8m0)
     return y, q, sx
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 block-scale small-M fused MoE
+# ---------------------------------------------------------------------------------------------
+#
+# sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small sort and FP8 block-scale
+# small-M kernel", section Modifications: e4m3 expert weights with one fp32 scale per 128x128
+# block, converted to bf16 at scale 1 with each block's scale applied to the partial sum, and a
+# test against a dequantised reference.  The phase structure comes from sglang "[AMD] Small-M
+# MXFP4 fused-MoE kernel for gfx950 (Qwen)", section Modifications: bf16 activations, phase 1
+# gate/up with silu(g) * u stored as bf16, phase 2 the down projection with the top-k weights
+# applied in fp32.  Readings where the pages are silent: w13 holds the gate rows [0, I) above the
+# up rows [I, 2 I); a (token, slot) pair whose expert id lies outside [0, E) contributes nothing.
+#
+# Since a block scale multiplies every product of its block, applying it to the block's partial
+# sum equals multiplying by the dequantised weight; the reference below is that dequantised
+# product, in fp64.
+
+_E4M3_TABLE = None
+
+
+def _e4m3_table() -> np.ndarray:
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = np.array([e4m3_decode(i) for i in range(256)], dtype=np.float64)
+    return _E4M3_TABLE
+
+
+def dequant_weight(w8: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """fp64 [N, K] with entry dec(w8[n, k]) * sw[n // 128, k // 128] (exact: a 4-bit significand
+    times an fp32 scale fits in a double)."""
+    w8 = np.asarray(w8, dtype=np.uint8)
+    N, K = w8.shape
+    s = np.asarray(sw, dtype=np.float32).astype(np.float64)
+    assert s.shape == (N // 128, K // 128)
+    return _e4m3_table()[w8] * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """g * sigmoid(g) = g / (1 + e^-g), in fp64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def moe_gate_up(x: np.ndarray, w13e: np.ndarray, sw13e: np.ndarray):
+    """One expert's phase-1 GEMM for fp64 activations x [..., H]: returns (g, u), each [..., I],
+    from the gate rows [0, I) and the up rows [I, 2 I) of the dequantised w13."""
+    W = dequant_weight(w13e, sw13e)
+    I = W.shape[0] // 2
+    gu = np.asarray(x, dtype=np.float64) @ W.T
+    return gu[..., :I], gu[..., I:]
+
+
+def moe(x_bits: np.ndarray, ids: np.ndarray, tw: np.ndarray, w13, sw13, w2, sw2,
+        E: int | None = None):
+    """Whole MoE layer.
+
+    x_bits bf16 bits [T, H]; ids int [T, S]; tw float32 [T, S]; for every expert id e in use,
+    w13[e] e4m3 [2 I, H] with sw13[e] fp32 [2 I/128, H/128] and w2[e] e4m3 [H, I] with sw2[e] fp32
+    [H/128, I/128] (w13/w2 may be arrays or mappings holding only the experts in use; E
+    defaults to len(sw13)).  Returns (h bf16 bits [T, S, I], ref fp64 [T, H]):
+      h[t, s] = RNE_bf16(silu(g) * u), g and u the expert's gate and up outputs for token t;
+      ref[t]  = sum over slots s of tw[t, s] * (dequantised w2[e]) @ h[t, s].
+    Pairs with an id outside [0, E) leave h at zero and add nothing.  The bf16 output is
+    round_bf16(ref)."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    ids = np.asarray(ids)
+    tw = np.asarray(tw, dtype=np.float32)
+    T, H = x_bits.shape
+    S = ids.shape[1]
+    E = len(sw13) if E is None else E
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    some_w2 = next(iter(w2.values())) if isinstance(w2, dict) else w2[0]
+    I = np.asarray(some_w2).shape[1]
+    h = np.zeros((T, S, I), dtype=np.uint16)
+    ref = np.zeros((T, H), dtype=np.float64)
+    for t in range(T):
+        for s in range(S):
+            e = int(ids[t, s])
+            if e < 0 or e >= E:
+                continue
+            g, u = moe_gate_up(x[t], w13[e], sw13[e])
+            h[t, s] = round_bf16(silu(g) * u)
+            hv = bf16_to_f32(h[t, s]).astype(np.float64)
+            ref[t] += float(tw[t, s]) * (dequant_weight(w2[e], sw2[e]) @ hv)
+    return h, ref

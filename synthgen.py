@@ -18,6 +18,10 @@ used, these synthetic draws stand in for them):
 * W, fp32 [N, K]: w ~ N(0, 0.02), weight copy i drawn with seed tuple (seed, 1, i).  The fp8
   weight and its block scales are derived from it by a quantiser (oracle or library), never
   here.
+* MoE routing (sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small sort and
+  FP8 block-scale small-M kernel", Kernel microbenchmarks: E = 513 experts, 11 slots per token):
+  read as 512 routed experts plus one shared expert; see gen_moe_routing.  Expert e's fp32
+  weights are gen_w copies with copy index 2 e (w13) and 2 e + 1 (w2).
 """
 from __future__ import annotations
 
@@ -72,3 +76,26 @@ def outlier_rows(M: int, seed: int = 0) -> np.ndarray:
     """The rows gen_x(..., outliers=True) turns into outlier rows."""
     orng = np.random.default_rng([seed, 0, 1])
     return orng.permutation(M)[: math.ceil(0.05 * M)]
+
+
+def gen_moe_routing(T: int, S: int, E: int, seed: int = 0, shared: bool = True):
+    """Synthetic top-k routing: (ids int32 [T, S], tw float32 [T, S]).
+
+    With shared=True the last slot of every token holds expert E - 1 (the always-on shared expert)
+    with weight 1, and the other S - 1 slots hold distinct experts drawn uniformly from [0, E - 1)
+    with weights v / sum(v), v ~ U(0.05, 1).  With shared=False all S slots are routed that way
+    over [0, E).  Seed tuple (seed, 2)."""
+    rng = np.random.default_rng([seed, 2])
+    routed = S - 1 if shared else S
+    pool = E - 1 if shared else E
+    assert 0 <= routed <= pool
+    ids = np.empty((T, S), dtype=np.int32)
+    tw = np.empty((T, S), dtype=np.float32)
+    for t in range(T):
+        ids[t, :routed] = rng.permutation(pool)[:routed]
+        v = rng.uniform(0.05, 1.0, size=routed)
+        tw[t, :routed] = (v / v.sum()).astype(np.float32)
+        if shared:
+            ids[t, routed] = E - 1
+            tw[t, routed] = 1.0
+    return ids, tw
