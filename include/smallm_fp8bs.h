@@ -33,21 +33,28 @@
  *    the outputs are left untouched.  SMALLM_ERR_HIP means the launch itself failed.
  *  - Inputs must be finite; the results for NaN or infinite inputs are unspecified.
  *  - Results are deterministic: the same inputs give bit-identical outputs, eagerly or replayed
- *    from a graph (fixed reduction order, no atomics).
+ *    from a graph (fixed reduction order; the only atomic is the MoE's integer LDS min, whose
+ *    result does not depend on order).
  */
 #ifndef SMALLM_FP8BS_H
 #define SMALLM_FP8BS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define SMALLM_FP8BS_ABI_VERSION 3
+#define SMALLM_FP8BS_ABI_VERSION 4
 #define SMALLM_FP8BS_MAX_M 256
 #define SMALLM_FP8BS_RMS_MAX_M (1 << 20) /* rows of one producer call */
 #define SMALLM_FP8BS_RMS_MAX_H 16384     /* values per row of one producer call */
+#define SMALLM_FP8BS_MOE_MAX_T 48        /* tokens of one MoE call */
+#define SMALLM_FP8BS_MOE_MAX_S 16        /* expert slots per token */
+#define SMALLM_FP8BS_MOE_MAX_E 4096      /* experts */
+#define SMALLM_FP8BS_MOE_MAX_H 16384     /* hidden size */
+#define SMALLM_FP8BS_MOE_MAX_I 2048      /* intermediate size per expert */
 
 typedef enum {
   SMALLM_OK = 0,
@@ -187,6 +194,66 @@ int smallm_fp8bs_quant_gemm_e8m0(const uint16_t* x, int64_t ldx, const uint8_t* 
                                  uint32_t layout_id, const uint8_t* sw_e8m0, uint16_t* y,
                                  int64_t ldy, int M, int N, int K, uint8_t* q_dbg,
                                  uint8_t* sx_dbg_e8m0, void* stream);
+
+/* --------------------------------------------------------------------------------------------
+ * FP8 block-scale small-M fused MoE layer
+ * ------------------------------------------------------------------------------------------ */
+
+/* The layer of sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small sort and
+ * FP8 block-scale small-M kernel" (Modifications: e4m3 expert weights with one fp32 scale per
+ * 128x128 block, converted to bf16 at scale 1 with the block scale applied to the partial sum)
+ * in the two phases of sglang "[AMD] Small-M MXFP4 fused-MoE kernel for gfx950 (Qwen)"
+ * (Modifications: bf16 activations; phase 1 gate/up, silu(g) * u written as bf16; phase 2 the
+ * down projection with the top-k weights applied in fp32), for T tokens and S slots per token:
+ *   (g | u) = x[t] . dequant(w13[e])^T,   h[t, s] = RNE_bf16(silu(g) * u),   e = topk_ids[t, s]
+ *   y[t]    = RNE_bf16( sum_s topk_w[t, s] * h[t, s] . dequant(w2[e])^T )
+ * with silu(g) = g / (1 + e^-g) in fp32 and fp32 accumulation.  Expert e's w13 is e4m3 [2 I, H]
+ * (gate rows [0, I) above up rows [I, 2 I)) with sw13 fp32 [2 I/128, H/128]; its w2 is e4m3
+ * [H, I] with sw2 fp32 [H/128, I/128]; experts are stacked: w13 [E, 2 I, H], sw13
+ * [E, 2 I/128, H/128], w2 [E, H, I], sw2 [E, H/128, I/128], all contiguous. */
+
+/* Tag of the packed MoE weight layout (both w13 and w2). */
+uint32_t smallm_fp8bs_moe_layout_id(void);
+
+/* SMALLM_OK when (T, S, E, H, I) is in range: 1 <= T <= SMALLM_FP8BS_MOE_MAX_T,
+ * 1 <= S <= SMALLM_FP8BS_MOE_MAX_S, 1 <= E <= SMALLM_FP8BS_MOE_MAX_E, H and I positive multiples
+ * of 128 up to SMALLM_FP8BS_MOE_MAX_H / SMALLM_FP8BS_MOE_MAX_I; else SMALLM_ERR_SHAPE. */
+int smallm_fp8bs_moe_supported(int T, int S, int E, int H, int I);
+
+/* Weight preparation at load time (not timed): permute E stacked row-major e4m3 [R, K] expert
+ * matrices (R, K multiples of 128) into the packed layout, E * R * K bytes, each expert in its
+ * own [e R K, (e + 1) R K) byte range, so experts may be packed in batches.  gate_up = 1 for w13
+ * (R = 2 I, K = H: gate and up rows of the same intermediate columns are interleaved in 8-row
+ * groups), 0 for w2 (R = H, K = I).  16-byte aligned pointers.  unpack is the inverse. */
+int smallm_fp8bs_moe_pack(const uint8_t* w8, uint8_t* w_packed, int E, int R, int K, int gate_up,
+                          void* stream);
+int smallm_fp8bs_moe_unpack(const uint8_t* w_packed, uint8_t* w8, int E, int R, int K,
+                            int gate_up, void* stream);
+
+/* Workspace bytes smallm_fp8bs_moe needs for (T, S, H, I), 0 when out of range: the bf16
+ * intermediate h [T * S, I] rounded up to 256 bytes, then, when the down projection is split over
+ * NS = smallm_fp8bs_moe_splits(T, S) > 1 workgroups per output tile, fp32 partial sums
+ * [NS, T, H]. */
+size_t smallm_fp8bs_moe_workspace_bytes(int T, int S, int H, int I);
+
+/* NS for (T, S): ceil(T * S / 32) clamped to [1, 16]; 0 when out of range. */
+int smallm_fp8bs_moe_splits(int T, int S);
+
+/* The layer: two launches on `stream`, three when NS > 1.  x: bf16 [T, ldx]; topk_ids: int32
+ * [T, S] expert ids (a pair whose id lies outside [0, E) contributes nothing and its h row is not
+ * written; a token may name one expert in several slots, whose weights then add); topk_w: fp32
+ * [T, S]; w13_packed / w2_packed from smallm_fp8bs_moe_pack with layout_id =
+ * smallm_fp8bs_moe_layout_id() (else SMALLM_ERR_LAYOUT); workspace: caller-owned device memory of
+ * at least smallm_fp8bs_moe_workspace_bytes(T, S, H, I) bytes (else SMALLM_ERR_SHAPE), 256-byte
+ * aligned; on return its first T * S * I bf16 values hold h[t, s] at row t * S + s (the
+ * intermediate between the launches, also the test surface).  y: bf16 [T, ldy].  Each expert in
+ * use is read once per phase however many tokens name it.  ids, weights and scales must be
+ * 4-byte aligned, x 16-byte aligned with ldx a multiple of 8. */
+int smallm_fp8bs_moe(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                     int T, int S, const uint8_t* w13_packed, const float* sw13,
+                     const uint8_t* w2_packed, const float* sw2, uint32_t layout_id, int E, int H,
+                     int I, void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -360,12 +360,11 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
-def moe_gate_up(x: np.ndarray, w13e: np.ndarray, sw13e: np.ndarray):
-    """One expert's phase-1 GEMM for fp64 activations x [..., H]: returns (g, u), each [..., I],
-    from the gate rows [0, I) and the up rows [I, 2 I) of the dequantised w13."""
-    W = dequant_weight(w13e, sw13e)
-    I = W.shape[0] // 2
-    gu = np.asarray(x, dtype=np.float64) @ W.T
+def moe_gate_up(x: np.ndarray, W13: np.ndarray):
+    """Phase-1 GEMM of one expert for fp64 activations x [..., H] and its dequantised w13
+    [2 I, H]: returns (g, u), each [..., I], from the gate rows [0, I) and the up rows [I, 2 I)."""
+    I = W13.shape[0] // 2
+    gu = np.asarray(x, dtype=np.float64) @ W13.T
     return gu[..., :I], gu[..., I:]
 
 
@@ -391,14 +390,19 @@ def moe(x_bits: np.ndarray, ids: np.ndarray, tw: np.ndarray, w13, sw13, w2, sw2,
     some_w2 = next(iter(w2.values())) if isinstance(w2, dict) else w2[0]
     I = np.asarray(some_w2).shape[1]
     h = np.zeros((T, S, I), dtype=np.uint16)
-    ref = np.zeros((T, H), dtype=np.float64)
-    for t in range(T):
-        for s in range(S):
-            e = int(ids[t, s])
-            if e < 0 or e >= E:
-                continue
-            g, u = moe_gate_up(x[t], w13[e], sw13[e])
+    # every pair's term tw * (w2 @ h), computed expert by expert so that each expert is
+    # dequantised once, then summed over the slots in slot order
+    term = np.zeros((T, S, H), dtype=np.float64)
+    for e in sorted(set(int(v) for v in ids.ravel() if 0 <= v < E)):
+        pairs = [(t, s) for t in range(T) for s in range(S) if int(ids[t, s]) == e]
+        W13 = dequant_weight(w13[e], sw13[e])
+        W2 = dequant_weight(w2[e], sw2[e])
+        for t, s in pairs:
+            g, u = moe_gate_up(x[t], W13)
             h[t, s] = round_bf16(silu(g) * u)
             hv = bf16_to_f32(h[t, s]).astype(np.float64)
-            ref[t] += float(tw[t, s]) * (dequant_weight(w2[e], sw2[e]) @ hv)
+            term[t, s] = float(tw[t, s]) * (W2 @ hv)
+    ref = np.zeros((T, H), dtype=np.float64)
+    for s in range(S):
+        ref += term[:, s]
     return h, ref

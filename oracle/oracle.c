@@ -185,6 +185,8 @@ static float block_amax_f32(const float* w, int64_t ldw, int nb, int kb) {
 /* fp32 block scales: sw = RN32(amax / 448), w8 = enc(RN32(w / sw)); w: fp32 [N, ldw]. */
 void oracle_quant_weight_fp32(const float* w, int64_t ldw, int N, int K, uint8_t* w8, float* sw) {
   int NB = N / 128, KB = K / 128;
+  /* blocks are independent: threads split them, each block's arithmetic is unchanged */
+#pragma omp parallel for collapse(2) schedule(static)
   for (int nb = 0; nb < NB; ++nb)
     for (int kb = 0; kb < KB; ++kb) {
       float amax = block_amax_f32(w, ldw, nb, kb);
@@ -216,6 +218,7 @@ int oracle_e8m0_round_exponent(double amax) {
 /* e8m0 block scales: byte E + 127, w8 = enc(w * 2^-E), saturating at 448. */
 void oracle_quant_weight_e8m0(const float* w, int64_t ldw, int N, int K, uint8_t* w8, uint8_t* sw) {
   int NB = N / 128, KB = K / 128;
+#pragma omp parallel for collapse(2) schedule(static)
   for (int nb = 0; nb < NB; ++nb)
     for (int kb = 0; kb < KB; ++kb) {
       int E = oracle_e8m0_round_exponent((double)block_amax_f32(w, ldw, nb, kb));

@@ -47,6 +47,13 @@ EXPORTS = (
     "smallm_fp8bs_quant_gemm_e8m0",
     "smallm_fp8bs_rmsnorm_quant",
     "smallm_fp8bs_rmsnorm_quant_e8m0",
+    "smallm_fp8bs_moe_layout_id",
+    "smallm_fp8bs_moe_supported",
+    "smallm_fp8bs_moe_pack",
+    "smallm_fp8bs_moe_unpack",
+    "smallm_fp8bs_moe_workspace_bytes",
+    "smallm_fp8bs_moe_splits",
+    "smallm_fp8bs_moe",
 )
 
 
@@ -105,6 +112,13 @@ def lib():
         "smallm_fp8bs_quant_gemm_e8m0": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
         "smallm_fp8bs_rmsnorm_quant": (I, [P, I64, P, ctypes.c_float, P, I64, P, I64, P, I, I, P]),
         "smallm_fp8bs_rmsnorm_quant_e8m0": (I, [P, I64, P, ctypes.c_float, P, I64, P, I64, P, I, I, P]),
+        "smallm_fp8bs_moe_layout_id": (U32, []),
+        "smallm_fp8bs_moe_supported": (I, [I, I, I, I, I]),
+        "smallm_fp8bs_moe_pack": (I, [P, P, I, I, I, I, P]),
+        "smallm_fp8bs_moe_unpack": (I, [P, P, I, I, I, I, P]),
+        "smallm_fp8bs_moe_workspace_bytes": (ctypes.c_size_t, [I, I, I, I]),
+        "smallm_fp8bs_moe_splits": (I, [I, I]),
+        "smallm_fp8bs_moe": (I, [P, I64, P, P, I, I, P, P, P, P, U32, I, I, I, P, ctypes.c_size_t, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -408,3 +422,117 @@ def algorithmic_bytes(M: int, N: int, K: int, e8m0: bool = False) -> int:
     activations and the bf16 output."""
     s_w = 1 if e8m0 else 4
     return N * K + s_w * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 block-scale small-M fused MoE layer
+# ---------------------------------------------------------------------------------------------
+
+MOE_MAX_T = 48
+
+
+def smallm_fp8bs_moe_layout_id() -> int:
+    return int(lib().smallm_fp8bs_moe_layout_id())
+
+
+def smallm_fp8bs_moe_supported(T: int, S: int, E: int, H: int, I: int) -> int:
+    return int(lib().smallm_fp8bs_moe_supported(T, S, E, H, I))
+
+
+def _need3(t, dtypes, name):
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes:
+        raise TypeError(f"{name} must be a tensor with dtype in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 3 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 3-D tensor")
+
+
+def _moe_pack(w, gate_up, out, stream, pack):
+    _need3(w, _F8, "w")
+    E, R, K = w.shape
+    out = torch.empty((E, R, K), dtype=torch.uint8, device=w.device) if out is None else out
+    _need3(out, _F8, "out")
+    fn = lib().smallm_fp8bs_moe_pack if pack else lib().smallm_fp8bs_moe_unpack
+    _check(fn(_ptr(w), _ptr(out), E, R, K, int(bool(gate_up)), _stream(stream)),
+           "smallm_fp8bs_moe_pack" if pack else "smallm_fp8bs_moe_unpack")
+    return out
+
+
+def smallm_fp8bs_moe_pack(w8, gate_up: bool, out=None, stream=None):
+    """Stacked row-major e4m3 expert matrices [E, R, K] -> packed MoE layout (same shape).
+    gate_up=True for w13 [E, 2 I, H], False for w2 [E, H, I]."""
+    return _moe_pack(w8, gate_up, out, stream, True)
+
+
+def smallm_fp8bs_moe_unpack(w_packed, gate_up: bool, out=None, stream=None):
+    return _moe_pack(w_packed, gate_up, out, stream, False)
+
+
+def smallm_fp8bs_moe_workspace_bytes(T: int, S: int, H: int, I: int) -> int:
+    return int(lib().smallm_fp8bs_moe_workspace_bytes(T, S, H, I))
+
+
+def smallm_fp8bs_moe_splits(T: int, S: int) -> int:
+    return int(lib().smallm_fp8bs_moe_splits(T, S))
+
+
+def moe_h_view(workspace, T: int, S: int, I: int):
+    """The bf16 intermediate h [T * S, I] at the start of a MoE workspace."""
+    return workspace[: T * S * I * 2].view(torch.bfloat16).view(T * S, I)
+
+
+def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, workspace=None, y=None,
+                     layout_id=None, stream=None):
+    """MoE layer: bf16 x [T, H], int32 topk_ids / fp32 topk_w [T, S], packed w13 [E, 2 I, H] with fp32
+    sw13 [E, 2 I/128, H/128], packed w2 [E, H, I] with fp32 sw2 [E, H/128, I/128].  Returns (y bf16
+    [T, H], h bf16 [T * S, I]); h, the intermediate silu(g) * u of every (token, slot) pair, is a view
+    of the workspace (uint8, smallm_fp8bs_moe_workspace_bytes long; allocated when None)."""
+    _need(x, _BF, "x")
+    T, H = x.shape
+    for t_, n_, dt in ((topk_ids, "topk_ids", torch.int32), (topk_w, "topk_w", torch.float32)):
+        if not isinstance(t_, torch.Tensor) or t_.dtype != dt or not t_.is_cuda or t_.dim() != 2:
+            raise TypeError(f"{n_} must be a 2-D {dt} device tensor")
+        _contig(t_, n_)
+    S = topk_ids.shape[1]
+    if tuple(topk_ids.shape) != (T, S) or tuple(topk_w.shape) != (T, S):
+        raise ValueError(f"topk_ids and topk_w must both be [{T}, S]")
+    _need3(w13_packed, _U8, "w13_packed")
+    _need3(w2_packed, _U8, "w2_packed")
+    E, I2, H2 = w13_packed.shape
+    I = I2 // 2
+    if H2 != H or tuple(w2_packed.shape) != (E, H, I):
+        raise ValueError(f"w13 must be [E, 2 I, {H}] and w2 [E, {H}, I], got {tuple(w13_packed.shape)} "
+                         f"and {tuple(w2_packed.shape)}")
+    for t_, n_, shp in ((sw13, "sw13", (E, I2 // 128, H // 128)), (sw2, "sw2", (E, H // 128, I // 128))):
+        if not isinstance(t_, torch.Tensor) or t_.dtype != torch.float32 or tuple(t_.shape) != shp:
+            raise ValueError(f"{n_} must be float32 {shp}")
+        _contig(t_, n_)
+    need = smallm_fp8bs_moe_workspace_bytes(T, S, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    elif workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    y = _out(y, T, H, x.device)
+    lid = smallm_fp8bs_moe_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_moe(_ptr(x), x.stride(0), _ptr(topk_ids), _ptr(topk_w), T, S, _ptr(w13_packed),
+                                  _ptr(sw13), _ptr(w2_packed), _ptr(sw2), lid, E, H, I, _ptr(workspace),
+                                  workspace.numel(), _ptr(y), y.stride(0), _stream(stream)), "smallm_fp8bs_moe")
+    return y, moe_h_view(workspace, T, S, I)
+
+
+def moe_algorithmic_bytes(ids, E: int, H: int, I: int) -> int:
+    """Bytes one MoE call must move at minimum: each expert in use once (e4m3 w13 and w2 with
+    their fp32 block scales), the bf16 activations, ids and weights, the bf16 intermediate
+    written and read once, and the bf16 output."""
+    import numpy as np
+    ids = np.asarray(ids)
+    T, S = ids.shape
+    used = np.unique(ids[(ids >= 0) & (ids < E)])
+    per_expert = 3 * H * I + 4 * (2 * I // 128) * (H // 128) + 4 * (H // 128) * (I // 128)
+    return int(len(used) * per_expert + 2 * T * H + 8 * T * S + 2 * 2 * T * S * I + 2 * T * H)
+
+
+def moe_workspace(T: int, S: int, H: int, I: int, device="cuda:0"):
+    """A workspace tensor for smallm_fp8bs_moe (256-byte aligned by the caching allocator)."""
+    return torch.empty(max(smallm_fp8bs_moe_workspace_bytes(T, S, H, I), 256), dtype=torch.uint8, device=device)

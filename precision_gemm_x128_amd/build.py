@@ -5,7 +5,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "smallm_fp8bs.hip")
+SRCS = [os.path.join(HERE, "csrc", "smallm_fp8bs.hip"), os.path.join(HERE, "csrc", "moe_fp8bs.hip")]
 LIB = os.path.join(HERE, "libsmallm_fp8bs.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "smallm_fp8bs.h")
 
@@ -33,7 +33,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile the HIP library in-tree (always recompiles)."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)

@@ -1,0 +1,470 @@
+// moe_fp8bs.hip -- FP8 block-scale small-M fused MoE layer on MI355X (gfx950 / CDNA4).
+//
+//   h[t, s] = bf16(silu(g) * u),  (g | u) = x[t] . dequant(w13[e])^T,  e = ids[t, s]
+//   y[t]    = bf16( sum_s tw[t, s] * h[t, s] . dequant(w2[e])^T )
+//
+// What is computed follows sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small
+// sort and FP8 block-scale small-M kernel", section Modifications (e4m3 expert weights converted
+// to bf16 at scale 1, one fp32 scale per 128x128 block applied to the block's partial sum), with
+// the two-phase structure of sglang "[AMD] Small-M MXFP4 fused-MoE kernel for gfx950 (Qwen)",
+// section Modifications (bf16 activations, phase 1 gate/up with silu(g) * u written as bf16,
+// phase 2 the down projection with the top-k weights applied in fp32).  w13 holds the gate rows
+// [0, I) above the up rows [I, 2 I).
+//
+// Design points of this implementation:
+//
+//  * No sort.  Each expert in use is streamed once per phase, with every token routed to it as
+//    a row of the MFMA A operand.  Phase 1 launches one workgroup per (token, slot) pair and
+//    8-column slice of the intermediate; a workgroup whose pair is not the first pair naming its
+//    expert exits after one pass over the ids in LDS, the others gather the expert's tokens with
+//    a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
+//    range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
+//    and its waves walk the experts whose first pair lies in its range.  With NS > 1 the
+//    workgroups leave fp32 partial sums in the caller's workspace and a third launch adds them in
+//    range order.
+//  * Packed weights: every 16-row x 128-K block of an expert matrix is one 2 KiB fragment in
+//    the lane order of an MFMA operand (lane l = 16 c + j holds row j and K bytes [32 c, 32 c + 32)
+//    of the block, bytes 0..15 in the first KiB and 16..31 in the second), fragments of one
+//    16-row tile consecutive along K.  In w13 a tile holds 8 gate rows and the 8 up rows of the
+//    same intermediate columns, so one workgroup owns both halves of silu(g) * u.
+//  * Arithmetic: e4m3 bytes become bf16 with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact), the
+//    products run on v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact in fp32), each
+//    128-K block's fp32 partial is multiplied by its block scale and added to an fp32
+//    accumulator.  Per-wave split-K partials are summed through LDS in a fixed order, so every
+//    result is deterministic and graph replays equal eager runs.
+
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/smallm_fp8bs.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kMoeThreads = 512;  // 8 waves, split-K over the 128-wide K blocks
+constexpr int kMoeWaves = kMoeThreads / 64;
+constexpr int kMoePairs = SMALLM_FP8BS_MOE_MAX_T * SMALLM_FP8BS_MOE_MAX_S;
+constexpr uint32_t kMoeLayoutId = 0x4D4F4510u;
+
+// the 32 e4m3 bytes a lane holds for one 128-K block, as four 8-value bf16 MFMA operands
+__device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi, v8bf out[4]) {
+  const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j], 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j], 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j + 1], 1.0f, false);
+    const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j + 1], 1.0f, true);
+    out[j] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+  }
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const u32x4& a, const v8bf& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+}
+
+// ---------------------------------------------------------------------------------------------
+// phase 1: gate/up GEMM of one expert for all its tokens, silu(g) * u -> h (bf16)
+// ---------------------------------------------------------------------------------------------
+//
+// grid (T * S, I / 8), 512 threads.  Workgroup (p, q) works when pair p is the first pair naming
+// its expert e.  Its A rows are the tokens routed to e, ascending (MT tiles of 16 at most, only
+// the occupied tiles are computed, rows past the last token are zero); its 16 columns are the gate
+// rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.
+
+template <int MT>
+__global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
+    int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13, int H, int I,
+    uint16_t* __restrict__ h) {
+  __shared__ int s_ids[kMoePairs];
+  __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];  // routed tokens, ascending; [MAX_T] = count
+  __shared__ float s_red[kMoeWaves * MT * 4 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = T * S;
+  const int p = blockIdx.x, q = blockIdx.y;
+  for (int i = tid; i < P; i += kMoeThreads) s_ids[i] = ids[i];
+  __syncthreads();
+  const int e = s_ids[p];
+  if (e < 0 || e >= E) return;
+  bool earlier = false;
+  for (int i = tid; i < p; i += kMoeThreads) earlier |= (s_ids[i] == e);
+  if (wave == 0) {
+    bool mine = false;
+    if (lane < T)
+      for (int s = 0; s < S; ++s) mine |= (s_ids[lane * S + s] == e);
+    const uint64_t m = __ballot(mine);
+    if (mine) s_tok[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+    if (lane == 0) s_tok[SMALLM_FP8BS_MOE_MAX_T] = __popcll(m);
+  }
+  if (__syncthreads_or(earlier)) return;
+  const int Me = s_tok[SMALLM_FP8BS_MOE_MAX_T];
+  const int tiles = (Me + 15) >> 4;
+
+  const int KB = H >> 7;
+  const int j = lane & 15, chunk = lane >> 4;
+  // column j < 8 is gate row 8q + j (scale block row q / 16), j >= 8 the matching up row
+  const int srow = (j < 8) ? (q >> 4) : ((I >> 7) + (q >> 4));
+  const float* swp = sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
+  const uint8_t* wp = w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
+  const uint16_t* xr[MT];
+  bool row_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int idx = 16 * mt + j;
+    row_ok[mt] = idx < Me;
+    xr[mt] = x + (int64_t)(row_ok[mt] ? s_tok[idx] : 0) * ldx + chunk * 32;
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int kb = wave; kb < KB; kb += kMoeWaves) {
+    const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
+    const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+    u32x4 a[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4* xa = (const u32x4*)(xr[mt] + kb * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[mt][i] = row_ok[mt] ? xa[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float s = swp[kb];
+    v8bf bv[4];
+    e4m3x32_to_bf16(b0, b1, bv);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt >= tiles) break;
+      v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + s * pm[i];
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[((wave * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
+  __syncthreads();
+
+  for (int o = tid; o < MT * 128; o += kMoeThreads) {
+    const int mt = o >> 7, r = (o >> 3) & 15, c = o & 7;
+    const int idx = 16 * mt + r;
+    if (idx >= Me) continue;
+    const int t = s_tok[idx];
+    // D row r, column c sits in lane 16 (r / 4) + c, register r % 4
+    const int base = (mt * 4 + (r & 3)) * 64 + 16 * (r >> 2) + c;
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMoeWaves; ++w) {
+      g = g + s_red[w * MT * 256 + base];
+      u = u + s_red[w * MT * 256 + base + 8];
+    }
+    const uint16_t hb = bf16_bits((g / (1.0f + expf(-g))) * u);
+    for (int s = 0; s < S; ++s)
+      if (s_ids[t * S + s] == e) h[(int64_t)(t * S + s) * I + 8 * q + c] = hb;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// phase 2: down projection, top-k weights in fp32, sum over slots -> y (bf16)
+// ---------------------------------------------------------------------------------------------
+//
+// grid (H / 16, NS), 512 threads.  Workgroup (b, z) owns output columns [16 b, 16 b + 16) for all
+// T tokens and the pairs [z P / NS, (z + 1) P / NS).  Wave w takes the pairs of that range with
+// index = w (mod 8) that are the first pair of their expert e and adds tw * (h . w2[e]^T) for every
+// token routed to e; the per-wave sums meet in LDS in wave order.  With NS = 1 the result is
+// written as bf16 y, else as the fp32 partial [z][t][n] that moe_reduce_kernel adds in z order.
+
+template <int MT>
+__global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ tw,
+    int T, int S, int E, const uint8_t* __restrict__ w2, const float* __restrict__ sw2, int H,
+    int I, uint16_t* __restrict__ y, int64_t ldy, float* __restrict__ part) {
+  __shared__ int s_ids[kMoePairs];
+  __shared__ float s_tw[kMoePairs];
+  __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];
+  __shared__ float s_red[kMoeWaves * MT * 4 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = T * S;
+  const int NS = gridDim.y, z = blockIdx.y;
+  const int lo = (int)((int64_t)z * P / NS), hi = (int)((int64_t)(z + 1) * P / NS);
+  for (int i = tid; i < P; i += kMoeThreads) {
+    s_ids[i] = ids[i];
+    s_tw[i] = tw[i];
+  }
+  for (int i = tid; i < E; i += kMoeThreads) s_first[i] = INT_MAX;
+  __syncthreads();
+  for (int i = tid; i < P; i += kMoeThreads) {
+    const int e = s_ids[i];
+    if (e >= 0 && e < E) atomicMin(&s_first[e], i);
+  }
+  __syncthreads();
+
+  const int KB2 = I >> 7, nb = blockIdx.x >> 3;
+  const int j = lane & 15, chunk = lane >> 4;
+  const uint8_t* wtile = w2 + (int64_t)blockIdx.x * KB2 * 2048 + lane * 16;
+  v4f acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int p = lo + wave; p < hi; p += kMoeWaves) {
+    const int e = s_ids[p];
+    if (e < 0 || e >= E || s_first[e] != p) continue;
+    // A row j of tile mt is token 16 mt + j: its first slot naming e and its summed weight
+    int slot[MT];
+    float wsum[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = 16 * mt + j;
+      slot[mt] = -1;
+      wsum[mt] = 0.0f;
+      if (t < T)
+        for (int s = 0; s < S; ++s)
+          if (s_ids[t * S + s] == e) {
+            if (slot[mt] < 0) slot[mt] = s;
+            wsum[mt] = wsum[mt] + s_tw[t * S + s];
+          }
+    }
+    const float* swp = sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
+    const uint8_t* wp = wtile + (int64_t)e * H * I;
+    for (int kb = 0; kb < KB2; ++kb) {
+      const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
+      const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+      const float s = swp[kb];
+      v8bf bv[4];
+      e4m3x32_to_bf16(b0, b1, bv);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (!__any(slot[mt] >= 0)) continue;
+        u32x4 a[4];
+        if (slot[mt] >= 0) {
+          const int t = 16 * mt + j;
+          const u32x4* ha =
+              (const u32x4*)(h + (int64_t)(t * S + slot[mt]) * I + kb * 128 + chunk * 32);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = ha[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
+        // D row 4 (lane / 16) + i belongs to token 16 mt + that row, whose weight lane (row) holds
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float wr = __shfl(wsum[mt], 4 * (lane >> 4) + i);
+          acc[mt][i] = acc[mt][i] + wr * (s * pm[i]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[((wave * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
+  __syncthreads();
+
+  for (int o = tid; o < MT * 256; o += kMoeThreads) {
+    const int mt = o >> 8, r = (o >> 4) & 15, c = o & 15;
+    const int t = 16 * mt + r;
+    if (t >= T) continue;
+    const int base = (mt * 4 + (r & 3)) * 64 + 16 * (r >> 2) + c;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMoeWaves; ++w) v = v + s_red[w * MT * 256 + base];
+    if (NS == 1)
+      y[(int64_t)t * ldy + blockIdx.x * 16 + c] = bf16_bits(v);
+    else
+      part[((int64_t)z * T + t) * H + blockIdx.x * 16 + c] = v;
+  }
+}
+
+// y[t, n] = bf16(sum over z = 0 .. NS-1 of part[z][t][n]), four outputs per thread
+__global__ __launch_bounds__(256) void moe_reduce_kernel(const float* __restrict__ part, int NS,
+                                                         int T, int H, uint16_t* __restrict__ y,
+                                                         int64_t ldy) {
+  const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (o >= (int64_t)T * H) return;
+  v4f v = *(const v4f*)(part + o);
+  for (int z = 1; z < NS; ++z) {
+    const v4f w = *(const v4f*)(part + (int64_t)z * T * H + o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] + w[i];
+  }
+  const int64_t t = o / H, n = o % H;
+  uint16_t* yp = y + t * ldy + n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) yp[i] = bf16_bits(v[i]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// weight (un)packing: one thread per 16-byte chunk of the packed layout
+// ---------------------------------------------------------------------------------------------
+//
+// Expert e's [R, K] matrix occupies bytes [e R K, (e + 1) R K) of both layouts.  Packed chunk
+// o of an expert: fragment f = o / 128 = tile * (K / 128) + kb, half = (o / 64) % 2, lane =
+// o % 64 (column j = lane % 16, K bytes 32 (lane / 16) + 16 half + [0, 16) of block kb).  Tile row
+// j is row 16 tile + j, or for w13 (GATE_UP) gate row 8 tile + j (j < 8) / up row I + 8 tile + j - 8.
+
+template <bool PACK, bool GATE_UP>
+__global__ __launch_bounds__(256) void moe_pack_kernel(const uint8_t* __restrict__ src,
+                                                       uint8_t* __restrict__ dst, int R, int K,
+                                                       int64_t chunks) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= chunks) return;
+  const int64_t per = (int64_t)R * K / 16;
+  const int64_t e = o / per, oe = o % per;
+  const int KB = K >> 7;
+  const int64_t f = oe >> 7;
+  const int within = (int)(oe & 127), half = within >> 6, lane = within & 63;
+  const int chunk = lane >> 4, j = lane & 15;
+  const int64_t tile = f / KB, kb = f % KB;
+  const int64_t n = GATE_UP ? ((j < 8) ? tile * 8 + j : (R >> 1) + tile * 8 + (j - 8)) : tile * 16 + j;
+  const int64_t lin = e * R * K + n * K + kb * 128 + chunk * 32 + half * 16;
+  const int64_t pk = e * R * K + oe * 16;
+  if (PACK)
+    *(u32x4*)(dst + pk) = *(const u32x4*)(src + lin);
+  else
+    *(u32x4*)(dst + lin) = *(const u32x4*)(src + pk);
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int launch_status() { return hipGetLastError() == hipSuccess ? SMALLM_OK : SMALLM_ERR_HIP; }
+
+int moe_pack_common(const uint8_t* src, uint8_t* dst, int E, int R, int K, int gate_up, bool pack,
+                    void* stream) {
+  if (!src || !dst) return SMALLM_ERR_INVALID;
+  if (E < 1 || R <= 0 || K <= 0 || (R & 127) || (K & 127)) return SMALLM_ERR_SHAPE;
+  if (gate_up != 0 && gate_up != 1) return SMALLM_ERR_INVALID;
+  if (!aligned16(src) || !aligned16(dst)) return SMALLM_ERR_ALIGN;
+  const int64_t chunks = (int64_t)E * R * K / 16;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  const hipStream_t st = (hipStream_t)stream;
+  if (pack) {
+    if (gate_up)
+      hipLaunchKernelGGL((moe_pack_kernel<true, true>), grid, dim3(256), 0, st, src, dst, R, K, chunks);
+    else
+      hipLaunchKernelGGL((moe_pack_kernel<true, false>), grid, dim3(256), 0, st, src, dst, R, K, chunks);
+  } else {
+    if (gate_up)
+      hipLaunchKernelGGL((moe_pack_kernel<false, true>), grid, dim3(256), 0, st, src, dst, R, K, chunks);
+    else
+      hipLaunchKernelGGL((moe_pack_kernel<false, false>), grid, dim3(256), 0, st, src, dst, R, K, chunks);
+  }
+  return launch_status();
+}
+
+// Workgroups per output tile in phase 2: about 32 pairs each, at most 16.
+inline int moe_splits(int T, int S) {
+  const int ns = (T * S + 31) / 32;
+  return ns < 1 ? 1 : (ns > 16 ? 16 : ns);
+}
+
+inline size_t moe_h_bytes(int T, int S, int I) { return ((size_t)T * S * I * 2 + 255) & ~(size_t)255; }
+
+inline size_t moe_workspace_bytes(int T, int S, int H, int I) {
+  const int ns = moe_splits(T, S);
+  return moe_h_bytes(T, S, I) + (ns > 1 ? (size_t)ns * T * H * 4 : 0);
+}
+
+template <int MT>
+void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float* tw, int T, int S,
+                const uint8_t* w13, const float* sw13, const uint8_t* w2, const float* sw2, int E,
+                int H, int I, uint8_t* ws, uint16_t* y, int64_t ldy, hipStream_t st) {
+  uint16_t* h = (uint16_t*)ws;
+  float* part = (float*)(ws + moe_h_bytes(T, S, I));
+  const int ns = moe_splits(T, S);
+  hipLaunchKernelGGL((moe_gate_up_kernel<MT>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x, ldx,
+                     ids, T, S, E, w13, sw13, H, I, h);
+  hipLaunchKernelGGL((moe_down_kernel<MT>), dim3(H / 16, ns), dim3(kMoeThreads), 0, st, h, ids, tw,
+                     T, S, E, w2, sw2, H, I, y, ldy, part);
+  if (ns > 1) {
+    const int64_t quads = (int64_t)T * H / 4;
+    hipLaunchKernelGGL(moe_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
+                       part, ns, T, H, y, ldy);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t smallm_fp8bs_moe_layout_id(void) { return kMoeLayoutId; }
+
+int smallm_fp8bs_moe_pack(const uint8_t* w8, uint8_t* w_packed, int E, int R, int K, int gate_up,
+                          void* stream) {
+  return moe_pack_common(w8, w_packed, E, R, K, gate_up, true, stream);
+}
+
+int smallm_fp8bs_moe_unpack(const uint8_t* w_packed, uint8_t* w8, int E, int R, int K, int gate_up,
+                            void* stream) {
+  return moe_pack_common(w_packed, w8, E, R, K, gate_up, false, stream);
+}
+
+int smallm_fp8bs_moe_supported(int T, int S, int E, int H, int I) {
+  if (T < 1 || T > SMALLM_FP8BS_MOE_MAX_T || S < 1 || S > SMALLM_FP8BS_MOE_MAX_S || E < 1 ||
+      E > SMALLM_FP8BS_MOE_MAX_E || H <= 0 || H > SMALLM_FP8BS_MOE_MAX_H || (H & 127) || I <= 0 ||
+      I > SMALLM_FP8BS_MOE_MAX_I || (I & 127))
+    return SMALLM_ERR_SHAPE;
+  return SMALLM_OK;
+}
+
+size_t smallm_fp8bs_moe_workspace_bytes(int T, int S, int H, int I) {
+  if (T < 1 || T > SMALLM_FP8BS_MOE_MAX_T || S < 1 || S > SMALLM_FP8BS_MOE_MAX_S || H <= 0 ||
+      H > SMALLM_FP8BS_MOE_MAX_H || (H & 127) || I <= 0 || I > SMALLM_FP8BS_MOE_MAX_I || (I & 127))
+    return 0;
+  return moe_workspace_bytes(T, S, H, I);
+}
+
+int smallm_fp8bs_moe_splits(int T, int S) {
+  if (T < 1 || T > SMALLM_FP8BS_MOE_MAX_T || S < 1 || S > SMALLM_FP8BS_MOE_MAX_S) return 0;
+  return moe_splits(T, S);
+}
+
+int smallm_fp8bs_moe(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, const float* topk_w,
+                     int T, int S, const uint8_t* w13_packed, const float* sw13,
+                     const uint8_t* w2_packed, const float* sw2, uint32_t layout_id, int E, int H,
+                     int I, void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
+                     void* stream) {
+  if (!x || !topk_ids || !topk_w || !w13_packed || !sw13 || !w2_packed || !sw2 || !workspace || !y)
+    return SMALLM_ERR_INVALID;
+  int st = smallm_fp8bs_moe_supported(T, S, E, H, I);
+  if (st) return st;
+  if (ldx < H || ldy < H) return SMALLM_ERR_SHAPE;
+  if (workspace_bytes < moe_workspace_bytes(T, S, H, I)) return SMALLM_ERR_SHAPE;
+  if (!aligned16(x) || ((ldx * 2) & 15) || !aligned16(w13_packed) || !aligned16(w2_packed) ||
+      ((uintptr_t)workspace & 255u) || ((uintptr_t)y & 1u) ||
+      ((uintptr_t)topk_ids & 3u) || ((uintptr_t)topk_w & 3u) || ((uintptr_t)sw13 & 3u) ||
+      ((uintptr_t)sw2 & 3u))
+    return SMALLM_ERR_ALIGN;
+  if (layout_id != kMoeLayoutId) return SMALLM_ERR_LAYOUT;
+  const hipStream_t hs = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  if (T <= 16)
+    launch_moe<1>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, w2_packed, sw2, E, H, I, ws, y, ldy, hs);
+  else if (T <= 32)
+    launch_moe<2>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, w2_packed, sw2, E, H, I, ws, y, ldy, hs);
+  else
+    launch_moe<3>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, w2_packed, sw2, E, H, I, ws, y, ldy, hs);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -20,8 +20,9 @@ used, these synthetic draws stand in for them):
   here.
 * MoE routing (sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small sort and
   FP8 block-scale small-M kernel", Kernel microbenchmarks: E = 513 experts, 11 slots per token):
-  read as 512 routed experts plus one shared expert; see gen_moe_routing.  Expert e's fp32
-  weights are gen_w copies with copy index 2 e (w13) and 2 e + 1 (w2).
+  read as 512 routed experts plus one shared expert; see gen_moe_routing.  Expert weights
+  arrive quantised (e4m3 with fp32 128x128 block scales), so they are drawn as bytes directly:
+  see gen_moe_expert (w13 of expert e with index 2 e, w2 with index 2 e + 1).
 """
 from __future__ import annotations
 
@@ -99,3 +100,41 @@ def gen_moe_routing(T: int, S: int, E: int, seed: int = 0, shared: bool = True):
             ids[t, routed] = E - 1
             tw[t, routed] = 1.0
     return ids, tw
+
+
+def _e4m3_normal_exponent_law(spread: float = 4.5) -> np.ndarray:
+    """Probabilities of the 16 exponent fields of |v| for v = z * 448 / spread, z ~ N(0, 1)
+    (a normal weight block whose largest value maps near 448), from the normal law."""
+    c = 448.0 / spread
+
+    def mass(lo, hi):   # P(lo <= |z| * c < hi)
+        return math.erf(hi / c / math.sqrt(2)) - math.erf(lo / c / math.sqrt(2))
+
+    p = [mass(0.0, 2.0 ** -6)]
+    p += [mass(2.0 ** (e - 7), 2.0 ** (e - 6)) for e in range(1, 15)]
+    p += [mass(256.0, 1e300)]
+    p = np.array(p)
+    return p / p.sum()
+
+
+def gen_moe_expert(R: int, K: int, seed: int, e: int):
+    """Expert e's e4m3 matrix [R, K] as bytes plus fp32 128x128 block scales.
+
+    The bytes are drawn to look like a quantised normal weight block: sign uniform, exponent
+    field from _e4m3_normal_exponent_law (through a 2^16-entry table), mantissa uniform (folded
+    to 0..6 in the top binade, so no NaN code).  Scales: 4.5 * sigma / 448 with sigma = 0.02 * U(0.8, 1.2) per block.  Seed tuple
+    (seed, 3, e), so any expert can be drawn on its own."""
+    rng = np.random.default_rng([seed, 3, e])
+    p = _e4m3_normal_exponent_law()
+    counts = np.floor(p * 65536).astype(np.int64)
+    counts[int(np.argmax(counts))] += 65536 - counts.sum()
+    table = np.repeat(np.arange(16, dtype=np.uint8), counts)          # 2^16-entry sampling table
+    ex = table[rng.integers(0, 65536, size=(R, K), dtype=np.uint16)]
+    b = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+    man = b & 7
+    man = np.where(ex == 15, man % 7, man).astype(np.uint8)
+    sign = b >> 7
+    w8 = (sign << 7) | (ex << 3) | man
+    sigma = 0.02 * rng.uniform(0.8, 1.2, size=(R // 128, K // 128))
+    sw = (4.5 * sigma / 448.0).astype(np.float32)
+    return w8.astype(np.uint8), sw

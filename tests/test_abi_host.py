@@ -76,7 +76,7 @@ def test_launch_plans_balance_the_cus():
 
 
 def test_version_layout_and_strerror():
-    assert P.smallm_fp8bs_abi_version() == 3
+    assert P.smallm_fp8bs_abi_version() == 4
     # columns per group: the widest C in {16, 8, 4, 2} giving a multiple of 256 column groups
     assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46380210
     assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46380204
@@ -166,6 +166,57 @@ def test_producer_rejections_happen_before_any_launch():
         assert fn(f, 4096, f, 1e-6, f, 4100, f, 4096, f, 4, 4096, None) == 3         # y pitch
         assert fn(f, 4096, f, 1e-6, f, 4096, f, 4104, f, 4, 4096, None) == 3         # q pitch
 
+
+
+def test_moe_rejections_happen_before_any_launch():
+    """smallm_fp8bs_moe and the MoE packers refuse bad pointers, shapes, alignment and layout
+    tags on the host (moe argument order: x, ldx, ids, tw, T, S, w13, sw13, w2, sw2, layout,
+    E, H, I, h, y, ldy, stream)."""
+    L = P.lib()
+    f = _fake()
+    lid = P.smallm_fp8bs_moe_layout_id()
+    assert lid == 0x4D4F4510
+    wsb = P.smallm_fp8bs_moe_workspace_bytes(4, 11, 4096, 256)
+    ok = [f, 4096, f, f, 4, 11, f, f, f, f, lid, 513, 4096, 256, f, wsb, f, 4096, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x", "ldx", "ids", "tw", "T", "S", "w13", "sw13", "w2", "sw2", "lid", "E", "H", "I",
+                 "ws", "wsb", "y", "ldy"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.smallm_fp8bs_moe(*a)
+
+    for name in ("x", "ids", "tw", "w13", "sw13", "w2", "sw2", "ws", "y"):
+        assert call(**{name: None}) == 1, name
+    assert call(T=0) == 2 and call(T=49) == 2 and call(S=0) == 2 and call(S=17) == 2
+    assert call(E=0) == 2 and call(E=4097) == 2
+    assert call(H=4000, ldx=4000, ldy=4000) == 2 and call(I=200) == 2 and call(I=4096) == 2
+    assert call(H=32768, ldx=32768, ldy=32768) == 2
+    assert call(ldx=4000) == 2 and call(ldy=4000) == 2
+    assert call(wsb=wsb - 1) == 2
+    assert call(x=_fake(0x10008)) == 3 and call(ldx=4100) == 3 and call(ws=_fake(0x10080)) == 3
+    assert call(w13=_fake(0x10008)) == 3 and call(w2=_fake(0x10004)) == 3
+    assert call(y=_fake(0x10001)) == 3 and call(ids=_fake(0x10002)) == 3 and call(tw=_fake(0x10002)) == 3
+    assert call(lid=lid ^ 1) == 4
+    # workspace: h rounded to 256 bytes, then NS fp32 partial planes when NS > 1
+    assert P.smallm_fp8bs_moe_splits(1, 11) == 1 and P.smallm_fp8bs_moe_splits(3, 11) == 2
+    assert P.smallm_fp8bs_moe_splits(20, 11) == 7 and P.smallm_fp8bs_moe_splits(48, 16) == 16
+    assert P.smallm_fp8bs_moe_splits(0, 11) == 0 and P.smallm_fp8bs_moe_splits(4, 17) == 0
+    assert P.smallm_fp8bs_moe_workspace_bytes(1, 11, 4096, 256) == 11 * 256 * 2          # 22 x 256 bytes
+    assert P.smallm_fp8bs_moe_workspace_bytes(1, 3, 4096, 128) == 768
+    assert P.smallm_fp8bs_moe_workspace_bytes(20, 11, 4096, 256) == 220 * 256 * 2 + 7 * 20 * 4096 * 4
+    assert P.smallm_fp8bs_moe_workspace_bytes(49, 11, 4096, 256) == 0
+    assert P.smallm_fp8bs_moe_supported(48, 16, 4096, 16384, 2048) == 0
+    assert P.smallm_fp8bs_moe_supported(1, 1, 1, 128, 128) == 0
+    for fn in (L.smallm_fp8bs_moe_pack, L.smallm_fp8bs_moe_unpack):
+        assert fn(None, f, 2, 256, 128, 1, None) == 1
+        assert fn(f, None, 2, 256, 128, 1, None) == 1
+        assert fn(f, f, 2, 256, 128, 2, None) == 1          # gate_up must be 0 or 1
+        assert fn(f, f, 0, 256, 128, 1, None) == 2
+        assert fn(f, f, 2, 200, 128, 0, None) == 2
+        assert fn(f, f, 2, 256, 100, 0, None) == 2
+        assert fn(_fake(0x10008), f, 2, 256, 128, 1, None) == 3
 
 def test_binding_rejects_wrong_dtypes_without_gpu():
     import torch

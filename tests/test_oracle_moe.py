@@ -89,7 +89,7 @@ def test_moe_gate_up_matches_block_scale_gemm_oracle(oracle_lib):
     assert np.all(sx == 1.0)
     w8, sw = oracle.quant_weight(synthgen.gen_w(2 * I, H, seed=40))
     ref = oracle.gemm(q, sx, w8, sw)
-    g, u = oracle.moe_gate_up(oracle.bf16_to_f32(x).astype(np.float64), w8, sw)
+    g, u = oracle.moe_gate_up(oracle.bf16_to_f32(x).astype(np.float64), oracle.dequant_weight(w8, sw))
     scale = np.abs(ref).max()
     assert np.allclose(g, ref[:, :I], rtol=1e-12, atol=1e-13 * scale)
     assert np.allclose(u, ref[:, I:], rtol=1e-12, atol=1e-13 * scale)
@@ -176,3 +176,14 @@ def test_moe_routing_generator_shape():
     for t in range(5):
         assert len(set(ids[t].tolist())) == 11
     assert np.allclose(tw[:, :10].sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_moe_expert_generator_draws_finite_normal_like_codes():
+    w8, sw = synthgen.gen_moe_expert(256, 512, seed=1, e=3)
+    assert w8.shape == (256, 512) and sw.shape == (2, 4) and sw.dtype == np.float32
+    assert not np.any((w8 & 0x7F) == 0x7F)                  # no NaN code
+    w8b, swb = synthgen.gen_moe_expert(256, 512, seed=1, e=3)
+    assert np.array_equal(w8, w8b) and np.array_equal(sw, swb)
+    v = np.abs(np.array([oracle.e4m3_decode(b) for b in range(256)])[w8])
+    # |v| = |z| * 448 / 4.5: the median of |z| is 0.674, so the median code value is near 67
+    assert 40 < np.median(v) < 100 and v.max() <= 448
