@@ -85,6 +85,37 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // the occupied tiles are computed, rows past the last token are zero); its 16 columns are the gate
 // rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.
 
+// The split-K loop of phase 1 over the first NT row tiles: wave w takes K blocks w, w + 8, ...;
+// each block's four MFMAs give the fp32 partial that its 128x128 scale multiplies into acc.
+template <int NT, int MT>
+__device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp,
+                                             const uint16_t* const (&xr)[MT],
+                                             const bool (&row_ok)[MT], int KB, int wave,
+                                             v4f (&acc)[MT]) {
+  for (int kb = wave; kb < KB; kb += kMoeWaves) {
+    const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
+    const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+    u32x4 a[NT][4];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) {
+      const u32x4* xa = (const u32x4*)(xr[mt] + kb * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[mt][i] = row_ok[mt] ? xa[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float s = swp[kb];
+    v8bf bv[4];
+    e4m3x32_to_bf16(b0, b1, bv);
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) {
+      v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + s * pm[i];
+    }
+  }
+}
+
 template <int MT>
 __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
@@ -131,30 +162,14 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
   v4f acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int kb = wave; kb < KB; kb += kMoeWaves) {
-    const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
-    const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
-    u32x4 a[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const u32x4* xa = (const u32x4*)(xr[mt] + kb * 128);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[mt][i] = row_ok[mt] ? xa[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-    const float s = swp[kb];
-    v8bf bv[4];
-    e4m3x32_to_bf16(b0, b1, bv);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt >= tiles) break;
-      v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + s * pm[i];
-    }
-  }
+  // one straight-line loop per occupied tile count (workgroup-uniform): no branch lies between an
+  // MFMA and the multiply-add that reads its result
+  if (MT == 1 || tiles == 1)
+    gate_up_loop<1, MT>(wp, swp, xr, row_ok, KB, wave, acc);
+  else if (MT == 2 || tiles == 2)
+    gate_up_loop<(MT < 2 ? MT : 2), MT>(wp, swp, xr, row_ok, KB, wave, acc);
+  else
+    gate_up_loop<MT, MT>(wp, swp, xr, row_ok, KB, wave, acc);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
