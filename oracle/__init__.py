@@ -17,7 +17,9 @@ passage of the pages it follows in the C source:
 The FP8 block-scale MoE layer (dequantised fp64 reference in numpy, at the end of this module)
 follows sglang "[AMD] gfx950 small-batch MoE: expert-count gate for the small sort and FP8
 block-scale small-M kernel", Modifications, and the phase structure of sglang "[AMD] Small-M
-MXFP4 fused-MoE kernel for gfx950 (Qwen)", Modifications.
+MXFP4 fused-MoE kernel for gfx950 (Qwen)", Modifications.  The same layer with MXFP4 expert
+weights (e2m1 elements, one e8m0 scale per 32 K elements, OCP Microscaling Formats v1.0) follows
+that page's Motivation and Modifications.
 """
 from __future__ import annotations
 
@@ -368,6 +370,33 @@ def moe_gate_up(x: np.ndarray, W13: np.ndarray):
     return gu[..., :I], gu[..., I:]
 
 
+def _moe_layer(x_bits: np.ndarray, ids: np.ndarray, tw: np.ndarray, E: int, I: int, W13_of, W2_of):
+    """The layer for dequantised expert weights: W13_of(e) fp64 [2 I, H], W2_of(e) fp64 [H, I]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    ids = np.asarray(ids)
+    tw = np.asarray(tw, dtype=np.float32)
+    T, H = x_bits.shape
+    S = ids.shape[1]
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    h = np.zeros((T, S, I), dtype=np.uint16)
+    # every pair's term tw * (w2 @ h), computed expert by expert so that each expert is
+    # dequantised once, then summed over the slots in slot order
+    term = np.zeros((T, S, H), dtype=np.float64)
+    for e in sorted(set(int(v) for v in ids.ravel() if 0 <= v < E)):
+        pairs = [(t, s) for t in range(T) for s in range(S) if int(ids[t, s]) == e]
+        W13 = W13_of(e)
+        W2 = W2_of(e)
+        for t, s in pairs:
+            g, u = moe_gate_up(x[t], W13)
+            h[t, s] = round_bf16(silu(g) * u)
+            hv = bf16_to_f32(h[t, s]).astype(np.float64)
+            term[t, s] = float(tw[t, s]) * (W2 @ hv)
+    ref = np.zeros((T, H), dtype=np.float64)
+    for s in range(S):
+        ref += term[:, s]
+    return h, ref
+
+
 def moe(x_bits: np.ndarray, ids: np.ndarray, tw: np.ndarray, w13, sw13, w2, sw2,
         E: int | None = None):
     """Whole MoE layer.
@@ -380,29 +409,66 @@ def moe(x_bits: np.ndarray, ids: np.ndarray, tw: np.ndarray, w13, sw13, w2, sw2,
       ref[t]  = sum over slots s of tw[t, s] * (dequantised w2[e]) @ h[t, s].
     Pairs with an id outside [0, E) leave h at zero and add nothing.  The bf16 output is
     round_bf16(ref)."""
-    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
-    ids = np.asarray(ids)
-    tw = np.asarray(tw, dtype=np.float32)
-    T, H = x_bits.shape
-    S = ids.shape[1]
     E = len(sw13) if E is None else E
-    x = bf16_to_f32(x_bits).astype(np.float64)
     some_w2 = next(iter(w2.values())) if isinstance(w2, dict) else w2[0]
     I = np.asarray(some_w2).shape[1]
-    h = np.zeros((T, S, I), dtype=np.uint16)
-    # every pair's term tw * (w2 @ h), computed expert by expert so that each expert is
-    # dequantised once, then summed over the slots in slot order
-    term = np.zeros((T, S, H), dtype=np.float64)
-    for e in sorted(set(int(v) for v in ids.ravel() if 0 <= v < E)):
-        pairs = [(t, s) for t in range(T) for s in range(S) if int(ids[t, s]) == e]
-        W13 = dequant_weight(w13[e], sw13[e])
-        W2 = dequant_weight(w2[e], sw2[e])
-        for t, s in pairs:
-            g, u = moe_gate_up(x[t], W13)
-            h[t, s] = round_bf16(silu(g) * u)
-            hv = bf16_to_f32(h[t, s]).astype(np.float64)
-            term[t, s] = float(tw[t, s]) * (W2 @ hv)
-    ref = np.zeros((T, H), dtype=np.float64)
-    for s in range(S):
-        ref += term[:, s]
-    return h, ref
+    return _moe_layer(x_bits, ids, tw, E, I, lambda e: dequant_weight(w13[e], sw13[e]),
+                      lambda e: dequant_weight(w2[e], sw2[e]))
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP4 expert weights for the same MoE layer
+# ---------------------------------------------------------------------------------------------
+#
+# sglang "[AMD] Small-M MXFP4 fused-MoE kernel for gfx950 (Qwen)", sections Motivation and
+# Modifications: the expert weights are MXFP4 (fp4x2 bytes, e2m1 elements with a power-of-two
+# e8m0 scale per 32 consecutive K elements of a row, the OCP Microscaling format), converted to
+# bf16 with the scale applied by the conversion, against bf16 activations; the test compares with
+# a dequantised reference.  The element and scale codecs follow the OCP Microscaling Formats (MX)
+# specification v1.0: e2m1 has one sign bit, two exponent bits with bias 1 and one mantissa bit
+# (exponent field 0 is subnormal: 0.5 * m), no infinities or NaN; the e8m0 scale byte b is
+# 2^(b - 127), 0xFF being NaN.  Reading where the pages are silent: in an fp4x2 byte the low
+# nibble holds the even K element and the high nibble the odd one; the scales of expert matrix
+# [R, K] are the row-major byte array [R, K/32].
+
+def e2m1_decode(c: int) -> float:
+    """Value of the 4-bit e2m1 code c (bit 3 sign, bits 2..1 exponent, bit 0 mantissa)."""
+    c = int(c) & 15
+    sign = -1.0 if c & 8 else 1.0
+    e, m = (c >> 1) & 3, c & 1
+    mag = 0.5 * m if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+    return sign * mag
+
+
+def e8m0_decode(b: int) -> float:
+    """Value of the e8m0 scale byte b: 2^(b - 127); NaN for 0xFF."""
+    b = int(b) & 255
+    return math.nan if b == 255 else math.ldexp(1.0, b - 127)
+
+
+def dequant_mxfp4(w4: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """fp64 [R, K] from fp4x2 bytes w4 [R, K/2] and e8m0 scales s [R, K/32]: element (r, k) is
+    e2m1(nibble k % 2 of byte k // 2) * 2^(s[r, k // 32] - 127), exact in a double."""
+    w4 = np.asarray(w4, dtype=np.uint8)
+    s = np.asarray(s, dtype=np.uint8)
+    R, K2 = w4.shape
+    K = 2 * K2
+    assert s.shape == (R, K // 32)
+    table = np.array([e2m1_decode(c) for c in range(16)], dtype=np.float64)
+    codes = np.empty((R, K), dtype=np.uint8)
+    codes[:, 0::2] = w4 & 15
+    codes[:, 1::2] = w4 >> 4
+    scale = np.array([e8m0_decode(b) for b in range(256)], dtype=np.float64)[s]
+    return table[codes] * np.repeat(scale, 32, axis=1)
+
+
+def moe_mxfp4(x_bits: np.ndarray, ids: np.ndarray, tw: np.ndarray, w13, s13, w2, s2,
+              E: int | None = None):
+    """The MoE layer of moe() with MXFP4 expert weights: w13[e] fp4x2 [2 I, H/2] with e8m0
+    s13[e] [2 I, H/32]; w2[e] fp4x2 [H, I/2] with e8m0 s2[e] [H, I/32].  Returns (h, ref) as
+    moe() does."""
+    E = len(s13) if E is None else E
+    some_w2 = next(iter(w2.values())) if isinstance(w2, dict) else w2[0]
+    I = 2 * np.asarray(some_w2).shape[1]
+    return _moe_layer(x_bits, ids, tw, E, I, lambda e: dequant_mxfp4(w13[e], s13[e]),
+                      lambda e: dequant_mxfp4(w2[e], s2[e]))

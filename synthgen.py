@@ -138,3 +138,38 @@ def gen_moe_expert(R: int, K: int, seed: int, e: int):
     sigma = 0.02 * rng.uniform(0.8, 1.2, size=(R // 128, K // 128))
     sw = (4.5 * sigma / 448.0).astype(np.float32)
     return w8.astype(np.uint8), sw
+
+
+def _e2m1_normal_magnitude_law(spread: float = 2.5) -> np.ndarray:
+    """Probabilities of the 8 e2m1 magnitude codes 0..7 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) for
+    |v| with v = z * 6 / spread, z ~ N(0, 1), binned at the midpoints between those values (a
+    normal group of 32 whose largest value lands near 6)."""
+    c = 6.0 / spread
+    edges = [0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, math.inf]
+
+    def mass(lo, hi):
+        top = 1.0 if hi == math.inf else math.erf(hi / c / math.sqrt(2))
+        return top - math.erf(lo / c / math.sqrt(2))
+
+    p = np.array([mass(edges[i], edges[i + 1]) for i in range(8)])
+    return p / p.sum()
+
+
+def gen_moe_expert_mxfp4(R: int, K: int, seed: int, e: int):
+    """Expert e's MXFP4 matrix [R, K]: fp4x2 bytes [R, K/2] (even K element in the low nibble) and
+    e8m0 scale bytes [R, K/32], one per 32 consecutive K elements of a row.
+
+    Codes: sign uniform, magnitude from _e2m1_normal_magnitude_law (through a 2^16-entry table).
+    Scales: byte 120 + U{-1, 0, 1} (2^-8 .. 2^-6, so 6 * scale spans the 0.02-sigma weights of
+    gen_moe_expert).  Seed tuple (seed, 4, e), so any expert can be drawn on its own."""
+    rng = np.random.default_rng([seed, 4, e])
+    p = _e2m1_normal_magnitude_law()
+    counts = np.floor(p * 65536).astype(np.int64)
+    counts[int(np.argmax(counts))] += 65536 - counts.sum()
+    table = np.repeat(np.arange(8, dtype=np.uint8), counts)
+    mag = table[rng.integers(0, 65536, size=(R, K), dtype=np.uint16)]
+    sign = rng.integers(0, 2, size=(R, K), dtype=np.uint8)
+    codes = (sign << 3) | mag
+    w4 = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    s = (120 + rng.integers(-1, 2, size=(R, K // 32))).astype(np.uint8)
+    return w4, s
