@@ -255,6 +255,44 @@ int smallm_fp8bs_moe(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, co
                      int I, void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
                      void* stream);
 
+/* --------------------------------------------------------------------------------------------
+ * The same MoE layer with MXFP4 expert weights
+ * ------------------------------------------------------------------------------------------ */
+
+/* The layer of sglang "[AMD] Small-M MXFP4 fused-MoE kernel for gfx950 (Qwen)" (Motivation and
+ * Modifications: fp4x2 expert weights converted to bf16 with their power-of-two scales, bf16
+ * activations, the two phases above), with the OCP Microscaling Formats v1.0 encodings: e2m1
+ * elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; values 0, 0.5 .. 6) two per
+ * byte, the even K element in the low nibble, and one e8m0 scale byte b (value 2^(b - 127)) per
+ * 32 consecutive K elements of a row.  Expert e's w13 is fp4x2 [2 I, H/2] with scales [2 I, H/32]
+ * (gate rows [0, I) above up rows [I, 2 I)); its w2 is fp4x2 [H, I/2] with scales [H, I/32];
+ * experts are stacked and contiguous.  Every scale byte of a group that holds a non-zero code must
+ * lie in [2, 252], so every dequantised weight is zero or a normal, finite bf16; other bytes give
+ * unspecified results.  Same formulas, shapes, limits and workspace as smallm_fp8bs_moe. */
+
+/* Tag of the packed MXFP4 MoE weight layout (weights and scales of both w13 and w2). */
+uint32_t smallm_fp8bs_moe_mxfp4_layout_id(void);
+
+/* Weight preparation at load time (not timed): permute E stacked fp4x2 [R, K/2] expert matrices
+ * (R, K multiples of 128) and their e8m0 scales [R, K/32] into the packed layouts, E * R * K / 2
+ * and E * R * K / 32 bytes, each expert in its own byte ranges.  gate_up = 1 for w13 (R = 2 I,
+ * K = H), 0 for w2 (R = H, K = I).  Weight pointers 16-byte aligned; scale pointers any alignment.
+ * unpack is the inverse. */
+int smallm_fp8bs_moe_mxfp4_pack(const uint8_t* w4, const uint8_t* s, uint8_t* w_packed,
+                                uint8_t* s_packed, int E, int R, int K, int gate_up, void* stream);
+int smallm_fp8bs_moe_mxfp4_unpack(const uint8_t* w_packed, const uint8_t* s_packed, uint8_t* w4,
+                                  uint8_t* s, int E, int R, int K, int gate_up, void* stream);
+
+/* The layer, as smallm_fp8bs_moe but with packed MXFP4 weights and their packed scales, and
+ * layout_id = smallm_fp8bs_moe_mxfp4_layout_id() (else SMALLM_ERR_LAYOUT).  Each expert in use
+ * is read once per phase: (3 H I) / 2 weight bytes and (3 H I) / 32 scale bytes. */
+int smallm_fp8bs_moe_mxfp4(const uint16_t* x, int64_t ldx, const int32_t* topk_ids,
+                           const float* topk_w, int T, int S, const uint8_t* w13_packed,
+                           const uint8_t* s13_packed, const uint8_t* w2_packed,
+                           const uint8_t* s2_packed, uint32_t layout_id, int E, int H, int I,
+                           void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

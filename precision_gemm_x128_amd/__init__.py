@@ -54,6 +54,10 @@ EXPORTS = (
     "smallm_fp8bs_moe_workspace_bytes",
     "smallm_fp8bs_moe_splits",
     "smallm_fp8bs_moe",
+    "smallm_fp8bs_moe_mxfp4_layout_id",
+    "smallm_fp8bs_moe_mxfp4_pack",
+    "smallm_fp8bs_moe_mxfp4_unpack",
+    "smallm_fp8bs_moe_mxfp4",
 )
 
 
@@ -119,6 +123,10 @@ def lib():
         "smallm_fp8bs_moe_workspace_bytes": (ctypes.c_size_t, [I, I, I, I]),
         "smallm_fp8bs_moe_splits": (I, [I, I]),
         "smallm_fp8bs_moe": (I, [P, I64, P, P, I, I, P, P, P, P, U32, I, I, I, P, ctypes.c_size_t, P, I64, P]),
+        "smallm_fp8bs_moe_mxfp4_layout_id": (U32, []),
+        "smallm_fp8bs_moe_mxfp4_pack": (I, [P, P, P, P, I, I, I, I, P]),
+        "smallm_fp8bs_moe_mxfp4_unpack": (I, [P, P, P, P, I, I, I, I, P]),
+        "smallm_fp8bs_moe_mxfp4": (I, [P, I64, P, P, I, I, P, P, P, P, U32, I, I, I, P, ctypes.c_size_t, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -482,12 +490,7 @@ def moe_h_view(workspace, T: int, S: int, I: int):
     return workspace[: T * S * I * 2].view(torch.bfloat16).view(T * S, I)
 
 
-def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, workspace=None, y=None,
-                     layout_id=None, stream=None):
-    """MoE layer: bf16 x [T, H], int32 topk_ids / fp32 topk_w [T, S], packed w13 [E, 2 I, H] with fp32
-    sw13 [E, 2 I/128, H/128], packed w2 [E, H, I] with fp32 sw2 [E, H/128, I/128].  Returns (y bf16
-    [T, H], h bf16 [T * S, I]); h, the intermediate silu(g) * u of every (token, slot) pair, is a view
-    of the workspace (uint8, smallm_fp8bs_moe_workspace_bytes long; allocated when None)."""
+def _moe_common(x, topk_ids, topk_w, w13_packed, w2_packed, fp4):
     _need(x, _BF, "x")
     T, H = x.shape
     for t_, n_, dt in ((topk_ids, "topk_ids", torch.int32), (topk_w, "topk_w", torch.float32)):
@@ -501,18 +504,34 @@ def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, work
     _need3(w2_packed, _U8, "w2_packed")
     E, I2, H2 = w13_packed.shape
     I = I2 // 2
-    if H2 != H or tuple(w2_packed.shape) != (E, H, I):
-        raise ValueError(f"w13 must be [E, 2 I, {H}] and w2 [E, {H}, I], got {tuple(w13_packed.shape)} "
+    f = 2 if fp4 else 1           # K elements per byte
+    if H2 * f != H or tuple(w2_packed.shape) != (E, H, I // f):
+        raise ValueError(f"w13 must be [E, 2 I, {H // f}] and w2 [E, {H}, I/{f}], got {tuple(w13_packed.shape)} "
                          f"and {tuple(w2_packed.shape)}")
-    for t_, n_, shp in ((sw13, "sw13", (E, I2 // 128, H // 128)), (sw2, "sw2", (E, H // 128, I // 128))):
+    return T, S, E, H, I
+
+
+def _moe_workspace_arg(workspace, T, S, H, I, device):
+    need = smallm_fp8bs_moe_workspace_bytes(T, S, H, I)
+    if workspace is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    return workspace
+
+
+def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, workspace=None, y=None,
+                     layout_id=None, stream=None):
+    """MoE layer: bf16 x [T, H], int32 topk_ids / fp32 topk_w [T, S], packed w13 [E, 2 I, H] with fp32
+    sw13 [E, 2 I/128, H/128], packed w2 [E, H, I] with fp32 sw2 [E, H/128, I/128].  Returns (y bf16
+    [T, H], h bf16 [T * S, I]); h, the intermediate silu(g) * u of every (token, slot) pair, is a view
+    of the workspace (uint8, smallm_fp8bs_moe_workspace_bytes long; allocated when None)."""
+    T, S, E, H, I = _moe_common(x, topk_ids, topk_w, w13_packed, w2_packed, False)
+    for t_, n_, shp in ((sw13, "sw13", (E, 2 * I // 128, H // 128)), (sw2, "sw2", (E, H // 128, I // 128))):
         if not isinstance(t_, torch.Tensor) or t_.dtype != torch.float32 or tuple(t_.shape) != shp:
             raise ValueError(f"{n_} must be float32 {shp}")
         _contig(t_, n_)
-    need = smallm_fp8bs_moe_workspace_bytes(T, S, H, I)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
-    elif workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    workspace = _moe_workspace_arg(workspace, T, S, H, I, x.device)
     y = _out(y, T, H, x.device)
     lid = smallm_fp8bs_moe_layout_id() if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_moe(_ptr(x), x.stride(0), _ptr(topk_ids), _ptr(topk_w), T, S, _ptr(w13_packed),
@@ -521,15 +540,74 @@ def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, work
     return y, moe_h_view(workspace, T, S, I)
 
 
-def moe_algorithmic_bytes(ids, E: int, H: int, I: int) -> int:
+# ---------------------------------------------------------------------------------------------
+# the MoE layer with MXFP4 expert weights
+# ---------------------------------------------------------------------------------------------
+
+def smallm_fp8bs_moe_mxfp4_layout_id() -> int:
+    return int(lib().smallm_fp8bs_moe_mxfp4_layout_id())
+
+
+def _moe_mxfp4_pack(w, s, gate_up, out, out_s, stream, pack):
+    _need3(w, _U8, "w")
+    _need3(s, _U8, "s")
+    E, R, K2 = w.shape
+    K = 2 * K2
+    if tuple(s.shape) != (E, R, K // 32):
+        raise ValueError(f"scales must be uint8 [{E}, {R}, {K // 32}], got {tuple(s.shape)}")
+    out = torch.empty_like(w) if out is None else out
+    out_s = torch.empty_like(s) if out_s is None else out_s
+    _need3(out, _U8, "out")
+    _need3(out_s, _U8, "out_s")
+    fn = lib().smallm_fp8bs_moe_mxfp4_pack if pack else lib().smallm_fp8bs_moe_mxfp4_unpack
+    _check(fn(_ptr(w), _ptr(s), _ptr(out), _ptr(out_s), E, R, K, int(bool(gate_up)), _stream(stream)),
+           "smallm_fp8bs_moe_mxfp4_pack" if pack else "smallm_fp8bs_moe_mxfp4_unpack")
+    return out, out_s
+
+
+def smallm_fp8bs_moe_mxfp4_pack(w4, s, gate_up: bool, out=None, out_s=None, stream=None):
+    """Stacked fp4x2 expert matrices [E, R, K/2] (uint8) and their e8m0 scales [E, R, K/32] ->
+    (packed weights, packed scales), same shapes.  gate_up=True for w13 (R = 2 I, K = H), False
+    for w2 (R = H, K = I)."""
+    return _moe_mxfp4_pack(w4, s, gate_up, out, out_s, stream, True)
+
+
+def smallm_fp8bs_moe_mxfp4_unpack(w_packed, s_packed, gate_up: bool, out=None, out_s=None, stream=None):
+    return _moe_mxfp4_pack(w_packed, s_packed, gate_up, out, out_s, stream, False)
+
+
+def smallm_fp8bs_moe_mxfp4(x, topk_ids, topk_w, w13_packed, s13_packed, w2_packed, s2_packed, workspace=None,
+                           y=None, layout_id=None, stream=None):
+    """MoE layer with MXFP4 experts: bf16 x [T, H], int32 topk_ids / fp32 topk_w [T, S], packed fp4x2
+    w13 [E, 2 I, H/2] with packed e8m0 scales [E, 2 I, H/32], packed w2 [E, H, I/2] with scales
+    [E, H, I/32].  Returns (y bf16 [T, H], h bf16 [T * S, I]) as smallm_fp8bs_moe does."""
+    T, S, E, H, I = _moe_common(x, topk_ids, topk_w, w13_packed, w2_packed, True)
+    for t_, n_, shp in ((s13_packed, "s13_packed", (E, 2 * I, H // 32)), (s2_packed, "s2_packed", (E, H, I // 32))):
+        if not isinstance(t_, torch.Tensor) or t_.dtype != torch.uint8 or tuple(t_.shape) != shp:
+            raise ValueError(f"{n_} must be uint8 {shp}")
+        _contig(t_, n_)
+    workspace = _moe_workspace_arg(workspace, T, S, H, I, x.device)
+    y = _out(y, T, H, x.device)
+    lid = smallm_fp8bs_moe_mxfp4_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_moe_mxfp4(_ptr(x), x.stride(0), _ptr(topk_ids), _ptr(topk_w), T, S,
+                                        _ptr(w13_packed), _ptr(s13_packed), _ptr(w2_packed), _ptr(s2_packed), lid,
+                                        E, H, I, _ptr(workspace), workspace.numel(), _ptr(y), y.stride(0),
+                                        _stream(stream)), "smallm_fp8bs_moe_mxfp4")
+    return y, moe_h_view(workspace, T, S, I)
+
+
+def moe_algorithmic_bytes(ids, E: int, H: int, I: int, mxfp4: bool = False) -> int:
     """Bytes one MoE call must move at minimum: each expert in use once (e4m3 w13 and w2 with
-    their fp32 block scales), the bf16 activations, ids and weights, the bf16 intermediate
-    written and read once, and the bf16 output."""
+    their fp32 block scales, or MXFP4 with their e8m0 group scales), the bf16 activations, ids and
+    weights, the bf16 intermediate written and read once, and the bf16 output."""
     import numpy as np
     ids = np.asarray(ids)
     T, S = ids.shape
     used = np.unique(ids[(ids >= 0) & (ids < E)])
-    per_expert = 3 * H * I + 4 * (2 * I // 128) * (H // 128) + 4 * (H // 128) * (I // 128)
+    if mxfp4:
+        per_expert = 3 * H * I // 2 + 3 * H * I // 32
+    else:
+        per_expert = 3 * H * I + 4 * (2 * I // 128) * (H // 128) + 4 * (H // 128) * (I // 128)
     return int(len(used) * per_expert + 2 * T * H + 8 * T * S + 2 * 2 * T * S * I + 2 * T * H)
 
 

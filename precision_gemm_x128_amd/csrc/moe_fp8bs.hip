@@ -50,6 +50,7 @@ constexpr int kMoeThreads = 512;  // 8 waves, split-K over the 128-wide K blocks
 constexpr int kMoeWaves = kMoeThreads / 64;
 constexpr int kMoePairs = SMALLM_FP8BS_MOE_MAX_T * SMALLM_FP8BS_MOE_MAX_S;
 constexpr uint32_t kMoeLayoutId = 0x4D4F4510u;
+constexpr uint32_t kMoeFp4LayoutId = 0x4D4F4504u;
 
 // the 32 e4m3 bytes a lane holds for one 128-K block, as four 8-value bf16 MFMA operands
 __device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi, v8bf out[4]) {
@@ -63,6 +64,24 @@ __device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi
     out[j] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
   }
 }
+
+// the 16 fp4x2 bytes a lane holds (32 e2m1 values of one 32-wide scale group, even K element in
+// each byte's low nibble) as four 8-value bf16 MFMA operands, scaled by the group's power of two
+// inside the conversion
+__device__ __forceinline__ void fp4x32_to_bf16(const u32x4& w, float scale, v8bf out[4]) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 0);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 1);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 2);
+    const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 3);
+    out[j] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+  }
+}
+
+// e8m0 byte b (1 <= b <= 254) as the fp32 2^(b - 127)
+__device__ __forceinline__ float e8m0_f32(uint32_t b) { return __builtin_bit_cast(float, b << 23); }
 
 __device__ __forceinline__ v4f mfma_bf16(const u32x4& a, const v8bf& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), b, c, 0, 0, 0);
@@ -85,16 +104,24 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // the occupied tiles are computed, rows past the last token are zero); its 16 columns are the gate
 // rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.
 
-// The split-K loop of phase 1 over the first NT row tiles: wave w takes K blocks w, w + 8, ...;
-// each block's four MFMAs give the fp32 partial that its 128x128 scale multiplies into acc.
-template <int NT, int MT>
+// The split-K loop of phase 1 over the first NT row tiles: wave w takes K blocks w, w + 8, ...
+// e4m3 weights (FP4 false): each block's four MFMAs give the fp32 partial that its 128x128 scale
+// multiplies into acc.  MXFP4 weights (FP4 true): the 32-wide group scales are applied by the
+// conversion to bf16, so the partial is added to acc as it is.
+template <int NT, int MT, bool FP4>
 __device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp,
+                                             const uint8_t* sbp,
                                              const uint16_t* const (&xr)[MT],
                                              const bool (&row_ok)[MT], int KB, int wave,
                                              v4f (&acc)[MT]) {
   for (int kb = wave; kb < KB; kb += kMoeWaves) {
-    const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
-    const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+    u32x4 b0, b1;
+    if constexpr (FP4) {
+      b0 = load_nt(wp + (int64_t)kb * 1024);
+    } else {
+      b0 = load_nt(wp + (int64_t)kb * 2048);
+      b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+    }
     u32x4 a[NT][4];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
@@ -102,25 +129,39 @@ __device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[mt][i] = row_ok[mt] ? xa[i] : u32x4{0u, 0u, 0u, 0u};
     }
-    const float s = swp[kb];
     v8bf bv[4];
-    e4m3x32_to_bf16(b0, b1, bv);
+    if constexpr (FP4) {
+      fp4x32_to_bf16(b0, e8m0_f32(sbp[(int64_t)kb * 64]), bv);
+      // the block's partial is added in the same block of code as its MFMAs (no MFMA result
+      // crosses the loop's back edge)
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int mt = 0; mt < NT; ++mt) {
+        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
+        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + s * pm[i];
+        for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + pm[i];
+      }
+    } else {
+      const float s = swp[kb];
+      e4m3x32_to_bf16(b0, b1, bv);
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + s * pm[i];
+      }
     }
   }
 }
 
-template <int MT>
+template <int MT, bool FP4>
 __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
-    int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13, int H, int I,
-    uint16_t* __restrict__ h) {
+    int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
+    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
   __shared__ int s_ids[kMoePairs];
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];  // routed tokens, ascending; [MAX_T] = count
   __shared__ float s_red[kMoeWaves * MT * 4 * 64];
@@ -149,8 +190,17 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
   const int j = lane & 15, chunk = lane >> 4;
   // column j < 8 is gate row 8q + j (scale block row q / 16), j >= 8 the matching up row
   const int srow = (j < 8) ? (q >> 4) : ((I >> 7) + (q >> 4));
-  const float* swp = sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
-  const uint8_t* wp = w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
+  const float* swp = nullptr;
+  const uint8_t* sbp = nullptr;
+  const uint8_t* wp;
+  if constexpr (FP4) {
+    // 1 KiB fragments; the packed group scales follow the fragment order, one byte per lane
+    wp = w13 + (int64_t)e * I * H + (int64_t)q * KB * 1024 + lane * 16;
+    sbp = s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64 + lane;
+  } else {
+    swp = sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
+    wp = w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
+  }
   const uint16_t* xr[MT];
   bool row_ok[MT];
 #pragma unroll
@@ -165,11 +215,11 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
   // one straight-line loop per occupied tile count (workgroup-uniform): no branch lies between an
   // MFMA and the multiply-add that reads its result
   if (MT == 1 || tiles == 1)
-    gate_up_loop<1, MT>(wp, swp, xr, row_ok, KB, wave, acc);
+    gate_up_loop<1, MT, FP4>(wp, swp, sbp, xr, row_ok, KB, wave, acc);
   else if (MT == 2 || tiles == 2)
-    gate_up_loop<(MT < 2 ? MT : 2), MT>(wp, swp, xr, row_ok, KB, wave, acc);
+    gate_up_loop<(MT < 2 ? MT : 2), MT, FP4>(wp, swp, sbp, xr, row_ok, KB, wave, acc);
   else
-    gate_up_loop<MT, MT>(wp, swp, xr, row_ok, KB, wave, acc);
+    gate_up_loop<MT, MT, FP4>(wp, swp, sbp, xr, row_ok, KB, wave, acc);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -206,11 +256,12 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
 // token routed to e; the per-wave sums meet in LDS in wave order.  With NS = 1 the result is
 // written as bf16 y, else as the fp32 partial [z][t][n] that moe_reduce_kernel adds in z order.
 
-template <int MT>
+template <int MT, bool FP4>
 __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ tw,
-    int T, int S, int E, const uint8_t* __restrict__ w2, const float* __restrict__ sw2, int H,
-    int I, uint16_t* __restrict__ y, int64_t ldy, float* __restrict__ part) {
+    int T, int S, int E, const uint8_t* __restrict__ w2, const float* __restrict__ sw2,
+    const uint8_t* __restrict__ s2, int H, int I, uint16_t* __restrict__ y, int64_t ldy,
+    float* __restrict__ part) {
   __shared__ int s_ids[kMoePairs];
   __shared__ float s_tw[kMoePairs];
   __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];
@@ -233,7 +284,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
 
   const int KB2 = I >> 7, nb = blockIdx.x >> 3;
   const int j = lane & 15, chunk = lane >> 4;
-  const uint8_t* wtile = w2 + (int64_t)blockIdx.x * KB2 * 2048 + lane * 16;
+  const uint8_t* wtile = w2 + (int64_t)blockIdx.x * KB2 * (FP4 ? 1024 : 2048) + lane * 16;
   v4f acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -256,14 +307,23 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
             wsum[mt] = wsum[mt] + s_tw[t * S + s];
           }
     }
-    const float* swp = sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
-    const uint8_t* wp = wtile + (int64_t)e * H * I;
+    const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
+    const uint8_t* sbp =
+        FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
+    const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
     for (int kb = 0; kb < KB2; ++kb) {
-      const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
-      const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
-      const float s = swp[kb];
       v8bf bv[4];
-      e4m3x32_to_bf16(b0, b1, bv);
+      float s;
+      if constexpr (FP4) {
+        // the group scale is applied by the conversion; the MFMA partial needs no block scale
+        fp4x32_to_bf16(load_nt(wp + (int64_t)kb * 1024), e8m0_f32(sbp[(int64_t)kb * 64]), bv);
+        s = 1.0f;
+      } else {
+        const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
+        const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+        s = swp[kb];
+        e4m3x32_to_bf16(b0, b1, bv);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (!__any(slot[mt] >= 0)) continue;
@@ -361,6 +421,40 @@ __global__ __launch_bounds__(256) void moe_pack_kernel(const uint8_t* __restrict
     *(u32x4*)(dst + lin) = *(const u32x4*)(src + pk);
 }
 
+// MXFP4 (un)packing: one thread per 16-byte chunk of fp4x2 bytes, which is one 32-wide scale
+// group, so the thread moves the group's scale byte too.  Expert e's matrix [R, K] occupies bytes
+// [e R K / 2, (e + 1) R K / 2) of the weight layouts and [e R K / 32, (e + 1) R K / 32) of the
+// scale layouts.  Packed chunk o of an expert: fragment f = o / 64 = tile * (K / 128) + kb, lane
+// = o % 64 (column j = lane % 16, K elements 32 (lane / 16) + [0, 32) of block kb, row-major bytes
+// 64 kb + 16 (lane / 16) + [0, 16)); the packed scale byte o is that group's scale.  Tile rows as
+// for e4m3.
+template <bool PACK, bool GATE_UP>
+__global__ __launch_bounds__(256) void moe_pack_fp4_kernel(const uint8_t* __restrict__ src,
+                                                           const uint8_t* __restrict__ src_s,
+                                                           uint8_t* __restrict__ dst,
+                                                           uint8_t* __restrict__ dst_s, int R,
+                                                           int K, int64_t chunks) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= chunks) return;
+  const int64_t per = (int64_t)R * K / 32;
+  const int64_t e = o / per, oe = o % per;
+  const int KB = K >> 7;
+  const int64_t f = oe >> 6;
+  const int lane = (int)(oe & 63), chunk = lane >> 4, j = lane & 15;
+  const int64_t tile = f / KB, kb = f % KB;
+  const int64_t n = GATE_UP ? ((j < 8) ? tile * 8 + j : (R >> 1) + tile * 8 + (j - 8)) : tile * 16 + j;
+  const int64_t lin = e * R * (K / 2) + n * (K / 2) + kb * 64 + chunk * 16;
+  const int64_t lin_s = e * per + n * (K / 32) + kb * 4 + chunk;
+  const int64_t pk = e * R * (K / 2) + oe * 16;
+  if (PACK) {
+    *(u32x4*)(dst + pk) = *(const u32x4*)(src + lin);
+    dst_s[o] = src_s[lin_s];
+  } else {
+    *(u32x4*)(dst + lin) = *(const u32x4*)(src + pk);
+    dst_s[lin_s] = src_s[o];
+  }
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline int launch_status() { return hipGetLastError() == hipSuccess ? SMALLM_OK : SMALLM_ERR_HIP; }
 
@@ -387,6 +481,29 @@ int moe_pack_common(const uint8_t* src, uint8_t* dst, int E, int R, int K, int g
   return launch_status();
 }
 
+int moe_pack_fp4_common(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, uint8_t* dst_s,
+                        int E, int R, int K, int gate_up, bool pack, void* stream) {
+  if (!src || !src_s || !dst || !dst_s) return SMALLM_ERR_INVALID;
+  if (E < 1 || R <= 0 || K <= 0 || (R & 127) || (K & 127)) return SMALLM_ERR_SHAPE;
+  if (gate_up != 0 && gate_up != 1) return SMALLM_ERR_INVALID;
+  if (!aligned16(src) || !aligned16(dst)) return SMALLM_ERR_ALIGN;
+  const int64_t chunks = (int64_t)E * R * K / 32;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  const hipStream_t st = (hipStream_t)stream;
+  if (pack) {
+    if (gate_up)
+      hipLaunchKernelGGL((moe_pack_fp4_kernel<true, true>), grid, dim3(256), 0, st, src, src_s, dst, dst_s, R, K, chunks);
+    else
+      hipLaunchKernelGGL((moe_pack_fp4_kernel<true, false>), grid, dim3(256), 0, st, src, src_s, dst, dst_s, R, K, chunks);
+  } else {
+    if (gate_up)
+      hipLaunchKernelGGL((moe_pack_fp4_kernel<false, true>), grid, dim3(256), 0, st, src, src_s, dst, dst_s, R, K, chunks);
+    else
+      hipLaunchKernelGGL((moe_pack_fp4_kernel<false, false>), grid, dim3(256), 0, st, src, src_s, dst, dst_s, R, K, chunks);
+  }
+  return launch_status();
+}
+
 // Workgroups per output tile in phase 2: about 32 pairs each, at most 16.
 inline int moe_splits(int T, int S) {
   const int ns = (T * S + 31) / 32;
@@ -400,22 +517,51 @@ inline size_t moe_workspace_bytes(int T, int S, int H, int I) {
   return moe_h_bytes(T, S, I) + (ns > 1 ? (size_t)ns * T * H * 4 : 0);
 }
 
-template <int MT>
+template <int MT, bool FP4>
 void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float* tw, int T, int S,
-                const uint8_t* w13, const float* sw13, const uint8_t* w2, const float* sw2, int E,
-                int H, int I, uint8_t* ws, uint16_t* y, int64_t ldy, hipStream_t st) {
+                const uint8_t* w13, const float* sw13, const uint8_t* s13, const uint8_t* w2,
+                const float* sw2, const uint8_t* s2, int E, int H, int I, uint8_t* ws,
+                uint16_t* y, int64_t ldy, hipStream_t st) {
   uint16_t* h = (uint16_t*)ws;
   float* part = (float*)(ws + moe_h_bytes(T, S, I));
   const int ns = moe_splits(T, S);
-  hipLaunchKernelGGL((moe_gate_up_kernel<MT>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x, ldx,
-                     ids, T, S, E, w13, sw13, H, I, h);
-  hipLaunchKernelGGL((moe_down_kernel<MT>), dim3(H / 16, ns), dim3(kMoeThreads), 0, st, h, ids, tw,
-                     T, S, E, w2, sw2, H, I, y, ldy, part);
+  hipLaunchKernelGGL((moe_gate_up_kernel<MT, FP4>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x,
+                     ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
+  hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kMoeThreads), 0, st, h, ids,
+                     tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part);
   if (ns > 1) {
     const int64_t quads = (int64_t)T * H / 4;
     hipLaunchKernelGGL(moe_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
                        part, ns, T, H, y, ldy);
   }
+}
+
+// Shared argument checks (all before any launch) and the M-bucket dispatch of both weight formats.
+template <bool FP4>
+int moe_call(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, const float* topk_w, int T,
+             int S, const uint8_t* w13, const float* sw13, const uint8_t* s13, const uint8_t* w2,
+             const float* sw2, const uint8_t* s2, uint32_t layout_id, uint32_t want_layout, int E,
+             int H, int I, void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
+             void* stream) {
+  if (!x || !topk_ids || !topk_w || !w13 || !w2 || !workspace || !y) return SMALLM_ERR_INVALID;
+  int st = smallm_fp8bs_moe_supported(T, S, E, H, I);
+  if (st) return st;
+  if (ldx < H || ldy < H) return SMALLM_ERR_SHAPE;
+  if (workspace_bytes < moe_workspace_bytes(T, S, H, I)) return SMALLM_ERR_SHAPE;
+  if (!aligned16(x) || ((ldx * 2) & 15) || !aligned16(w13) || !aligned16(w2) ||
+      ((uintptr_t)workspace & 255u) || ((uintptr_t)y & 1u) || ((uintptr_t)topk_ids & 3u) ||
+      ((uintptr_t)topk_w & 3u))
+    return SMALLM_ERR_ALIGN;
+  if (layout_id != want_layout) return SMALLM_ERR_LAYOUT;
+  const hipStream_t hs = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  if (T <= 16)
+    launch_moe<1, FP4>(x, ldx, topk_ids, topk_w, T, S, w13, sw13, s13, w2, sw2, s2, E, H, I, ws, y, ldy, hs);
+  else if (T <= 32)
+    launch_moe<2, FP4>(x, ldx, topk_ids, topk_w, T, S, w13, sw13, s13, w2, sw2, s2, E, H, I, ws, y, ldy, hs);
+  else
+    launch_moe<3, FP4>(x, ldx, topk_ids, topk_w, T, S, w13, sw13, s13, w2, sw2, s2, E, H, I, ws, y, ldy, hs);
+  return launch_status();
 }
 
 }  // namespace
@@ -459,27 +605,35 @@ int smallm_fp8bs_moe(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, co
                      const uint8_t* w2_packed, const float* sw2, uint32_t layout_id, int E, int H,
                      int I, void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
                      void* stream) {
-  if (!x || !topk_ids || !topk_w || !w13_packed || !sw13 || !w2_packed || !sw2 || !workspace || !y)
-    return SMALLM_ERR_INVALID;
-  int st = smallm_fp8bs_moe_supported(T, S, E, H, I);
-  if (st) return st;
-  if (ldx < H || ldy < H) return SMALLM_ERR_SHAPE;
-  if (workspace_bytes < moe_workspace_bytes(T, S, H, I)) return SMALLM_ERR_SHAPE;
-  if (!aligned16(x) || ((ldx * 2) & 15) || !aligned16(w13_packed) || !aligned16(w2_packed) ||
-      ((uintptr_t)workspace & 255u) || ((uintptr_t)y & 1u) ||
-      ((uintptr_t)topk_ids & 3u) || ((uintptr_t)topk_w & 3u) || ((uintptr_t)sw13 & 3u) ||
-      ((uintptr_t)sw2 & 3u))
-    return SMALLM_ERR_ALIGN;
-  if (layout_id != kMoeLayoutId) return SMALLM_ERR_LAYOUT;
-  const hipStream_t hs = (hipStream_t)stream;
-  uint8_t* ws = (uint8_t*)workspace;
-  if (T <= 16)
-    launch_moe<1>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, w2_packed, sw2, E, H, I, ws, y, ldy, hs);
-  else if (T <= 32)
-    launch_moe<2>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, w2_packed, sw2, E, H, I, ws, y, ldy, hs);
-  else
-    launch_moe<3>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, w2_packed, sw2, E, H, I, ws, y, ldy, hs);
-  return launch_status();
+  if (!sw13 || !sw2) return SMALLM_ERR_INVALID;
+  if (((uintptr_t)sw13 & 3u) || ((uintptr_t)sw2 & 3u)) return SMALLM_ERR_ALIGN;
+  return moe_call<false>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, nullptr, w2_packed, sw2,
+                         nullptr, layout_id, kMoeLayoutId, E, H, I, workspace, workspace_bytes, y,
+                         ldy, stream);
+}
+
+uint32_t smallm_fp8bs_moe_mxfp4_layout_id(void) { return kMoeFp4LayoutId; }
+
+int smallm_fp8bs_moe_mxfp4_pack(const uint8_t* w4, const uint8_t* s, uint8_t* w_packed,
+                                uint8_t* s_packed, int E, int R, int K, int gate_up, void* stream) {
+  return moe_pack_fp4_common(w4, s, w_packed, s_packed, E, R, K, gate_up, true, stream);
+}
+
+int smallm_fp8bs_moe_mxfp4_unpack(const uint8_t* w_packed, const uint8_t* s_packed, uint8_t* w4,
+                                  uint8_t* s, int E, int R, int K, int gate_up, void* stream) {
+  return moe_pack_fp4_common(w_packed, s_packed, w4, s, E, R, K, gate_up, false, stream);
+}
+
+int smallm_fp8bs_moe_mxfp4(const uint16_t* x, int64_t ldx, const int32_t* topk_ids,
+                           const float* topk_w, int T, int S, const uint8_t* w13_packed,
+                           const uint8_t* s13_packed, const uint8_t* w2_packed,
+                           const uint8_t* s2_packed, uint32_t layout_id, int E, int H, int I,
+                           void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
+                           void* stream) {
+  if (!s13_packed || !s2_packed) return SMALLM_ERR_INVALID;
+  return moe_call<true>(x, ldx, topk_ids, topk_w, T, S, w13_packed, nullptr, s13_packed, w2_packed,
+                        nullptr, s2_packed, layout_id, kMoeFp4LayoutId, E, H, I, workspace,
+                        workspace_bytes, y, ldy, stream);
 }
 
 }  // extern "C"

@@ -218,6 +218,49 @@ def test_moe_rejections_happen_before_any_launch():
         assert fn(f, f, 2, 256, 100, 0, None) == 2
         assert fn(_fake(0x10008), f, 2, 256, 128, 1, None) == 3
 
+
+def test_moe_mxfp4_rejections_happen_before_any_launch():
+    """smallm_fp8bs_moe_mxfp4 and its packers refuse bad pointers, shapes, alignment and layout
+    tags on the host (argument order: x, ldx, ids, tw, T, S, w13, s13, w2, s2, layout, E, H, I, ws,
+    ws bytes, y, ldy, stream); scale pointers need no alignment."""
+    L = P.lib()
+    f = _fake()
+    lid = P.smallm_fp8bs_moe_mxfp4_layout_id()
+    assert lid == 0x4D4F4504 and lid != P.smallm_fp8bs_moe_layout_id()
+    wsb = P.smallm_fp8bs_moe_workspace_bytes(4, 11, 4096, 256)
+    ok = [f, 4096, f, f, 4, 11, f, f, f, f, lid, 513, 4096, 256, f, wsb, f, 4096, None]
+    names = ["x", "ldx", "ids", "tw", "T", "S", "w13", "s13", "w2", "s2", "lid", "E", "H", "I",
+             "ws", "wsb", "y", "ldy"]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.smallm_fp8bs_moe_mxfp4(*a)
+
+    for name in ("x", "ids", "tw", "w13", "s13", "w2", "s2", "ws", "y"):
+        assert call(**{name: None}) == 1, name
+    assert call(T=0) == 2 and call(T=49) == 2 and call(S=17) == 2 and call(E=4097) == 2
+    assert call(I=200) == 2 and call(ldy=4000) == 2 and call(wsb=wsb - 1) == 2
+    assert call(x=_fake(0x10008)) == 3 and call(w13=_fake(0x10008)) == 3 and call(w2=_fake(0x10004)) == 3
+    assert call(ws=_fake(0x10080)) == 3 and call(ids=_fake(0x10002)) == 3
+    assert call(lid=P.smallm_fp8bs_moe_layout_id()) == 4
+    # the FP8 entry point refuses the MXFP4 tag, and the other way round
+    fp8 = [f, 4096, f, f, 4, 11, f, f, f, f, lid, 513, 4096, 256, f, wsb, f, 4096, None]
+    assert L.smallm_fp8bs_moe(*fp8) == 4
+    for fn in (L.smallm_fp8bs_moe_mxfp4_pack, L.smallm_fp8bs_moe_mxfp4_unpack):
+        assert fn(None, f, f, f, 2, 256, 128, 1, None) == 1
+        assert fn(f, None, f, f, 2, 256, 128, 1, None) == 1
+        assert fn(f, f, None, f, 2, 256, 128, 1, None) == 1
+        assert fn(f, f, f, None, 2, 256, 128, 1, None) == 1
+        assert fn(f, f, f, f, 2, 256, 128, 2, None) == 1
+        assert fn(f, f, f, f, 0, 256, 128, 1, None) == 2
+        assert fn(f, f, f, f, 2, 200, 128, 0, None) == 2
+        assert fn(f, f, f, f, 2, 256, 100, 0, None) == 2
+        assert fn(_fake(0x10008), f, f, f, 2, 256, 128, 1, None) == 3
+        assert fn(f, f, _fake(0x10008), f, 2, 256, 128, 1, None) == 3
+
+
 def test_binding_rejects_wrong_dtypes_without_gpu():
     import torch
     x16 = torch.zeros((4, 256), dtype=torch.float16)
