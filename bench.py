@@ -37,6 +37,13 @@ M_SWEEP = (1, 4, 8, 16, 32)
 COPIES = 24
 # The pages' fused-kernel times for this shape (us), same hardware and method: context for vs_baseline.
 PAGES_FUSED_US = {1: 6.8, 4: 7.3, 8: 7.7, 16: 9.0, 32: 12.8}
+# The pages' FP8 block-scale small-M MoE kernel on MI355X (E = 513, 11 slots, hidden 4096), in us:
+# intermediate 256 (TP4) and 128 (TP8) from the graph-replay table, TP8 from 24 tokens on from the
+# table with 60 layers rotated (context for the MoE configs; another implementation's times)
+PAGES_MOE_FP8_US = {256: {1: 26.6, 4: 43.4, 8: 63.7, 16: 97.5, 20: 115.3},
+                    128: {1: 22.7, 4: 30.1, 8: 41.4, 16: 60.4, 20: 68.7, 24: 65.2, 28: 75.8, 32: 82.9,
+                          36: 92.0, 48: 111.6}}
+MOE_LAYERS = 16
 
 
 def log(msg):
@@ -209,6 +216,75 @@ def two_launch_beyond(P, torch, np, synthgen, dev, copies, reps, Ms, N=4096, K=2
     return d
 
 
+def moe_sweeps(P, torch, np, synthgen, dev, reps, layers=MOE_LAYERS):
+    """The MoE layers on the pages' shapes (E = 513, 11 slots with the shared expert last, hidden
+    4096): FP8 block-scale at intermediate 256 and 128, MXFP4 at intermediate 256.  Each of `layers`
+    layers has its own 513 packed experts and its own routing; one HIP graph issues one call per
+    layer, so every call reads experts no other call in the graph touched (cold weights).  Weight
+    bytes are random codes (e4m3 without NaN codes, |w| <= 1.875 times a 2e-3 block scale; any
+    e2m1 code with scale byte 120), which changes nothing in the arithmetic's timing."""
+    E, S, H = 513, 11, 4096
+    res = {}
+    x = torch.from_numpy(synthgen.gen_x(48, H, seed=5).view(np.int16)).to(dev).view(torch.bfloat16)
+    for fmt, I, Ts in (("fp8", 256, (1, 4, 8, 16, 20)), ("fp8", 128, (1, 4, 8, 16, 20, 24, 32, 48)),
+                       ("mxfp4", 256, (1, 4, 8, 16, 20, 40))):
+        fp4 = fmt == "mxfp4"
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234 + I)
+        kdiv = 2 if fp4 else 1
+        w13 = torch.empty((layers * E, 2 * I, H // kdiv), dtype=torch.uint8, device=dev)
+        w2 = torch.empty((layers * E, H, I // kdiv), dtype=torch.uint8, device=dev)
+        if fp4:
+            s13 = torch.empty((layers * E, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+            s2 = torch.empty((layers * E, H, I // 32), dtype=torch.uint8, device=dev)
+        else:
+            s13 = torch.full((layers * E, 2 * I // 128, H // 128), 2e-3, dtype=torch.float32, device=dev)
+            s2 = torch.full((layers * E, H // 128, I // 128), 2e-3, dtype=torch.float32, device=dev)
+        for l in range(layers):
+            sl = slice(l * E, (l + 1) * E)
+            a = torch.randint(0, 256, (E, 2 * I, H // kdiv), dtype=torch.uint8, device=dev, generator=g)
+            b = torch.randint(0, 256, (E, H, I // kdiv), dtype=torch.uint8, device=dev, generator=g)
+            if fp4:
+                P.smallm_fp8bs_moe_mxfp4_pack(a, torch.full((E, 2 * I, H // 32), 120, dtype=torch.uint8, device=dev),
+                                              True, out=w13[sl], out_s=s13[sl])
+                P.smallm_fp8bs_moe_mxfp4_pack(b, torch.full((E, H, I // 32), 120, dtype=torch.uint8, device=dev),
+                                              False, out=w2[sl], out_s=s2[sl])
+            else:
+                P.smallm_fp8bs_moe_pack(a & 0xBF, True, out=w13[sl])
+                P.smallm_fp8bs_moe_pack(b & 0xBF, False, out=w2[sl])
+            del a, b
+        torch.cuda.synchronize()
+        d = {}
+        for T in Ts:
+            routes = [synthgen.gen_moe_routing(T, S, E, seed=100 * l + T) for l in range(layers)]
+            ids = [torch.from_numpy(r[0]).to(dev) for r in routes]
+            tw = [torch.from_numpy(r[1]).to(dev) for r in routes]
+            ws = P.moe_workspace(T, S, H, I, device=dev)
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            xt = x[:T]
+
+            def call(l):
+                sl = slice(l * E, (l + 1) * E)
+                if fp4:
+                    P.smallm_fp8bs_moe_mxfp4(xt, ids[l], tw[l], w13[sl], s13[sl], w2[sl], s2[sl], workspace=ws, y=y)
+                else:
+                    P.smallm_fp8bs_moe(xt, ids[l], tw[l], w13[sl], s13[sl], w2[sl], s2[sl], workspace=ws, y=y)
+
+            us = graph_us(torch, call, layers, reps)
+            nbytes = sum(P.moe_algorithmic_bytes(r[0], E, H, I, mxfp4=fp4) for r in routes) / layers
+            gbs = nbytes / (us * 1e-6) / 1e9
+            e = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes), "GB_s": round(gbs, 1),
+                 "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1), "launches": 2 + (P.smallm_fp8bs_moe_splits(T, S) > 1)}
+            if not fp4 and T in PAGES_MOE_FP8_US[I]:
+                e["pages_fp8_kernel_us"] = PAGES_MOE_FP8_US[I][T]
+            d[str(T)] = e
+        res[f"moe_{fmt}_E{E}_S{S}_H{H}_I{I}"] = d
+        log(f"[bench] moe {fmt} I={I}: " + " ".join(f"T={T} {d[str(T)]['us_per_call']:.1f}us" for T in Ts))
+        del w13, w2, s13, s2
+        torch.cuda.empty_cache()
+    return res
+
+
 def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
     """The other workloads of the method, timed the same way (per-M us/call, GB/s, % of peak):
     the single 4096x2048 call at M=4; the M sweeps on 4608x4096 and 4096x2048 with outlier rows;
@@ -253,6 +329,7 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
         res[f"e8m0_vs_fp32_{N}x{K}"] = d
         log(f"[bench] {N}x{K} e8m0 vs fp32: " + " ".join(f"M={M} {te[M]:.2f}/{tf[M]:.2f}us" for M in ms))
     res.update(producer_pipeline(P, torch, np, synthgen, dev, copies, reps))
+    res.update(moe_sweeps(P, torch, np, synthgen, dev, reps))
     return res
 
 
