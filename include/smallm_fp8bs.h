@@ -233,7 +233,8 @@ int smallm_fp8bs_moe_unpack(const uint8_t* w_packed, uint8_t* w8, int E, int R, 
 /* Workspace bytes smallm_fp8bs_moe needs for (T, S, H, I), 0 when out of range: the bf16
  * intermediate h [T * S, I] rounded up to 256 bytes, then, when the down projection is split over
  * NS = smallm_fp8bs_moe_splits(T, S) > 1 workgroups per output tile, fp32 partial sums
- * [NS, T, H]. */
+ * [NS, T, H].  Its contents need no initialisation; calls that share a workspace must not
+ * overlap. */
 size_t smallm_fp8bs_moe_workspace_bytes(int T, int S, int H, int I);
 
 /* NS for (T, S): ceil(T * S / 32) clamped to [1, 16]; 0 when out of range. */

@@ -19,9 +19,9 @@
 //    expert exits after one pass over the ids in LDS, the others gather the expert's tokens with
 //    a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
 //    range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
-//    and its waves walk the experts whose first pair lies in its range.  With NS > 1 the
-//    workgroups leave fp32 partial sums in the caller's workspace and a third launch adds them in
-//    range order.
+//    and its waves walk the experts whose first pair lies in its range, gathering each expert's
+//    tokens into MFMA rows as phase 1 does.  With NS > 1 the workgroups leave fp32 partial sums
+//    in the caller's workspace and a third launch adds them in range order.
 //  * Packed weights: every 16-row x 128-K block of an expert matrix is one 2 KiB fragment in
 //    the lane order of an MFMA operand (lane l = 16 c + j holds row j and K bytes [32 c, 32 c + 32)
 //    of the block, bytes 0..15 in the first KiB and 16..31 in the second), fragments of one
@@ -100,20 +100,20 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // ---------------------------------------------------------------------------------------------
 //
 // grid (T * S, I / 8), 512 threads.  Workgroup (p, q) works when pair p is the first pair naming
-// its expert e.  Its A rows are the tokens routed to e, ascending (MT tiles of 16 at most, only
-// the occupied tiles are computed, rows past the last token are zero); its 16 columns are the gate
-// rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.
+// its expert e.  Its A rows are the tokens routed to e, ascending, in tiles of 16 (rows past the
+// last token are zero); its 16 columns are the gate rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.
 
-// The split-K loop of phase 1 over the first NT row tiles: wave w takes K blocks w, w + 8, ...
+// The split-K loop of phase 1 for one 16-row tile: wave w takes K blocks w, w + 8, ...  (one
+// block's loads in flight per wave: issuing several blocks' loads first raised the registers from
+// 48 to 120 and, with fewer workgroups per CU, measured slower from four tokens on).
 // e4m3 weights (FP4 false): each block's four MFMAs give the fp32 partial that its 128x128 scale
 // multiplies into acc.  MXFP4 weights (FP4 true): the 32-wide group scales are applied by the
-// conversion to bf16, so the partial is added to acc as it is.
-template <int NT, int MT, bool FP4>
-__device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp,
-                                             const uint8_t* sbp,
-                                             const uint16_t* const (&xr)[MT],
-                                             const bool (&row_ok)[MT], int KB, int wave,
-                                             v4f (&acc)[MT]) {
+// conversion to bf16, so the partial is added to acc as it is.  Every partial is added in the same
+// block of code as its MFMAs (no MFMA result crosses a branch).
+template <bool FP4>
+__device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp, const uint8_t* sbp,
+                                            const uint16_t* xr, bool row_ok, int KB, int wave) {
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int kb = wave; kb < KB; kb += kMoeWaves) {
     u32x4 b0, b1;
     if constexpr (FP4) {
@@ -122,49 +122,36 @@ __device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp
       b0 = load_nt(wp + (int64_t)kb * 2048);
       b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
     }
-    u32x4 a[NT][4];
+    const u32x4* xa = (const u32x4*)(xr + kb * 128);
+    u32x4 a[4];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      const u32x4* xa = (const u32x4*)(xr[mt] + kb * 128);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[mt][i] = row_ok[mt] ? xa[i] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; ++i) a[i] = row_ok ? xa[i] : u32x4{0u, 0u, 0u, 0u};
     v8bf bv[4];
+    float sc;
     if constexpr (FP4) {
       fp4x32_to_bf16(b0, e8m0_f32(sbp[(int64_t)kb * 64]), bv);
-      // the block's partial is added in the same block of code as its MFMAs (no MFMA result
-      // crosses the loop's back edge)
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + pm[i];
-      }
+      sc = 1.0f;
     } else {
-      const float s = swp[kb];
+      sc = swp[kb];
       e4m3x32_to_bf16(b0, b1, bv);
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[mt][i], bv[i], pm);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] + s * pm[i];
-      }
     }
+    v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = acc[i] + sc * pm[i];
   }
+  return acc;
 }
 
-template <int MT, bool FP4>
+template <bool FP4>
 __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
     const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
   __shared__ int s_ids[kMoePairs];
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];  // routed tokens, ascending; [MAX_T] = count
-  __shared__ float s_red[kMoeWaves * MT * 4 * 64];
+  __shared__ float s_red[kMoeWaves * 4 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * S;
   const int p = blockIdx.x, q = blockIdx.y;
@@ -201,48 +188,35 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
     swp = sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
     wp = w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
   }
-  const uint16_t* xr[MT];
-  bool row_ok[MT];
+  // the row tiles one after another (only an expert with more than 16 tokens, in practice the
+  // shared one, has a second or third; its weight slice is then re-read from L2)
+  for (int tile = 0; tile < tiles; ++tile) {
+    const int idx = 16 * tile + j;
+    const bool row_ok = idx < Me;
+    const uint16_t* xr = x + (int64_t)(row_ok ? s_tok[idx] : 0) * ldx + chunk * 32;
+    const v4f acc = gate_up_loop<FP4>(wp, swp, sbp, xr, row_ok, KB, wave);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int idx = 16 * mt + j;
-    row_ok[mt] = idx < Me;
-    xr[mt] = x + (int64_t)(row_ok[mt] ? s_tok[idx] : 0) * ldx + chunk * 32;
-  }
-  v4f acc[MT];
+    for (int i = 0; i < 4; ++i) s_red[(wave * 4 + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (tid < 128) {
+      const int r = tid >> 3, c = tid & 7;
+      const int k = 16 * tile + r;
+      if (k < Me) {
+        const int t = s_tok[k];
+        // D row r, column c sits in lane 16 (r / 4) + c, register r % 4
+        const int base = (r & 3) * 64 + 16 * (r >> 2) + c;
+        float g = 0.0f, u = 0.0f;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // one straight-line loop per occupied tile count (workgroup-uniform): no branch lies between an
-  // MFMA and the multiply-add that reads its result
-  if (MT == 1 || tiles == 1)
-    gate_up_loop<1, MT, FP4>(wp, swp, sbp, xr, row_ok, KB, wave, acc);
-  else if (MT == 2 || tiles == 2)
-    gate_up_loop<(MT < 2 ? MT : 2), MT, FP4>(wp, swp, sbp, xr, row_ok, KB, wave, acc);
-  else
-    gate_up_loop<MT, MT, FP4>(wp, swp, sbp, xr, row_ok, KB, wave, acc);
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[((wave * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
-  __syncthreads();
-
-  for (int o = tid; o < MT * 128; o += kMoeThreads) {
-    const int mt = o >> 7, r = (o >> 3) & 15, c = o & 7;
-    const int idx = 16 * mt + r;
-    if (idx >= Me) continue;
-    const int t = s_tok[idx];
-    // D row r, column c sits in lane 16 (r / 4) + c, register r % 4
-    const int base = (mt * 4 + (r & 3)) * 64 + 16 * (r >> 2) + c;
-    float g = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMoeWaves; ++w) {
-      g = g + s_red[w * MT * 256 + base];
-      u = u + s_red[w * MT * 256 + base + 8];
+        for (int w = 0; w < kMoeWaves; ++w) {
+          g = g + s_red[w * 256 + base];
+          u = u + s_red[w * 256 + base + 8];
+        }
+        const uint16_t hb = bf16_bits((g / (1.0f + expf(-g))) * u);
+        for (int s = 0; s < S; ++s)
+          if (s_ids[t * S + s] == e) h[(int64_t)(t * S + s) * I + 8 * q + c] = hb;
+      }
     }
-    const uint16_t hb = bf16_bits((g / (1.0f + expf(-g))) * u);
-    for (int s = 0; s < S; ++s)
-      if (s_ids[t * S + s] == e) h[(int64_t)(t * S + s) * I + 8 * q + c] = hb;
+    __syncthreads();
   }
 }
 
@@ -250,11 +224,17 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
 // phase 2: down projection, top-k weights in fp32, sum over slots -> y (bf16)
 // ---------------------------------------------------------------------------------------------
 //
-// grid (H / 16, NS), 512 threads.  Workgroup (b, z) owns output columns [16 b, 16 b + 16) for all
-// T tokens and the pairs [z P / NS, (z + 1) P / NS).  Wave w takes the pairs of that range with
-// index = w (mod 8) that are the first pair of their expert e and adds tw * (h . w2[e]^T) for every
-// token routed to e; the per-wave sums meet in LDS in wave order.  With NS = 1 the result is
-// written as bf16 y, else as the fp32 partial [z][t][n] that moe_reduce_kernel adds in z order.
+// grid (H / 16, NS), 512 threads.  Workgroup (b, z) owns output columns [16 b, 16 b + 16) and the
+// pairs [z P / NS, (z + 1) P / NS).  Wave w takes the pairs of that range with index = w (mod 8)
+// that are the first pair of their expert e.  It gathers the tokens routed to e with a ballot
+// (ascending, each with the first slot naming e and the sum of the top-k weights of the slots
+// naming e), runs one 16-row MFMA tile per 16 of those tokens over the expert's K blocks, and adds
+// weight * (h . w2[e]^T) into the token's row of its own LDS slice.  The slices meet in wave
+// order.  With NS = 1 the workgroup writes bf16 y, else the fp32 partial [z][t][n] that
+// moe_reduce_kernel adds in z order.  (Adding the partials in the last workgroup to arrive would
+// need a device-scope fence per workgroup, which on this target writes back and invalidates the
+// whole L2 and measured several times slower than the extra launch.)  Every result is
+// deterministic.
 
 template <int MT, bool FP4>
 __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
@@ -262,10 +242,14 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
     int T, int S, int E, const uint8_t* __restrict__ w2, const float* __restrict__ sw2,
     const uint8_t* __restrict__ s2, int H, int I, uint16_t* __restrict__ y, int64_t ldy,
     float* __restrict__ part) {
+  constexpr int ROWS = 16 * MT;
   __shared__ int s_ids[kMoePairs];
   __shared__ float s_tw[kMoePairs];
   __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];
-  __shared__ float s_red[kMoeWaves * MT * 4 * 64];
+  __shared__ float s_acc[kMoeWaves][ROWS][16];
+  __shared__ int s_tok[kMoeWaves][ROWS];    // token of gathered row k (this wave's current expert)
+  __shared__ int s_hrow[kMoeWaves][ROWS];   // its h row t * S + first slot naming the expert
+  __shared__ float s_wt[kMoeWaves][ROWS];   // its summed top-k weight
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * S;
   const int NS = gridDim.y, z = blockIdx.y;
@@ -275,6 +259,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
     s_tw[i] = tw[i];
   }
   for (int i = tid; i < E; i += kMoeThreads) s_first[i] = INT_MAX;
+  for (int i = lane; i < ROWS * 16; i += 64) s_acc[wave][i >> 4][i & 15] = 0.0f;
   __syncthreads();
   for (int i = tid; i < P; i += kMoeThreads) {
     const int e = s_ids[i];
@@ -285,90 +270,84 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
   const int KB2 = I >> 7, nb = blockIdx.x >> 3;
   const int j = lane & 15, chunk = lane >> 4;
   const uint8_t* wtile = w2 + (int64_t)blockIdx.x * KB2 * (FP4 ? 1024 : 2048) + lane * 16;
-  v4f acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int p = lo + wave; p < hi; p += kMoeWaves) {
     const int e = s_ids[p];
     if (e < 0 || e >= E || s_first[e] != p) continue;
-    // A row j of tile mt is token 16 mt + j: its first slot naming e and its summed weight
-    int slot[MT];
-    float wsum[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int t = 16 * mt + j;
-      slot[mt] = -1;
-      wsum[mt] = 0.0f;
-      if (t < T)
-        for (int s = 0; s < S; ++s)
-          if (s_ids[t * S + s] == e) {
-            if (slot[mt] < 0) slot[mt] = s;
-            wsum[mt] = wsum[mt] + s_tw[t * S + s];
-          }
+    // gather: lane t (< T) is routed to e when some slot of token t names it
+    int slot = -1;
+    float wsum = 0.0f;
+    if (lane < T)
+      for (int s = 0; s < S; ++s)
+        if (s_ids[lane * S + s] == e) {
+          if (slot < 0) slot = s;
+          wsum = wsum + s_tw[lane * S + s];
+        }
+    const uint64_t m = __ballot(slot >= 0);
+    if (slot >= 0) {
+      const int k = __popcll(m & ((1ull << lane) - 1ull));
+      s_tok[wave][k] = lane;
+      s_hrow[wave][k] = lane * S + slot;
+      s_wt[wave][k] = wsum;
     }
+    const int Me = __popcll(m);
     const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
     const uint8_t* sbp =
         FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
     const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
-    for (int kb = 0; kb < KB2; ++kb) {
-      v8bf bv[4];
-      float s;
-      if constexpr (FP4) {
-        // the group scale is applied by the conversion; the MFMA partial needs no block scale
-        fp4x32_to_bf16(load_nt(wp + (int64_t)kb * 1024), e8m0_f32(sbp[(int64_t)kb * 64]), bv);
-        s = 1.0f;
-      } else {
-        const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
-        const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
-        s = swp[kb];
-        e4m3x32_to_bf16(b0, b1, bv);
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (!__any(slot[mt] >= 0)) continue;
-        u32x4 a[4];
-        if (slot[mt] >= 0) {
-          const int t = 16 * mt + j;
-          const u32x4* ha =
-              (const u32x4*)(h + (int64_t)(t * S + slot[mt]) * I + kb * 128 + chunk * 32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = ha[i];
+    for (int tile = 0; tile * 16 < Me; ++tile) {
+      const int k = 16 * tile + j;
+      const bool ok = k < Me;
+      const uint16_t* hr = h + (int64_t)(ok ? s_hrow[wave][k] : 0) * I + chunk * 32;
+      v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int kb = 0; kb < KB2; ++kb) {
+        v8bf bv[4];
+        float sc;
+        if constexpr (FP4) {
+          // the group scale is applied by the conversion; the partial needs no block scale
+          fp4x32_to_bf16(load_nt(wp + (int64_t)kb * 1024), e8m0_f32(sbp[(int64_t)kb * 64]), bv);
+          sc = 1.0f;
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = u32x4{0u, 0u, 0u, 0u};
+          const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
+          const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+          sc = swp[kb];
+          e4m3x32_to_bf16(b0, b1, bv);
         }
+        const u32x4* ha = (const u32x4*)(hr + kb * 128);
+        u32x4 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = ok ? ha[i] : u32x4{0u, 0u, 0u, 0u};
         v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
-        // D row 4 (lane / 16) + i belongs to token 16 mt + that row, whose weight lane (row) holds
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float wr = __shfl(wsum[mt], 4 * (lane >> 4) + i);
-          acc[mt][i] = acc[mt][i] + wr * (s * pm[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + sc * pm[i];
+      }
+      // D row r = 4 (lane / 16) + i is gathered row 16 tile + r; its token's LDS row gets the
+      // weighted partial (rows are distinct tokens, so no two lanes add to one element)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * tile + 4 * chunk + i;
+        if (r < Me) {
+          const int t = s_tok[wave][r];
+          s_acc[wave][t][j] = s_acc[wave][t][j] + s_wt[wave][r] * acc[i];
         }
       }
     }
   }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[((wave * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
   __syncthreads();
 
-  for (int o = tid; o < MT * 256; o += kMoeThreads) {
-    const int mt = o >> 8, r = (o >> 4) & 15, c = o & 15;
-    const int t = 16 * mt + r;
-    if (t >= T) continue;
-    const int base = (mt * 4 + (r & 3)) * 64 + 16 * (r >> 2) + c;
+  // this workgroup's T x 16 result: the wave slices in wave order
+  const int64_t col0 = (int64_t)blockIdx.x * 16;
+  for (int o = tid; o < T * 16; o += kMoeThreads) {
+    const int t = o >> 4, c = o & 15;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMoeWaves; ++w) v = v + s_red[w * MT * 256 + base];
+    for (int w = 0; w < kMoeWaves; ++w) v = v + s_acc[w][t][c];
     if (NS == 1)
-      y[(int64_t)t * ldy + blockIdx.x * 16 + c] = bf16_bits(v);
+      y[(int64_t)t * ldy + col0 + c] = bf16_bits(v);
     else
-      part[((int64_t)z * T + t) * H + blockIdx.x * 16 + c] = v;
+      part[((int64_t)z * T + t) * H + col0 + c] = v;
   }
 }
 
@@ -525,7 +504,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
   uint16_t* h = (uint16_t*)ws;
   float* part = (float*)(ws + moe_h_bytes(T, S, I));
   const int ns = moe_splits(T, S);
-  hipLaunchKernelGGL((moe_gate_up_kernel<MT, FP4>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x,
+  hipLaunchKernelGGL((moe_gate_up_kernel<FP4>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x,
                      ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kMoeThreads), 0, st, h, ids,
                      tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part);
