@@ -48,6 +48,10 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kMoeThreads = 512;  // 8 waves, split-K over the 128-wide K blocks
 constexpr int kMoeWaves = kMoeThreads / 64;
+// phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
+// workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
+constexpr int kDownThreads = 1024;
+constexpr int kDownWaves = kDownThreads / 64;
 constexpr int kMoePairs = SMALLM_FP8BS_MOE_MAX_T * SMALLM_FP8BS_MOE_MAX_S;
 constexpr uint32_t kMoeLayoutId = 0x4D4F4510u;
 constexpr uint32_t kMoeFp4LayoutId = 0x4D4F4504u;
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
 // deterministic.
 
 template <int MT, bool FP4>
-__global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
+__global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ tw,
     int T, int S, int E, const uint8_t* __restrict__ w2, const float* __restrict__ sw2,
     const uint8_t* __restrict__ s2, int H, int I, uint16_t* __restrict__ y, int64_t ldy,
@@ -246,22 +250,22 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
   __shared__ int s_ids[kMoePairs];
   __shared__ float s_tw[kMoePairs];
   __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];
-  __shared__ float s_acc[kMoeWaves][ROWS][16];
-  __shared__ int s_tok[kMoeWaves][ROWS];    // token of gathered row k (this wave's current expert)
-  __shared__ int s_hrow[kMoeWaves][ROWS];   // its h row t * S + first slot naming the expert
-  __shared__ float s_wt[kMoeWaves][ROWS];   // its summed top-k weight
+  __shared__ float s_acc[kDownWaves][ROWS][16];
+  __shared__ int s_tok[kDownWaves][ROWS];    // token of gathered row k (this wave's current expert)
+  __shared__ int s_hrow[kDownWaves][ROWS];   // its h row t * S + first slot naming the expert
+  __shared__ float s_wt[kDownWaves][ROWS];   // its summed top-k weight
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * S;
   const int NS = gridDim.y, z = blockIdx.y;
   const int lo = (int)((int64_t)z * P / NS), hi = (int)((int64_t)(z + 1) * P / NS);
-  for (int i = tid; i < P; i += kMoeThreads) {
+  for (int i = tid; i < P; i += kDownThreads) {
     s_ids[i] = ids[i];
     s_tw[i] = tw[i];
   }
-  for (int i = tid; i < E; i += kMoeThreads) s_first[i] = INT_MAX;
+  for (int i = tid; i < E; i += kDownThreads) s_first[i] = INT_MAX;
   for (int i = lane; i < ROWS * 16; i += 64) s_acc[wave][i >> 4][i & 15] = 0.0f;
   __syncthreads();
-  for (int i = tid; i < P; i += kMoeThreads) {
+  for (int i = tid; i < P; i += kDownThreads) {
     const int e = s_ids[i];
     if (e >= 0 && e < E) atomicMin(&s_first[e], i);
   }
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
   const int j = lane & 15, chunk = lane >> 4;
   const uint8_t* wtile = w2 + (int64_t)blockIdx.x * KB2 * (FP4 ? 1024 : 2048) + lane * 16;
 
-  for (int p = lo + wave; p < hi; p += kMoeWaves) {
+  for (int p = lo + wave; p < hi; p += kDownWaves) {
     const int e = s_ids[p];
     if (e < 0 || e >= E || s_first[e] != p) continue;
     // gather: lane t (< T) is routed to e when some slot of token t names it
@@ -339,11 +343,11 @@ __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
 
   // this workgroup's T x 16 result: the wave slices in wave order
   const int64_t col0 = (int64_t)blockIdx.x * 16;
-  for (int o = tid; o < T * 16; o += kMoeThreads) {
+  for (int o = tid; o < T * 16; o += kDownThreads) {
     const int t = o >> 4, c = o & 15;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMoeWaves; ++w) v = v + s_acc[w][t][c];
+    for (int w = 0; w < kDownWaves; ++w) v = v + s_acc[w][t][c];
     if (NS == 1)
       y[(int64_t)t * ldy + col0 + c] = bf16_bits(v);
     else
@@ -483,9 +487,9 @@ int moe_pack_fp4_common(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, 
   return launch_status();
 }
 
-// Workgroups per output tile in phase 2: about 32 pairs each, at most 16.
+// Workgroups per output tile in phase 2: about 64 pairs each (four per wave), at most 16.
 inline int moe_splits(int T, int S) {
-  const int ns = (T * S + 31) / 32;
+  const int ns = (T * S + 63) / 64;
   return ns < 1 ? 1 : (ns > 16 ? 16 : ns);
 }
 
@@ -506,7 +510,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
   const int ns = moe_splits(T, S);
   hipLaunchKernelGGL((moe_gate_up_kernel<FP4>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x,
                      ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
-  hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kMoeThreads), 0, st, h, ids,
+  hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kDownThreads), 0, st, h, ids,
                      tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part);
   if (ns > 1) {
     const int64_t quads = (int64_t)T * H / 4;
