@@ -32,6 +32,11 @@
 //    128-K block's fp32 partial is multiplied by its block scale and added to an fp32
 //    accumulator.  Per-wave split-K partials are summed through LDS in a fixed order, so every
 //    result is deterministic and graph replays equal eager runs.
+//  * MXFP4 experts (sglang "[AMD] Small-M MXFP4 fused-MoE kernel for gfx950 (Qwen)",
+//    Modifications; OCP Microscaling e2m1 elements with one e8m0 scale per 32 K elements): the
+//    same kernels with FP4 = true.  A fragment is 1 KiB (16 rows x 128 K as fp4x2); each lane's
+//    16 bytes are exactly one scale group, whose byte is packed in fragment order beside it, and
+//    v_cvt_scalef32_pk_bf16_fp4 applies that power of two while converting (exact).
 
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -46,8 +51,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int kMoeThreads = 512;  // 8 waves, split-K over the 128-wide K blocks
-constexpr int kMoeWaves = kMoeThreads / 64;
+// phase 1: 8 waves per workgroup, each over K/128/8 blocks of the expert's 16 rows (16 waves
+// measured slower from four tokens on: most workgroups only find that their pair is not the first
+// of its expert, and a larger workgroup makes that dearer)
+constexpr int kGateThreads = 512;
+constexpr int kGateWaves = kGateThreads / 64;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
 // workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
 constexpr int kDownThreads = 1024;
@@ -118,7 +126,7 @@ template <bool FP4>
 __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp, const uint8_t* sbp,
                                             const uint16_t* xr, bool row_ok, int KB, int wave) {
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kb = wave; kb < KB; kb += kMoeWaves) {
+  for (int kb = wave; kb < KB; kb += kGateWaves) {
     u32x4 b0, b1;
     if constexpr (FP4) {
       b0 = load_nt(wp + (int64_t)kb * 1024);
@@ -149,22 +157,22 @@ __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp,
 }
 
 template <bool FP4>
-__global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
+__global__ __launch_bounds__(kGateThreads) void moe_gate_up_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
     const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
   __shared__ int s_ids[kMoePairs];
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];  // routed tokens, ascending; [MAX_T] = count
-  __shared__ float s_red[kMoeWaves * 4 * 64];
+  __shared__ float s_red[kGateWaves * 4 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * S;
   const int p = blockIdx.x, q = blockIdx.y;
-  for (int i = tid; i < P; i += kMoeThreads) s_ids[i] = ids[i];
+  for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
   __syncthreads();
   const int e = s_ids[p];
   if (e < 0 || e >= E) return;
   bool earlier = false;
-  for (int i = tid; i < p; i += kMoeThreads) earlier |= (s_ids[i] == e);
+  for (int i = tid; i < p; i += kGateThreads) earlier |= (s_ids[i] == e);
   if (wave == 0) {
     bool mine = false;
     if (lane < T)
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
         const int base = (r & 3) * 64 + 16 * (r >> 2) + c;
         float g = 0.0f, u = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kMoeWaves; ++w) {
+        for (int w = 0; w < kGateWaves; ++w) {
           g = g + s_red[w * 256 + base];
           u = u + s_red[w * 256 + base + 8];
         }
@@ -228,8 +236,8 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gate_up_kernel(
 // phase 2: down projection, top-k weights in fp32, sum over slots -> y (bf16)
 // ---------------------------------------------------------------------------------------------
 //
-// grid (H / 16, NS), 512 threads.  Workgroup (b, z) owns output columns [16 b, 16 b + 16) and the
-// pairs [z P / NS, (z + 1) P / NS).  Wave w takes the pairs of that range with index = w (mod 8)
+// grid (H / 16, NS), 1024 threads.  Workgroup (b, z) owns output columns [16 b, 16 b + 16) and the
+// pairs [z P / NS, (z + 1) P / NS).  Wave w takes the pairs of that range with index = w (mod 16)
 // that are the first pair of their expert e.  It gathers the tokens routed to e with a ballot
 // (ascending, each with the first slot naming e and the sum of the top-k weights of the slots
 // naming e), runs one 16-row MFMA tile per 16 of those tokens over the expert's K blocks, and adds
@@ -508,7 +516,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
   uint16_t* h = (uint16_t*)ws;
   float* part = (float*)(ws + moe_h_bytes(T, S, I));
   const int ns = moe_splits(T, S);
-  hipLaunchKernelGGL((moe_gate_up_kernel<FP4>), dim3(T * S, I / 8), dim3(kMoeThreads), 0, st, x,
+  hipLaunchKernelGGL((moe_gate_up_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st, x,
                      ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kDownThreads), 0, st, h, ids,
                      tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part);
