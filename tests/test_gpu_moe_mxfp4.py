@@ -227,6 +227,61 @@ def test_mxfp4_scale_range_ends():
     _BANKS.clear()
 
 
+def _as_mxfp4(values):
+    """Exact MXFP4 encoding of an fp64 matrix [R, K] whose every 32-wide group is a power of two
+    times e2m1 values: (fp4x2 bytes [R, K/2], e8m0 scales [R, K/32]), by search over the scale
+    bytes; all-zero groups get byte 127.  Raises if a group has no exact encoding."""
+    e2m1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    R, K = values.shape
+    codes = np.zeros((R, K), dtype=np.uint8)
+    scales = np.full((R, K // 32), 127, dtype=np.uint8)
+    for r in range(R):
+        for g in range(K // 32):
+            v = values[r, 32 * g:32 * g + 32]
+            if not v.any():
+                continue
+            for b in range(2, 253):
+                m = np.abs(v) / 2.0 ** (b - 127)
+                if all(x in e2m1 for x in m):
+                    scales[r, g] = b
+                    for i, x in enumerate(m):
+                        codes[r, 32 * g + i] = e2m1.index(x) | (8 if v[i] < 0 else 0)
+                    break
+            else:
+                raise ValueError(f"row {r} group {g} has no exact MXFP4 encoding")
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), scales
+
+
+def test_mxfp4_handworked_layer_on_gpu():
+    """The hand-worked layer of tests/golden/moe_handworked.json with its weights re-expressed
+    exactly in MXFP4 (every weight there is an e2m1 value times a power of two): the dequantised
+    weights are the same numbers, so h and y must be the hand-worked bits."""
+    note("mxfp4 hand-worked layer")
+    from test_oracle_moe import golden_layer
+    G, x, ids, tw, w13, sw13, w2, sw2 = golden_layer()
+    E = w13.shape[0]
+    d13 = [oracle.dequant_weight(w13[e], sw13[e]) for e in range(E)]
+    d2 = [oracle.dequant_weight(w2[e], sw2[e]) for e in range(E)]
+    enc13 = [_as_mxfp4(d) for d in d13]
+    enc2 = [_as_mxfp4(d) for d in d2]
+    for e in range(E):    # the encodings dequantise to the same values
+        assert np.array_equal(oracle.dequant_mxfp4(*enc13[e]), d13[e])
+        assert np.array_equal(oracle.dequant_mxfp4(*enc2[e]), d2[e])
+    st = lambda lst, i: torch.from_numpy(np.stack([t[i] for t in lst])).to(DEV)
+    w13p, s13p = P.smallm_fp8bs_moe_mxfp4_pack(st(enc13, 0), st(enc13, 1), True)
+    w2p, s2p = P.smallm_fp8bs_moe_mxfp4_pack(st(enc2, 0), st(enc2, 1), False)
+    y, h = P.smallm_fp8bs_moe_mxfp4(to_dev_bf16(x), torch.from_numpy(ids).to(DEV), torch.from_numpy(tw).to(DEV),
+                                    w13p, s13p, w2p, s2p)
+    torch.cuda.synchronize()
+    y = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    h = h.view(torch.int16).cpu().numpy().view(np.uint16).reshape(G["T"], G["S"], G["I"])
+    for d in G["h"]:
+        assert h[d["t"], d["s"], d["j"]] == int(d["bits"], 16), d
+    for d in G["y"]:
+        assert y[d["t"], d["n"]] == int(d["bits"], 16), d
+    assert np.count_nonzero(h & 0x7FFF) == len(G["h"]) and np.count_nonzero(y & 0x7FFF) == len(G["y"])
+
+
 def test_mxfp4_ignores_invalid_ids_and_adds_repeated_experts():
     note("mxfp4 invalid and repeated ids")
     T, S, E, H, I = 6, 5, 24, 512, 256
