@@ -287,7 +287,8 @@ def moe_sweeps(P, torch, np, synthgen, dev, reps, layers=MOE_LAYERS):
 
 def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
     """The other workloads of the method, timed the same way (per-M us/call, GB/s, % of peak):
-    the single 4096x2048 call at M=4; the M sweeps on 4608x4096 and 4096x2048 with outlier rows;
+    the single 4096x2048 call at M=4; the M sweeps on 4608x4096 and 4096x2048 with outlier rows
+    (the latter also over 64 weight copies, more than the MALL holds);
     M = 33..256 on 4096x2048 with the MFMA rate beside the bandwidth (fused, and quant then the
     tiled GEMM on pre-quantised input); the e8m0-scale path on
     4096x2048 and 2048x4096 beside the fp32-scale path on the same data; and the producer-side
@@ -306,6 +307,11 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
         t, _ = time_config(P, torch, np, synthgen, dev, N, K, list(M_SWEEP), copies, reps, outliers=True)
         res[f"sweep_{N}x{K}_outliers"] = {str(M): entry(N, K, M, t[M]) for M in M_SWEEP}
         log(f"[bench] {N}x{K} outliers: " + " ".join(f"M={M} {t[M]:.2f}us" for M in M_SWEEP))
+    # 24 copies of an 8 MiB weight (192 MiB) fit in the 256 MB MALL: the same sweep over 64 copies
+    # (512 MiB) shows whether the 24-copy figures were helped by it
+    t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, list(M_SWEEP), 64, reps, outliers=True)
+    res["sweep_4096x2048_outliers_64copies"] = {str(M): entry(4096, 2048, M, t[M]) for M in M_SWEEP}
+    log("[bench] 4096x2048 outliers, 64 copies: " + " ".join(f"M={M} {t[M]:.2f}us" for M in M_SWEEP))
     big = (33, 48, 64, 128, 256)
     t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, list(big), copies, reps)
     d = {}
