@@ -811,6 +811,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       for (int mt = 0; mt < MT; ++mt) acc[0][mt] += acc_odd[mt];
     }
   } else {
+    __builtin_amdgcn_s_setprio(3);
     for (int rd = 0; rd < rounds; ++rd) {
       const int kb0 = rd * KC;
       const int KCr = min(KC, KB - kb0);
