@@ -811,6 +811,8 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
       for (int mt = 0; mt < MT; ++mt) acc[0][mt] += acc_odd[mt];
     }
   } else {
+    // the quantisers' loads and VALU work issue ahead of the MFMA waves' on their SIMD: the MFMA
+    // waves only wait for their weights, while the staged activations gate every MFMA
     __builtin_amdgcn_s_setprio(3);
     for (int rd = 0; rd < rounds; ++rd) {
       const int kb0 = rd * KC;
