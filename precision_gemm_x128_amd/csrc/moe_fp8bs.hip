@@ -495,10 +495,13 @@ int moe_pack_fp4_common(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, 
   return launch_status();
 }
 
-// Workgroups per output tile in phase 2: about 64 pairs each (four per wave), at most 16.
+// Workgroups per output tile in phase 2: one up to 128 pairs, else max(2, ceil(pairs / 256)), at
+// most 16 (measured on the pages' shapes: two beat one from 176 pairs on, and two or three beat
+// the four or five of one per 128 pairs from 264 pairs on).
 inline int moe_splits(int T, int S) {
-  const int ns = (T * S + 63) / 64;
-  return ns < 1 ? 1 : (ns > 16 ? 16 : ns);
+  const int P = T * S;
+  const int ns = P <= 128 ? 1 : ((P + 255) / 256 > 2 ? (P + 255) / 256 : 2);
+  return ns > 16 ? 16 : ns;
 }
 
 inline size_t moe_h_bytes(int T, int S, int I) { return ((size_t)T * S * I * 2 + 255) & ~(size_t)255; }

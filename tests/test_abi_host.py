@@ -200,13 +200,13 @@ def test_moe_rejections_happen_before_any_launch():
     assert call(y=_fake(0x10001)) == 3 and call(ids=_fake(0x10002)) == 3 and call(tw=_fake(0x10002)) == 3
     assert call(lid=lid ^ 1) == 4
     # workspace: h rounded to 256 bytes, then NS fp32 partial planes when NS > 1
-    assert P.smallm_fp8bs_moe_splits(1, 11) == 1 and P.smallm_fp8bs_moe_splits(5, 11) == 1
-    assert P.smallm_fp8bs_moe_splits(6, 11) == 2 and P.smallm_fp8bs_moe_splits(20, 11) == 4
-    assert P.smallm_fp8bs_moe_splits(48, 16) == 12
+    assert P.smallm_fp8bs_moe_splits(1, 11) == 1 and P.smallm_fp8bs_moe_splits(11, 11) == 1
+    assert P.smallm_fp8bs_moe_splits(12, 11) == 2 and P.smallm_fp8bs_moe_splits(20, 11) == 2
+    assert P.smallm_fp8bs_moe_splits(48, 11) == 3 and P.smallm_fp8bs_moe_splits(48, 16) == 3
     assert P.smallm_fp8bs_moe_splits(0, 11) == 0 and P.smallm_fp8bs_moe_splits(4, 17) == 0
     assert P.smallm_fp8bs_moe_workspace_bytes(1, 11, 4096, 256) == 11 * 256 * 2          # 22 x 256 bytes
     assert P.smallm_fp8bs_moe_workspace_bytes(1, 3, 4096, 128) == 768
-    assert P.smallm_fp8bs_moe_workspace_bytes(20, 11, 4096, 256) == 220 * 256 * 2 + 4 * 20 * 4096 * 4
+    assert P.smallm_fp8bs_moe_workspace_bytes(20, 11, 4096, 256) == 220 * 256 * 2 + 2 * 20 * 4096 * 4
     assert P.smallm_fp8bs_moe_workspace_bytes(49, 11, 4096, 256) == 0
     assert P.smallm_fp8bs_moe_supported(48, 16, 4096, 16384, 2048) == 0
     assert P.smallm_fp8bs_moe_supported(1, 1, 1, 128, 128) == 0

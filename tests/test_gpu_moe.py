@@ -247,7 +247,7 @@ def test_moe_handworked_layer_on_gpu():
 
 def test_moe_deterministic_and_graph_replay_bitwise():
     note("moe graph replay")
-    T, S, E, H, I = 8, 11, 513, 4096, 256
+    T, S, E, H, I = 12, 11, 513, 4096, 256
     B = bank(E, H, I)
     ids, tw = synthgen.gen_moe_routing(T, S, E, seed=21)
     w13p, sw13, w2p, sw2 = B.packed(ids)

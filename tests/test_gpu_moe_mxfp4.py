@@ -303,13 +303,14 @@ def test_mxfp4_ignores_invalid_ids_and_adds_repeated_experts():
 
 def test_mxfp4_deterministic_and_graph_replay_bitwise():
     note("mxfp4 graph replay")
-    T, S, E, H, I = 8, 11, 513, 4096, 256
+    T, S, E, H, I = 12, 11, 513, 4096, 256
     B = bank(E, H, I)
     ids, tw = synthgen.gen_moe_routing(T, S, E, seed=21)
     w13p, s13p, w2p, s2p = B.packed(ids)
     x = to_dev_bf16(synthgen.gen_x(T, H, seed=21))
     idd = torch.from_numpy(ids).to(DEV)
     twd = torch.from_numpy(tw).to(DEV)
+    assert P.smallm_fp8bs_moe_splits(T, S) > 1          # the three-launch form is captured
     y1, h1 = P.smallm_fp8bs_moe_mxfp4(x, idd, twd, w13p, s13p, w2p, s2p)
     y2, h2 = P.smallm_fp8bs_moe_mxfp4(x, idd, twd, w13p, s13p, w2p, s2p)
     torch.cuda.synchronize()
