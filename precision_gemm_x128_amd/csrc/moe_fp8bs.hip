@@ -14,10 +14,11 @@
 // Design points of this implementation:
 //
 //  * No sort.  Each expert in use is streamed once per phase, with every token routed to it as
-//    a row of the MFMA A operand.  Phase 1 launches one workgroup per (token, slot) pair and
-//    8-column slice of the intermediate; a workgroup whose pair is not the first pair naming its
-//    expert exits after one pass over the ids in LDS, the others gather the expert's tokens with
-//    a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
+//    a row of the MFMA A operand.  Phase 1 works on (expert, 8-column slice) items.  Up to 256
+//    pairs it launches one workgroup per (token, slot) pair and slice, and a workgroup whose pair
+//    is not the first pair naming its expert exits.  Above, a fixed grid of 768 workgroups lists
+//    the distinct experts in LDS and walks the items.  Either way the expert's tokens are gathered
+//    with a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
 //    range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
 //    and its waves walk the experts whose first pair lies in its range, gathering each expert's
 //    tokens into MFMA rows as phase 1 does.  With NS > 1 the workgroups leave fp32 partial sums
@@ -56,6 +57,12 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // of its expert, and a larger workgroup makes that dearer)
 constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
+// Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs; above, a fixed grid of
+// kGateGrid workgroups walking the (expert, slice) items.  Measured on the pages' shapes: above 256
+// pairs the fixed grid of 768 took 90 us instead of 103 at 32 tokens (intermediate 128) and 150
+// instead of 158 at 40 (MXFP4); at 220 pairs it was up to 7 % slower; 1024 workgroups were slower.
+constexpr int kGateItemsFrom = 256;
+constexpr int kGateGrid = 768;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
 // workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
 constexpr int kDownThreads = 1024;
@@ -111,9 +118,9 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // phase 1: gate/up GEMM of one expert for all its tokens, silu(g) * u -> h (bf16)
 // ---------------------------------------------------------------------------------------------
 //
-// grid (T * S, I / 8), 512 threads.  Workgroup (p, q) works when pair p is the first pair naming
-// its expert e.  Its A rows are the tokens routed to e, ascending, in tiles of 16 (rows past the
-// last token are zero); its 16 columns are the gate rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.
+// Work item (e, q): expert e's 8-column slice q, 512 threads.  Its A rows are the tokens routed to
+// e, ascending, in tiles of 16 (rows past the last token are zero); its 16 columns are the gate
+// rows 8q..8q+7 and up rows I+8q..I+8q+7 of e.  Two grids hand out the items (below).
 
 // The split-K loop of phase 1 for one 16-row tile: wave w takes K blocks w, w + 8, ...  (one
 // block's loads in flight per wave: issuing several blocks' loads first raised the registers from
@@ -156,35 +163,17 @@ __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp,
   return acc;
 }
 
+// Phase 1 for one work item: expert e's 8-column slice q, for the Me tokens listed (ascending) in
+// s_tok.  All threads of the workgroup call it; it ends with a barrier, after which s_tok may be
+// rewritten.
 template <bool FP4>
-__global__ __launch_bounds__(kGateThreads) void moe_gate_up_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
-    int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
-    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
-  __shared__ int s_ids[kMoePairs];
-  __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];  // routed tokens, ascending; [MAX_T] = count
-  __shared__ float s_red[kGateWaves * 4 * 64];
+__device__ __forceinline__ void gate_up_item(
+    int e, int q, int Me, const int* s_ids, const int* s_tok, float* s_red,
+    const uint16_t* __restrict__ x, int64_t ldx, int S, const uint8_t* __restrict__ w13,
+    const float* __restrict__ sw13, const uint8_t* __restrict__ s13, int H, int I,
+    uint16_t* __restrict__ h) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int P = T * S;
-  const int p = blockIdx.x, q = blockIdx.y;
-  for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
-  __syncthreads();
-  const int e = s_ids[p];
-  if (e < 0 || e >= E) return;
-  bool earlier = false;
-  for (int i = tid; i < p; i += kGateThreads) earlier |= (s_ids[i] == e);
-  if (wave == 0) {
-    bool mine = false;
-    if (lane < T)
-      for (int s = 0; s < S; ++s) mine |= (s_ids[lane * S + s] == e);
-    const uint64_t m = __ballot(mine);
-    if (mine) s_tok[__popcll(m & ((1ull << lane) - 1ull))] = lane;
-    if (lane == 0) s_tok[SMALLM_FP8BS_MOE_MAX_T] = __popcll(m);
-  }
-  if (__syncthreads_or(earlier)) return;
-  const int Me = s_tok[SMALLM_FP8BS_MOE_MAX_T];
   const int tiles = (Me + 15) >> 4;
-
   const int KB = H >> 7;
   const int j = lane & 15, chunk = lane >> 4;
   // column j < 8 is gate row 8q + j (scale block row q / 16), j >= 8 the matching up row
@@ -229,6 +218,90 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate_up_kernel(
       }
     }
     __syncthreads();
+  }
+}
+
+// Wave 0 lists the tokens routed to expert e in s_tok (ascending), the count in s_tok[MAX_T].
+__device__ __forceinline__ void gather_tokens(int e, int T, int S, const int* s_ids, int* s_tok) {
+  const int lane = threadIdx.x & 63;
+  bool mine = false;
+  if (lane < T)
+    for (int s = 0; s < S; ++s) mine |= (s_ids[lane * S + s] == e);
+  const uint64_t m = __ballot(mine);
+  if (mine) s_tok[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+  if (lane == 0) s_tok[SMALLM_FP8BS_MOE_MAX_T] = __popcll(m);
+}
+
+// Up to 256 pairs: grid (T * S, I / 8).  Workgroup (p, q) works when pair p is the first pair
+// naming its expert e, on item (e, q); the others leave after one pass over the ids in LDS.
+template <bool FP4>
+__global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
+    int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
+    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
+  __shared__ int s_ids[kMoePairs];
+  __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];
+  __shared__ float s_red[kGateWaves * 4 * 64];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int P = T * S;
+  const int p = blockIdx.x, q = blockIdx.y;
+  for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
+  __syncthreads();
+  const int e = s_ids[p];
+  if (e < 0 || e >= E) return;
+  bool earlier = false;
+  for (int i = tid; i < p; i += kGateThreads) earlier |= (s_ids[i] == e);
+  if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
+  if (__syncthreads_or(earlier)) return;
+  gate_up_item<FP4>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S, w13, sw13,
+                    s13, H, I, h);
+}
+
+// Above 256 pairs: at most kGateGrid workgroups.  Every workgroup lists the distinct experts in
+// LDS, ordered by the first pair naming each, and takes the items (d-th distinct expert, slice q)
+// blockIdx.x, blockIdx.x + gridDim.x, ...; every wave runs the same bounded loop.
+template <bool FP4>
+__global__ __launch_bounds__(kGateThreads) void moe_gate_up_items_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
+    int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
+    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
+  __shared__ int s_ids[kMoePairs];
+  __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];   // first pair naming each expert
+  __shared__ int s_dexp[kMoePairs];                 // the distinct experts, by first pair
+  __shared__ int s_nd;
+  __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];
+  __shared__ float s_red[kGateWaves * 4 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = T * S;
+  for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
+  for (int i = tid; i < E; i += kGateThreads) s_first[i] = INT_MAX;
+  __syncthreads();
+  for (int i = tid; i < P; i += kGateThreads) {
+    const int e = s_ids[i];
+    if (e >= 0 && e < E) atomicMin(&s_first[e], i);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int nd = 0;
+    for (int c0 = 0; c0 < P; c0 += 64) {
+      const int pp = c0 + lane;
+      const int e = pp < P ? s_ids[pp] : -1;
+      const bool first = e >= 0 && e < E && s_first[e] == pp;
+      const uint64_t m = __ballot(first);
+      if (first) s_dexp[nd + __popcll(m & ((1ull << lane) - 1ull))] = e;
+      nd += __popcll(m);
+    }
+    if (lane == 0) s_nd = nd;
+  }
+  __syncthreads();
+  const int QN = I >> 3;
+  const int items = s_nd * QN;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int e = s_dexp[item / QN], q = item % QN;
+    if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
+    __syncthreads();
+    gate_up_item<FP4>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S, w13,
+                      sw13, s13, H, I, h);
   }
 }
 
@@ -519,8 +592,14 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
   uint16_t* h = (uint16_t*)ws;
   float* part = (float*)(ws + moe_h_bytes(T, S, I));
   const int ns = moe_splits(T, S);
-  hipLaunchKernelGGL((moe_gate_up_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st, x,
-                     ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
+  if (T * S <= kGateItemsFrom) {
+    hipLaunchKernelGGL((moe_gate_up_pairs_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st,
+                       x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
+  } else {
+    const int max_items = (T * S < E ? T * S : E) * (I / 8);
+    hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(max_items < kGateGrid ? max_items : kGateGrid),
+                       dim3(kGateThreads), 0, st, x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
+  }
   hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kDownThreads), 0, st, h, ids,
                      tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part);
   if (ns > 1) {

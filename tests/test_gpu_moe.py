@@ -207,9 +207,10 @@ def test_moe_small_shapes(T, S, E, H, I, shared, seed):
     check_against_oracle(x, ids, tw, B, f"T={T} S={S} E={E} H={H} I={I}")
 
 
-def test_moe_ignores_invalid_ids_and_adds_repeated_experts():
-    note("moe invalid and repeated ids")
-    T, S, E, H, I = 6, 5, 24, 512, 256
+@pytest.mark.parametrize("T,S", [(6, 5), (30, 11)])   # 30 pairs: pair grid; 330: item grid
+def test_moe_ignores_invalid_ids_and_adds_repeated_experts(T, S):
+    note(f"moe invalid and repeated ids T={T} S={S}")
+    E, H, I = 24, 512, 256
     B = bank(E, H, I)
     ids, tw = synthgen.gen_moe_routing(T, S, E, seed=11, shared=False)
     ids[0, 1] = -1

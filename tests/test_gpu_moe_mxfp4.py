@@ -282,9 +282,10 @@ def test_mxfp4_handworked_layer_on_gpu():
     assert np.count_nonzero(h & 0x7FFF) == len(G["h"]) and np.count_nonzero(y & 0x7FFF) == len(G["y"])
 
 
-def test_mxfp4_ignores_invalid_ids_and_adds_repeated_experts():
-    note("mxfp4 invalid and repeated ids")
-    T, S, E, H, I = 6, 5, 24, 512, 256
+@pytest.mark.parametrize("T,S", [(6, 5), (30, 11)])   # 30 pairs: pair grid; 330: item grid
+def test_mxfp4_ignores_invalid_ids_and_adds_repeated_experts(T, S):
+    note(f"mxfp4 invalid and repeated ids T={T} S={S}")
+    E, H, I = 24, 512, 256
     B = bank(E, H, I)
     ids, tw = synthgen.gen_moe_routing(T, S, E, seed=11, shared=False)
     ids[0, 1] = -1

@@ -44,8 +44,8 @@ def test_gemm_kernels_use_no_scratch(device_asm):
     assert len(kernels) >= 64
     others = re.findall(r"^(_Z\S*(?:tiled_gemm_kernel|rmsnorm_quant_kernel)\S*):", text, re.M)
     assert len(others) == 4
-    moe = re.findall(r"^(_Z\S*moe_(?:gate_up|down)_kernel\S*):", text, re.M)
-    assert len(moe) == 8
+    moe = re.findall(r"^(_Z\S*moe_(?:gate_up_pairs|gate_up_items|down)_kernel\S*):", text, re.M)
+    assert len(moe) == 10
     kernels += others + moe
     spills = []
     for k in kernels:
