@@ -195,6 +195,9 @@ SMALL_CASES = [
     (1, 1, 1, 256, 256, False, 5),        # one pair
     (48, 1, 1, 384, 128, False, 6),       # all 48 tokens on one expert
     (2, 16, 64, 256, 128, False, 7),      # 16 slots
+    (48, 16, 4096, 256, 128, False, 9),   # largest T, S and E: 768 pairs, item grid, full expert table
+    (3, 2, 3, 16384, 256, False, 10),     # largest hidden size: 128 K blocks in phase 1
+    (3, 2, 3, 1024, 2048, False, 12),     # largest intermediate: 16 K blocks in phase 2
     (40, 11, 64, 4096, 256, True, 8),     # 40 tokens over few experts: two and three row tiles
 ]
 

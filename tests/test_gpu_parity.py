@@ -306,9 +306,11 @@ def test_fused_full_shapes_all_m(N, K, e8m0):
 
 
 # Shapes that exercise every work split of the launch plan: column groups of C = 16, 8, 4, 2
-# columns; 1, 2, 3, 5, 9 and 12 column groups per workgroup; K shared by 4, 2 or 1 MFMA waves.
+# columns; 1, 2, 3, 5, 9 and 12 column groups per workgroup; K shared by 4, 2 or 1 MFMA waves;
+# and K of 16384 and 12416 (several K rounds, the last one ragged).
 PLAN_SHAPES = [(8192, 256), (12288, 256), (6144, 1024), (5120, 512), (4608, 1024), (2048, 512),
-               (36864, 128), (49152, 256)]
+               (36864, 128), (49152, 256),
+               (2048, 16384), (1024, 12416)]   # long K: four full rounds; 97 K blocks, a ragged last round
 
 
 @pytest.mark.parametrize("N,K", PLAN_SHAPES)
