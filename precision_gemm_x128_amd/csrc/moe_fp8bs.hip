@@ -173,6 +173,10 @@ __device__ __forceinline__ void gate_up_item(
     const float* __restrict__ sw13, const uint8_t* __restrict__ s13, int H, int I,
     uint16_t* __restrict__ h) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the expert, slice and token count are the same in every lane (read from LDS): scalar registers
+  e = __builtin_amdgcn_readfirstlane(e);
+  q = __builtin_amdgcn_readfirstlane(q);
+  Me = __builtin_amdgcn_readfirstlane(Me);
   const int tiles = (Me + 15) >> 4;
   const int KB = H >> 7;
   const int j = lane & 15, chunk = lane >> 4;

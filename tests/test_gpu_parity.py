@@ -154,7 +154,8 @@ def special_x(M, K, seed):
     return x
 
 
-QUANT_SHAPES = [(1, 2048), (3, 512), (4, 2048), (9, 4096), (16, 4096), (17, 2048), (32, 4096), (256, 2048)]
+QUANT_SHAPES = [(1, 2048), (3, 512), (4, 2048), (9, 4096), (16, 4096), (17, 2048), (32, 4096), (256, 2048),
+                (2, 16384), (33, 12416)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
