@@ -16,9 +16,9 @@
 //  * No sort.  Each expert in use is streamed once per phase, with every token routed to it as
 //    a row of the MFMA A operand.  Phase 1 works on (expert, 8-column slice) items.  Up to 256
 //    pairs it launches one workgroup per (token, slot) pair and slice, and a workgroup whose pair
-//    is not the first pair naming its expert exits.  Above, a fixed grid of 768 workgroups lists
-//    the distinct experts in LDS and walks the items.  Either way the expert's tokens are gathered
-//    with a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
+//    is not the first pair naming its expert exits.  Above, a fixed grid (768 workgroups, 1024
+//    for MXFP4) lists the distinct experts in LDS and walks the items.  Either way the expert's
+//    tokens are gathered with a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
 //    range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
 //    and its waves walk the experts whose first pair lies in its range, gathering each expert's
 //    tokens into MFMA rows as phase 1 does.  With NS > 1 the workgroups leave fp32 partial sums
@@ -60,9 +60,12 @@ constexpr int kGateWaves = kGateThreads / 64;
 // Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs; above, a fixed grid of
 // kGateGrid workgroups walking the (expert, slice) items.  Measured on the pages' shapes: above 256
 // pairs the fixed grid of 768 took 90 us instead of 103 at 32 tokens (intermediate 128) and 150
-// instead of 158 at 40 (MXFP4); at 220 pairs it was up to 7 % slower; 1024 workgroups were slower.
+// instead of 158 at 40 (MXFP4); at 220 pairs it was up to 7 % slower.  The FP8 kernel needs 70 VGPRs
+// (three workgroups per CU, and 1024 workgroups were slower); the MXFP4 one fits 64 without spills,
+// so four workgroups share a CU and its grid is 1024 (147 us instead of 150 at 40 tokens).
 constexpr int kGateItemsFrom = 256;
 constexpr int kGateGrid = 768;
+constexpr int kGateGridFp4 = 1024;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
 // workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
 constexpr int kDownThreads = 1024;
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
 // LDS, ordered by the first pair naming each, and takes the items (d-th distinct expert, slice q)
 // blockIdx.x, blockIdx.x + gridDim.x, ...; every wave runs the same bounded loop.
 template <bool FP4>
-__global__ __launch_bounds__(kGateThreads) void moe_gate_up_items_kernel(
+__global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(FP4 ? 8 : 1))) void moe_gate_up_items_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
     const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
@@ -601,7 +604,8 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   } else {
     const int max_items = (T * S < E ? T * S : E) * (I / 8);
-    hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(max_items < kGateGrid ? max_items : kGateGrid),
+    const int grid = FP4 ? kGateGridFp4 : kGateGrid;
+    hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(max_items < grid ? max_items : grid),
                        dim3(kGateThreads), 0, st, x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   }
   hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kDownThreads), 0, st, h, ids,
