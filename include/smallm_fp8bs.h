@@ -237,8 +237,7 @@ int smallm_fp8bs_moe_unpack(const uint8_t* w_packed, uint8_t* w8, int E, int R, 
  * overlap. */
 size_t smallm_fp8bs_moe_workspace_bytes(int T, int S, int H, int I);
 
-/* NS for (T, S): 1 when T * S <= 128, else max(2, ceil(T * S / 256)), at most 16; 0 when out of
- * range. */
+/* NS for (T, S): 1 when T * S <= 128, else 2; 0 when out of range. */
 int smallm_fp8bs_moe_splits(int T, int S);
 
 /* The layer: two launches on `stream`, three when NS > 1.  x: bf16 [T, ldx]; topk_ids: int32

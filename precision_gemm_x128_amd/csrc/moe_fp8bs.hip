@@ -575,14 +575,12 @@ int moe_pack_fp4_common(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, 
   return launch_status();
 }
 
-// Workgroups per output tile in phase 2: one up to 128 pairs, else max(2, ceil(pairs / 256)), at
-// most 16 (measured on the pages' shapes: two beat one from 176 pairs on, and two or three beat
-// the four or five of one per 128 pairs from 264 pairs on).
-inline int moe_splits(int T, int S) {
-  const int P = T * S;
-  const int ns = P <= 128 ? 1 : ((P + 255) / 256 > 2 ? (P + 255) / 256 : 2);
-  return ns > 16 ? 16 : ns;
-}
+// Workgroups per output tile in phase 2: one up to 128 pairs, else two.  At 64 VGPRs two
+// workgroups of 1024 threads share a CU, so on the pages' hidden size (256 column tiles) two splits
+// fill the chip in one round and a third adds a second, partly empty one.  Measured at 11 slots,
+// hidden 4096: two beat one from 176 pairs on; at 528 pairs (intermediate 128) two took 118 us per
+// layer, three 126, four 129 and six 131; at 440 pairs (MXFP4) two took 147 us, three or more 156.
+inline int moe_splits(int T, int S) { return T * S <= 128 ? 1 : 2; }
 
 inline size_t moe_h_bytes(int T, int S, int I) { return ((size_t)T * S * I * 2 + 255) & ~(size_t)255; }
 

@@ -202,7 +202,7 @@ def test_moe_rejections_happen_before_any_launch():
     # workspace: h rounded to 256 bytes, then NS fp32 partial planes when NS > 1
     assert P.smallm_fp8bs_moe_splits(1, 11) == 1 and P.smallm_fp8bs_moe_splits(11, 11) == 1
     assert P.smallm_fp8bs_moe_splits(12, 11) == 2 and P.smallm_fp8bs_moe_splits(20, 11) == 2
-    assert P.smallm_fp8bs_moe_splits(48, 11) == 3 and P.smallm_fp8bs_moe_splits(48, 16) == 3
+    assert P.smallm_fp8bs_moe_splits(48, 11) == 2 and P.smallm_fp8bs_moe_splits(48, 16) == 2
     assert P.smallm_fp8bs_moe_splits(0, 11) == 0 and P.smallm_fp8bs_moe_splits(4, 17) == 0
     assert P.smallm_fp8bs_moe_workspace_bytes(1, 11, 4096, 256) == 11 * 256 * 2          # 22 x 256 bytes
     assert P.smallm_fp8bs_moe_workspace_bytes(1, 3, 4096, 128) == 768
