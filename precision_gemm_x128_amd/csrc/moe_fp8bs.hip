@@ -16,8 +16,8 @@
 //  * No sort.  Each expert in use is streamed once per phase, with every token routed to it as
 //    a row of the MFMA A operand.  Phase 1 works on (expert, 8-column slice) items.  Up to 256
 //    pairs it launches one workgroup per (token, slot) pair and slice, and a workgroup whose pair
-//    is not the first pair naming its expert exits.  Above, a fixed grid (768 workgroups, 1024
-//    for MXFP4) lists the distinct experts in LDS and walks the items.  Either way the expert's
+//    is not the first pair naming its expert exits.  Above, a fixed grid of 1024 workgroups
+//    lists the distinct experts in LDS and walks the items.  Either way the expert's
 //    tokens are gathered with a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
 //    range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
 //    and its waves walk the experts whose first pair lies in its range, gathering each expert's
@@ -59,13 +59,13 @@ constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
 // Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs; above, a fixed grid of
 // kGateGrid workgroups walking the (expert, slice) items.  Measured on the pages' shapes: above 256
-// pairs the fixed grid of 768 took 90 us instead of 103 at 32 tokens (intermediate 128) and 150
-// instead of 158 at 40 (MXFP4); at 220 pairs it was up to 7 % slower.  The FP8 kernel needs 70 VGPRs
-// (three workgroups per CU, and 1024 workgroups were slower); the MXFP4 one fits 64 without spills,
-// so four workgroups share a CU and its grid is 1024 (147 us instead of 150 at 40 tokens).
+// pairs the fixed grid took 90 us instead of 103 at 32 tokens (intermediate 128) and 150 instead
+// of 158 at 40 (MXFP4); at 220 pairs it was up to 7 % slower.  The item kernels fit 64 VGPRs
+// without spills (a scalar wave index; unmasked activation loads for FP8), so four workgroups
+// share a CU and 1024 fill the chip in one round: 114 us instead of 118 at 48 tokens and 87
+// instead of 90 at 32 (FP8, intermediate 128) against 768 workgroups at 70 VGPRs.
 constexpr int kGateItemsFrom = 256;
-constexpr int kGateGrid = 768;
-constexpr int kGateGridFp4 = 1024;
+constexpr int kGateGrid = 1024;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
 // workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
 constexpr int kDownThreads = 1024;
@@ -132,7 +132,10 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // multiplies into acc.  MXFP4 weights (FP4 true): the 32-wide group scales are applied by the
 // conversion to bf16, so the partial is added to acc as it is.  Every partial is added in the same
 // block of code as its MFMAs (no MFMA result crosses a branch).
-template <bool FP4>
+// DENSE: every lane loads its activation row (rows past the token count read a valid row and are
+// zeroed after the load), which saves the exec-mask branches and the registers they hold; masked
+// loads (DENSE false) keep the empty rows off the load pipeline that the weight stream shares.
+template <bool FP4, bool DENSE>
 __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp, const uint8_t* sbp,
                                             const uint16_t* xr, bool row_ok, int KB, int wave) {
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -147,7 +150,14 @@ __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp,
     const u32x4* xa = (const u32x4*)(xr + kb * 128);
     u32x4 a[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = row_ok ? xa[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DENSE) {
+        const u32x4 v = xa[i];
+        a[i] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        a[i] = row_ok ? xa[i] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
     v8bf bv[4];
     float sc;
     if constexpr (FP4) {
@@ -169,13 +179,16 @@ __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp,
 // Phase 1 for one work item: expert e's 8-column slice q, for the Me tokens listed (ascending) in
 // s_tok.  All threads of the workgroup call it; it ends with a barrier, after which s_tok may be
 // rewritten.
-template <bool FP4>
+template <bool FP4, bool DENSE>
 __device__ __forceinline__ void gate_up_item(
     int e, int q, int Me, const int* s_ids, const int* s_tok, float* s_red,
     const uint16_t* __restrict__ x, int64_t ldx, int S, const uint8_t* __restrict__ w13,
     const float* __restrict__ sw13, const uint8_t* __restrict__ s13, int H, int I,
     uint16_t* __restrict__ h) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: loop counters, scale loads and addresses derived from it
+  // stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the expert, slice and token count are the same in every lane (read from LDS): scalar registers
   e = __builtin_amdgcn_readfirstlane(e);
   q = __builtin_amdgcn_readfirstlane(q);
@@ -202,7 +215,7 @@ __device__ __forceinline__ void gate_up_item(
     const int idx = 16 * tile + j;
     const bool row_ok = idx < Me;
     const uint16_t* xr = x + (int64_t)(row_ok ? s_tok[idx] : 0) * ldx + chunk * 32;
-    const v4f acc = gate_up_loop<FP4>(wp, swp, sbp, xr, row_ok, KB, wave);
+    const v4f acc = gate_up_loop<FP4, DENSE>(wp, swp, sbp, xr, row_ok, KB, wave);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_red[(wave * 4 + i) * 64 + lane] = acc[i];
     __syncthreads();
@@ -260,15 +273,17 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
   for (int i = tid; i < p; i += kGateThreads) earlier |= (s_ids[i] == e);
   if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
   if (__syncthreads_or(earlier)) return;
-  gate_up_item<FP4>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S, w13, sw13,
-                    s13, H, I, h);
+  gate_up_item<FP4, false>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
+                           w13, sw13, s13, H, I, h);
 }
 
 // Above 256 pairs: at most kGateGrid workgroups.  Every workgroup lists the distinct experts in
 // LDS, ordered by the first pair naming each, and takes the items (d-th distinct expert, slice q)
 // blockIdx.x, blockIdx.x + gridDim.x, ...; every wave runs the same bounded loop.
+// At most 64 VGPRs (eight waves per SIMD): four workgroups per CU.
 template <bool FP4>
-__global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(FP4 ? 8 : 1))) void moe_gate_up_items_kernel(
+__global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void moe_gate_up_items_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
     const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
@@ -278,7 +293,10 @@ __global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(FP
   __shared__ int s_nd;
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];
   __shared__ float s_red[kGateWaves * 4 * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: loop counters, scale loads and addresses derived from it
+  // stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = T * S;
   for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
   for (int i = tid; i < E; i += kGateThreads) s_first[i] = INT_MAX;
@@ -307,8 +325,10 @@ __global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(FP
     const int e = s_dexp[item / QN], q = item % QN;
     if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
     __syncthreads();
-    gate_up_item<FP4>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S, w13,
-                      sw13, s13, H, I, h);
+    // unmasked activation loads bring the FP8 kernel to 64 VGPRs; the MXFP4 one fits with masked
+    // loads, which measured faster for it
+    gate_up_item<FP4, !FP4>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
+                            w13, sw13, s13, H, I, h);
   }
 }
 
@@ -342,7 +362,10 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
   __shared__ int s_tok[kDownWaves][ROWS];    // token of gathered row k (this wave's current expert)
   __shared__ int s_hrow[kDownWaves][ROWS];   // its h row t * S + first slot naming the expert
   __shared__ float s_wt[kDownWaves][ROWS];   // its summed top-k weight
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: loop counters, scale loads and addresses derived from it
+  // stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = T * S;
   const int NS = gridDim.y, z = blockIdx.y;
   const int lo = (int)((int64_t)z * P / NS), hi = (int)((int64_t)(z + 1) * P / NS);
@@ -602,8 +625,8 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   } else {
     const int max_items = (T * S < E ? T * S : E) * (I / 8);
-    const int grid = FP4 ? kGateGridFp4 : kGateGrid;
-    hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(max_items < grid ? max_items : grid),
+    const int grid = max_items < kGateGrid ? max_items : kGateGrid;
+    hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(grid),
                        dim3(kGateThreads), 0, st, x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   }
   hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kDownThreads), 0, st, h, ids,
