@@ -389,6 +389,19 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
   for (int p = lo + wave; p < hi; p += kDownWaves) {
     const int e = s_ids[p];
     if (e < 0 || e >= E || s_first[e] != p) continue;
+    const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
+    const uint8_t* sbp =
+        FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
+    const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
+    // FP8: the first K block's weights and scale depend only on the expert, so they are loaded
+    // before the gather and are in flight during it (MXFP4 has no registers to spare for this)
+    u32x4 pre0 = u32x4{0u, 0u, 0u, 0u}, pre1 = u32x4{0u, 0u, 0u, 0u};
+    float pre_s = 0.0f;
+    if constexpr (!FP4) {
+      pre0 = load_nt(wp);
+      pre1 = load_nt(wp + 1024);
+      pre_s = swp[0];
+    }
     // gather: lane t (< T) is routed to e when some slot of token t names it
     int slot = -1;
     float wsum = 0.0f;
@@ -406,10 +419,6 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
       s_wt[wave][k] = wsum;
     }
     const int Me = __popcll(m);
-    const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
-    const uint8_t* sbp =
-        FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
-    const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
     for (int tile = 0; tile * 16 < Me; ++tile) {
       const int k = 16 * tile + j;
       const bool ok = k < Me;
@@ -423,9 +432,10 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
           fp4x32_to_bf16(load_nt(wp + (int64_t)kb * 1024), e8m0_f32(sbp[(int64_t)kb * 64]), bv);
           sc = 1.0f;
         } else {
-          const u32x4 b0 = load_nt(wp + (int64_t)kb * 2048);
-          const u32x4 b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
-          sc = swp[kb];
+          const bool first = tile == 0 && kb == 0;
+          const u32x4 b0 = first ? pre0 : load_nt(wp + (int64_t)kb * 2048);
+          const u32x4 b1 = first ? pre1 : load_nt(wp + (int64_t)kb * 2048 + 1024);
+          sc = first ? pre_s : swp[kb];
           e4m3x32_to_bf16(b0, b1, bv);
         }
         const u32x4* ha = (const u32x4*)(hr + kb * 128);
