@@ -393,14 +393,17 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
     const uint8_t* sbp =
         FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
     const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
-    // FP8: the first K block's weights and scale depend only on the expert, so they are loaded
-    // before the gather and are in flight during it (MXFP4 has no registers to spare for this)
+    // the first K block's weights and scale depend only on the expert, so they are loaded before
+    // the gather and are in flight during it
     u32x4 pre0 = u32x4{0u, 0u, 0u, 0u}, pre1 = u32x4{0u, 0u, 0u, 0u};
     float pre_s = 0.0f;
     if constexpr (!FP4) {
       pre0 = load_nt(wp);
       pre1 = load_nt(wp + 1024);
       pre_s = swp[0];
+    } else {
+      pre0 = load_nt(wp);
+      pre_s = e8m0_f32(sbp[0]);
     }
     // gather: lane t (< T) is routed to e when some slot of token t names it
     int slot = -1;
@@ -429,7 +432,9 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
         float sc;
         if constexpr (FP4) {
           // the group scale is applied by the conversion; the partial needs no block scale
-          fp4x32_to_bf16(load_nt(wp + (int64_t)kb * 1024), e8m0_f32(sbp[(int64_t)kb * 64]), bv);
+          const bool first = tile == 0 && kb == 0;
+          fp4x32_to_bf16(first ? pre0 : load_nt(wp + (int64_t)kb * 1024),
+                         first ? pre_s : e8m0_f32(sbp[(int64_t)kb * 64]), bv);
           sc = 1.0f;
         } else {
           const bool first = tile == 0 && kb == 0;
