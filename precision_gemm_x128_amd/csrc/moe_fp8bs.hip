@@ -14,12 +14,12 @@
 // Design points of this implementation:
 //
 //  * No sort.  Each expert in use is streamed once per phase, with every token routed to it as
-//    a row of the MFMA A operand.  Phase 1 works on (expert, 8-column slice) items.  Up to 256
-//    pairs it launches one workgroup per (token, slot) pair and slice, and a workgroup whose pair
-//    is not the first pair naming its expert exits.  Above, a fixed grid of 1024 workgroups
-//    lists the distinct experts in LDS and walks the items.  Either way the expert's
-//    tokens are gathered with a ballot.  Phase 2 launches NS workgroups per 16 output columns, each over a contiguous
-//    range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
+//    a row of the MFMA A operand.  Phase 1 works on (expert, 8-column slice) items.  Up to 128
+//    pairs (32 for MXFP4) it launches one workgroup per (token, slot) pair and slice, and a
+//    workgroup whose pair is not the first pair naming its expert exits.  Above, a fixed grid of
+//    1024 workgroups lists the distinct experts in LDS and walks the items.  Either way the
+//    expert's tokens are gathered with a ballot.  Phase 2 launches NS workgroups per 16 output
+//    columns, each over a contiguous range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
 //    and its waves walk the experts whose first pair lies in its range, gathering each expert's
 //    tokens into MFMA rows as phase 1 does.  With NS > 1 the workgroups leave fp32 partial sums
 //    in the caller's workspace and a third launch adds them in range order.
@@ -57,14 +57,18 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // of its expert, and a larger workgroup makes that dearer)
 constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
-// Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs; above, a fixed grid of
-// kGateGrid workgroups walking the (expert, slice) items.  Measured on the pages' shapes: above 256
-// pairs the fixed grid took 90 us instead of 103 at 32 tokens (intermediate 128) and 150 instead
-// of 158 at 40 (MXFP4); at 220 pairs it was up to 7 % slower.  The item kernels fit 64 VGPRs
-// without spills (a scalar wave index; unmasked activation loads for FP8), so four workgroups
-// share a CU and 1024 fill the chip in one round: 114 us instead of 118 at 48 tokens and 87
-// instead of 90 at 32 (FP8, intermediate 128) against 768 workgroups at 70 VGPRs.
-constexpr int kGateItemsFrom = 256;
+// Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs (kGateItemsFromFp4 for
+// MXFP4); above, a fixed grid of kGateGrid workgroups walking the (expert, slice) items.  The item
+// kernels fit 64 VGPRs without spills (a scalar wave index; unmasked activation loads for FP8), so
+// four workgroups share a CU and 1024 fill the chip in one round: 114 us instead of 118 at 48
+// tokens and 87 instead of 90 at 32 (FP8, intermediate 128) against 768 workgroups at 70 VGPRs.
+// Against the per-pair grid, on the pages' shapes (11 slots): the item grid took 87 us instead of
+// 102 at 32 tokens and 114 instead of 129 at 48 (FP8, intermediate 128), 145 instead of 156 at 40
+// (MXFP4); at 16 tokens it was 3-4 % faster for both formats, and for MXFP4 it was 3 % faster from
+// four tokens on.  For FP8 at 8 tokens and intermediate 256 it was 1.6 % slower, hence the two
+// thresholds.
+constexpr int kGateItemsFrom = 128;
+constexpr int kGateItemsFromFp4 = 32;
 constexpr int kGateGrid = 1024;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
 // workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
@@ -252,8 +256,9 @@ __device__ __forceinline__ void gather_tokens(int e, int T, int S, const int* s_
   if (lane == 0) s_tok[SMALLM_FP8BS_MOE_MAX_T] = __popcll(m);
 }
 
-// Up to 256 pairs: grid (T * S, I / 8).  Workgroup (p, q) works when pair p is the first pair
-// naming its expert e, on item (e, q); the others leave after one pass over the ids in LDS.
+// Up to 128 pairs (32 for MXFP4): grid (T * S, I / 8).  Workgroup (p, q) works when pair p is
+// the first pair naming its expert e, on item (e, q); the others leave after one pass over the
+// ids in LDS.
 template <bool FP4>
 __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
                            w13, sw13, s13, H, I, h);
 }
 
-// Above 256 pairs: at most kGateGrid workgroups.  Every workgroup lists the distinct experts in
+// Above that: at most kGateGrid workgroups.  Every workgroup lists the distinct experts in
 // LDS, ordered by the first pair naming each, and takes the items (d-th distinct expert, slice q)
 // blockIdx.x, blockIdx.x + gridDim.x, ...; every wave runs the same bounded loop.
 // At most 64 VGPRs (eight waves per SIMD): four workgroups per CU.
@@ -635,7 +640,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
   uint16_t* h = (uint16_t*)ws;
   float* part = (float*)(ws + moe_h_bytes(T, S, I));
   const int ns = moe_splits(T, S);
-  if (T * S <= kGateItemsFrom) {
+  if (T * S <= (FP4 ? kGateItemsFromFp4 : kGateItemsFrom)) {
     hipLaunchKernelGGL((moe_gate_up_pairs_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st,
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   } else {
