@@ -16,8 +16,8 @@
 //  * No sort.  Each expert in use is streamed once per phase, with every token routed to it as
 //    a row of the MFMA A operand.  Phase 1 works on (expert, 8-column slice) items.  Up to 128
 //    pairs (32 for MXFP4) it launches one workgroup per (token, slot) pair and slice, and a
-//    workgroup whose pair is not the first pair naming its expert exits.  Above, a fixed grid of
-//    1024 workgroups lists the distinct experts in LDS and walks the items.  Either way the
+//    workgroup whose pair is not the first pair naming its expert exits.  Above, a fixed grid
+//    (2048 workgroups, 3072 for MXFP4) lists the distinct experts in LDS and walks the items.  Either way the
 //    expert's tokens are gathered with a ballot.  Phase 2 launches NS workgroups per 16 output
 //    columns, each over a contiguous range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
 //    and its waves walk the experts whose first pair lies in its range, gathering each expert's
@@ -58,10 +58,16 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
 // Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs (kGateItemsFromFp4 for
-// MXFP4); above, a fixed grid of kGateGrid workgroups walking the (expert, slice) items.  The item
-// kernels fit 64 VGPRs without spills (a scalar wave index; unmasked activation loads for FP8), so
-// four workgroups share a CU and 1024 fill the chip in one round: 114 us instead of 118 at 48
-// tokens and 87 instead of 90 at 32 (FP8, intermediate 128) against 768 workgroups at 70 VGPRs.
+// MXFP4); above, a fixed grid of kGateGrid (kGateGridFp4) workgroups walking the (expert, slice)
+// items.  The item kernels fit 64 VGPRs without spills (a scalar wave index; unmasked activation
+// loads for FP8), so four workgroups share a CU: 1024 are resident at once.  A grid of exactly
+// 1024 assigns every workgroup ceil or floor of items / 1024 items, and a last round that only a
+// few workgroups have costs a whole round (3088 items at 24 tokens, intermediate 128: four rounds
+// for an average of three).  With two or three workgroups per slot the later ones start as slots
+// free up, and the tail shrinks.  Measured (11 slots, hidden 4096): FP8 at intermediate 128, 1024
+// / 2048 / 3072 workgroups took 73.7 / 70.5 / 72.4 us at 24 tokens, 87.4 / 83.4 / 84.3 at 32 and
+// 113.8 / 109.8 / 109.4 at 48; MXFP4 took 74.6 / 72.8 / 70.8 us at 16 tokens and 145.7 / 141.8 /
+// 136.5 at 40; one workgroup per possible item was no better and less steady.
 // Against the per-pair grid, on the pages' shapes (11 slots): the item grid took 87 us instead of
 // 102 at 32 tokens and 114 instead of 129 at 48 (FP8, intermediate 128), 145 instead of 156 at 40
 // (MXFP4); at 16 tokens it was 3-4 % faster for both formats, and for MXFP4 it was 3 % faster from
@@ -69,7 +75,8 @@ constexpr int kGateWaves = kGateThreads / 64;
 // thresholds.
 constexpr int kGateItemsFrom = 128;
 constexpr int kGateItemsFromFp4 = 32;
-constexpr int kGateGrid = 1024;
+constexpr int kGateGrid = 2048;
+constexpr int kGateGridFp4 = 3072;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
 // workgroups share a CU (66 VGPRs halved the occupancy and measured up to 25 % slower)
 constexpr int kDownThreads = 1024;
@@ -645,7 +652,8 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   } else {
     const int max_items = (T * S < E ? T * S : E) * (I / 8);
-    const int grid = max_items < kGateGrid ? max_items : kGateGrid;
+    const int most = FP4 ? kGateGridFp4 : kGateGrid;
+    const int grid = max_items < most ? max_items : most;
     hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(grid),
                        dim3(kGateThreads), 0, st, x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
   }
