@@ -199,6 +199,8 @@ SMALL_CASES = [
     (3, 2, 3, 16384, 256, False, 10),     # largest hidden size: 128 K blocks in phase 1
     (3, 2, 3, 1024, 2048, False, 12),     # largest intermediate: 16 K blocks in phase 2
     (40, 11, 64, 4096, 256, True, 8),     # 40 tokens over few experts: two and three row tiles
+    (2, 16, 100, 512, 256, False, 13),    # 32 pairs: the largest per-pair grid in phase 1
+    (11, 3, 100, 512, 256, False, 14),    # 33 pairs: the smallest item grid in phase 1
 ]
 
 
