@@ -354,6 +354,8 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times): the "
                          "reference kernel for scaling HBM byte counters, then exit")
+    ap.add_argument("--moe-only", action="store_true",
+                    help="only time the MoE layers (as in the other workloads) and print them as JSON")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -381,6 +383,9 @@ def main():
         return
     N, K, copies = args.N, args.K, args.copies
     P.lib()
+    if args.moe_only:
+        print(json.dumps({"moe": moe_sweeps(P, torch, np, synthgen, dev, max(1, args.reps))}))
+        return
 
     # ---- inputs: 24 cold weight copies, quantised and packed on the device (load-time work) ----
     t0 = time.time()
