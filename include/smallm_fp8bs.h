@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMALLM_FP8BS_ABI_VERSION 4
+#define SMALLM_FP8BS_ABI_VERSION 5
 #define SMALLM_FP8BS_MAX_M 256
 #define SMALLM_FP8BS_RMS_MAX_M (1 << 20) /* rows of one producer call */
 #define SMALLM_FP8BS_RMS_MAX_H 16384     /* values per row of one producer call */
@@ -69,11 +69,13 @@ typedef enum {
 int smallm_fp8bs_abi_version(void);
 
 /* Identifier of the packed layout smallm_fp8bs_pack_weight produces for an [N, K] weight (0 for
- * an invalid shape).  The layout groups C consecutive weight columns (C = 16, 8, 4 or 2, chosen
- * from N and K so that the column groups split evenly over the GPU's 256 compute units), and the
- * id encodes C.  The GEMM entry points take the id back and refuse weights packed for another
- * layout (the pages' guard only takes the fused path for a weight marked as preshuffled, section
- * Modifications). */
+ * an invalid shape).  The layout deals the columns to workgroups: each gets NA (0 or 1) group of
+ * 16 columns, stored as one 2 KiB fragment per 128-wide K block, and a remainder group of CB
+ * (0, 2, 4 or 8) columns whose fragments hold SB consecutive K blocks, chosen from N and K so
+ * that the GPU's 256 compute units each stream the same number of weight bytes.  The id is
+ * 0x46390000 | NA << 12 | CB << 4 | SB.  The GEMM entry points take the id back and refuse
+ * weights packed for another layout (the pages' guard only takes the fused path for a weight
+ * marked as preshuffled, section Modifications). */
 uint32_t smallm_fp8bs_weight_layout_id(int N, int K);
 
 /* Static description of a status code.  Never NULL. */
@@ -84,13 +86,12 @@ const char* smallm_fp8bs_strerror(int status);
 int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx);
 
 /* Host-only description of the launch the GEMM entry points make for (M, N, K), for tools and
- * benchmarks.  plan10 receives, in order: C (columns per group), CGW (column groups per
- * workgroup), the number of workgroups along N, NWK and NWC (the MFMA waves form an NWK x NWC
- * grid: NWK waves split each round's K groups, NWC waves split the column groups), NCG (column
- * groups per MFMA wave, which share one read of each activation tile), NKG (K groups per MFMA
- * wave per round), KC (K blocks per round), QW (quantising waves) and MT (16-row M tiles per
- * workgroup).  Returns SMALLM_OK or the shape error. */
-int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan10);
+ * benchmarks.  plan8 receives, in order: the number of workgroups along N, NA, CB and SB (the
+ * packed layout, as in smallm_fp8bs_weight_layout_id), R (K blocks per wave), RC (K blocks per
+ * round of a wave), the waves per workgroup and MT (16-row M tiles per workgroup; M above 32
+ * runs in 32-row chunks along the grid's second dimension).  Returns SMALLM_OK or the shape
+ * error. */
+int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan8);
 
 /* --------------------------------------------------------------------------------------------
  * Load-time weight preparation (not on the per-token path)

@@ -149,9 +149,13 @@ def smallm_fp8bs_weight_layout_id(N: int, K: int) -> int:
     return int(lib().smallm_fp8bs_weight_layout_id(N, K))
 
 
-def layout_columns(N: int, K: int) -> int:
-    """Weight columns per group (C) of the packed layout for an [N, K] weight."""
-    return smallm_fp8bs_weight_layout_id(N, K) & 0xFF
+def weight_layout(N: int, K: int) -> dict:
+    """The packed layout for an [N, K] weight: NA 16-column groups and a CB-column remainder group
+    per workgroup, SB K blocks per remainder fragment (decoded from the layout id)."""
+    lid = smallm_fp8bs_weight_layout_id(N, K)
+    if lid == 0:
+        raise ValueError(f"no packed layout for N={N} K={K}")
+    return {"NA": (lid >> 12) & 0xF, "CB": (lid >> 4) & 0xFF, "SB": lid & 0xF}
 
 
 def strerror(status: int) -> str:
@@ -165,7 +169,7 @@ def smallm_fp8bs_supported(M: int, N: int, K: int, ldx: int) -> int:
     return int(lib().smallm_fp8bs_supported(M, N, K, ldx))
 
 
-PLAN_FIELDS = ("C", "CGW", "nwg", "NWK", "NWC", "NCG", "NKG", "KC", "QW", "MT")
+PLAN_FIELDS = ("nwg", "NA", "CB", "SB", "R", "RC", "NW", "MT")
 
 
 def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
@@ -175,16 +179,12 @@ def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
     return dict(zip(PLAN_FIELDS, list(buf)))
 
 
-TILED_FROM_M = 32   # the pre-quantised GEMM is MFMA-tiled above this M with 16-column layouts
-TILED_ROWS = 32
-
-
 def kernel_name(M: int, N: int, K: int, mode: int = 0) -> str:
-    """Name of the GEMM kernel instantiation (mode 0 fused fp32, 1 fused e8m0, 2/3 pre-quantised)."""
-    if mode >= 2 and M > TILED_FROM_M and layout_columns(N, K) == 16 and K // 128 <= 128:
-        return f"tiled_gemm_kernel<{TILED_ROWS}, {'true' if mode == 3 else 'false'}>"
+    """Name of the GEMM kernel instantiation (mode 0 fused fp32, 1 fused e8m0, 2/3 pre-quantised),
+    as the profiler prints it."""
     p = smallm_fp8bs_launch_plan(M, N, K)
-    return f"smallm_gemm_kernel<{p['MT']}, {p['C']}, {p['NCG']}, {p['NKG']}, {mode}>"
+    hasb = "true" if p["CB"] else "false"
+    return f"smallm_gemm_kernel<{p['MT']}, {mode}, {p['NA']}, {hasb}, {p['SB']}, {p['RC']}>"
 
 
 # ---------------------------------------------------------------------------------------------

@@ -38,6 +38,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "../../include/smallm_fp8bs.h"
 
 namespace {
@@ -257,25 +259,49 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
 // weight (un)packing: one thread per 16-byte chunk of the packed layout
 // ---------------------------------------------------------------------------------------------
 //
-// Packed layout with C weight columns per group (C in {16, 8, 4, 2}, S = 16 / C K-blocks per
-// fragment): fragment f = cg * KG + h (KG = K / (128 S)) holds columns [cg C, cg C + C) and K-blocks
-// [h S, h S + S).  Its 16 MFMA B columns are j = c S + s (column c of the group, K-block s of the
-// fragment).  Lane l = 16 chunk + j of the fragment holds K bytes [32 chunk, 32 chunk + 32) of that
-// column and K-block: bytes 0..15 at l * 16, bytes 16..31 at 1024 + l * 16.
+// Packed layout.  The N columns are dealt to NWG workgroups; workgroup w owns
+//   * NA (0 or 1) group of 16 columns, [16 w, 16 w + 16), stored as K / 128 fragments of 2 KiB in
+//     K order (one fragment per 128-wide K block: the B operand of one 16x16x128 MFMA), and
+//   * a remainder group of CB columns (0, 2, 4 or 8), [16 NA NWG + CB w, + CB), stored as
+//     K / (128 SB) fragments of CB * SB * 128 bytes, each holding SB consecutive K blocks of the
+//     CB columns side by side (B column j = c SB + s is column c in K block s of the fragment).
+// Workgroup w's bytes are contiguous, at w * (16 NA + CB) * K: the 16-column fragments first.  In a
+// fragment with NB B columns (16, or CB * SB), lane l = 16 chunk + j (j < NB) holds K bytes
+// [32 chunk, 32 chunk + 32) of B column j: bytes 0..15 at (chunk NB + j) * 16 and bytes 16..31
+// at NB * 64 + (chunk NB + j) * 16, so a wave fetches a fragment with two loads that each cover
+// NB * 64 contiguous bytes.  The remainder group lets every workgroup stream the same number of
+// bytes (one workgroup per CU) while keeping most fragments free of the padding that chaining
+// several K blocks in one MFMA would cost.
 
-template <bool PACK, int C>
+struct PackGeom {
+  int na, cb, sb, nwg;
+};
+
+template <bool PACK>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                                   int K, int64_t chunks) {
-  constexpr int S = 16 / C;
+                                                   int K, PackGeom g, int64_t chunks) {
   const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (o >= chunks) return;
-  const int KG = (K >> 7) / S;
-  const int64_t f = o >> 7;
-  const int within = (int)(o & 127), half = within >> 6, lane = within & 63;
-  const int chunk = lane >> 4, j = lane & 15;
-  const int64_t cg = f / KG, h = f % KG;
-  const int64_t n = cg * C + j / S;
-  const int64_t k = (h * S + j % S) * 128 + chunk * 32 + half * 16;
+  const int KB = K >> 7;
+  const int64_t region = (int64_t)(16 * g.na + g.cb) * K;  // bytes per workgroup
+  const int64_t w = (o * 16) / region;
+  const int64_t off = o * 16 - w * region;
+  const int64_t abytes = (int64_t)g.na * KB * 2048;
+  int64_t n, k;
+  if (off < abytes) {
+    const int64_t kb = off >> 11;
+    const int within = (int)(off & 2047), half = within >> 10, lane = (within & 1023) >> 4;
+    n = 16 * w + (lane & 15);
+    k = kb * 128 + (lane >> 4) * 32 + half * 16;
+  } else {
+    const int nb = g.cb * g.sb, fb = nb * 128;
+    const int64_t ob = off - abytes;
+    const int64_t f = ob / fb;
+    const int within = (int)(ob - f * fb), half = within / (fb >> 1), idx = (within % (fb >> 1)) >> 4;
+    const int chunk = idx / nb, j = idx % nb;
+    n = (int64_t)16 * g.na * g.nwg + (int64_t)g.cb * w + j / g.sb;
+    k = (f * g.sb + j % g.sb) * 128 + chunk * 32 + half * 16;
+  }
   if (PACK)
     *(u32x4*)(dst + o * 16) = *(const u32x4*)(src + n * K + k);
   else
@@ -494,471 +520,362 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
 
 enum Mode { kFusedF32 = 0, kFusedE8 = 1, kPreqF32 = 2, kPreqE8 = 3 };
 
-constexpr int kKCMax = 32;      // K blocks staged per round
-constexpr int kMaxMfmaWaves = 12;  // MFMA waves per workgroup (the quantising waves come first)
+constexpr int kMaxWaves = 8;  // waves per workgroup
 
-template <int MT, int C, int NCG, int NKG, int MODE>
+template <int MT, int RC, int MODE>
 struct GemmCfg {
   static constexpr bool kE8 = (MODE & 1) != 0;
   static constexpr bool kPreq = (MODE & 2) != 0;
-  static constexpr int kS = 16 / C;                 // K blocks per weight fragment
-  static constexpr int kMP = 16 * MT;               // rows per workgroup (M padded to the MFMA)
-  static constexpr int kStq = kKCMax * kMP * kRowStride;
-  static constexpr int kSts = kKCMax * kMP * (kE8 ? 1 : 4);
-  // partial-sum block of one (MFMA wave, column group, M tile): 4 x 64 floats, padded so that
-  // consecutive column groups start 16 floats apart modulo the 64 LDS banks
-  static constexpr int kRedPitch = 4 * 64 + 16 / MT;
-  static constexpr int kRed = kMaxMfmaWaves * NCG * MT * kRedPitch * 4;
-  // One M tile with shared activation tiles (NCG > 1): the partial sums get their own LDS space
-  // after the staging area, so the last round needs no barrier between the MFMAs and the
-  // partial-sum writes.  Otherwise they reuse the staging space.
-  static constexpr bool kRedOwn = (MT == 1 && NCG > 1);
-  static constexpr int kRedOff = kRedOwn ? (kStq + kSts + 15) / 16 * 16 : 0;
-  static constexpr int kSmem = kRedOwn ? kRedOff + kRed : ((kStq + kSts) > kRed ? (kStq + kSts) : kRed);
+  static constexpr int kMP = 16 * MT;                    // rows per workgroup (M padded to the MFMA)
+  static constexpr int kPasses = MT * RC;                // 16-group passes of a full round
+  static constexpr int kStq = RC * kMP * kRowStride;     // one wave's staged e4m3 rows
+  static constexpr int kSts = RC * kMP * 4;              // their scales (fp32, or e8m0 bytes)
+  static constexpr int kRed = 2 * MT * 4 * 64 * 4;       // one wave's partial sums (both groups)
+  static constexpr int kWave = ((kStq + kSts > kRed ? kStq + kSts : kRed) + 15) / 16 * 16;
+  static constexpr int kSmem = kMaxWaves * kWave;
 };
 
-// One workgroup owns CGW consecutive column groups (C columns each) and all of K; with 256
-// workgroups every CU streams the same number of weight bytes.  The first QW waves quantise (or
-// stage) the activations of a round of K blocks into LDS, two passes of loads in flight per wave.
-// The NWK * NWC MFMA waves follow.  MFMA wave (kq, cq) = (w % NWK, w / NWK) owns the column
-// groups cq, cq + NWC, ... (NCG at most) and, in every round, part kq of NWK contiguous parts of
-// that round's K groups (NKG at most): it reads each staged activation tile of its K groups once and
-// multiplies it into the weight fragments of all its column groups, so the activation bytes cross
-// the LDS once per NCG column groups.  Every weight load is unconditional (a buffer load whose
-// offset points past the workgroup's region when the slot is unused, so the hardware returns zeros
-// without touching memory); the code between the loads and the MFMAs is straight-line, which lets
-// each MFMA wait only for its own fragment.
-//
-// A fragment's S K blocks are S MFMAs chained into one accumulator.  MFMA s must only count in
-// the lanes whose B column belongs to K block s; the other lanes get the B-scale byte 0 (2^-127)
-// for it, so their share is scaled down by 2^-127 (below 2^-127 * 448^2 * 128 of that block's raw
-// dot product) instead of costing a masking operation per MFMA.  In the fp32-scale modes each
-// lane then multiplies the fragment's partial by x_scale * w_scale of its own K block (the pages'
-// 128x128 weight_scale_inv); in the e8m0 modes the scales are the MFMA's own e8m0 scale operands
-// and the accumulator runs over all of K.
-template <int MT, int C, int NCG, int NKG, int MODE>
-__global__ __launch_bounds__(1024) void smallm_gemm_kernel(
+// A wave-uniform fp32 value loaded through the scalar cache.
+__device__ __forceinline__ float sload_f32(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
+}
+
+__device__ __forceinline__ float dpp_f32_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_f32_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+}
+
+// One workgroup per column share of the packed layout (one per CU for the pages' shapes).  Wave w
+// owns K blocks [w R, w R + R) of both of the workgroup's column groups and runs over them in
+// rounds of RC blocks:
+//   1. it loads the activation rows of the round's K blocks (bf16, or pre-quantised bytes and
+//      scales), then issues every weight fragment of the round as non-temporal 16-byte buffer
+//      loads, the activation loads first so that they are not queued behind the weight stream;
+//   2. it quantises the rows itself, a DPP quad of lanes per 1x128 group with 16 groups per pass
+//      (row-major over the round's K blocks, so that one pass covers 16 / RC rows), and stages the
+//      e4m3 bytes and scales in its own part of LDS; no other wave reads them, so there is no
+//      workgroup barrier before the MFMAs;
+//   3. each fragment is consumed as soon as its own loads have landed: a 16-column fragment is one
+//      16x16x128 MFMA per M tile; a remainder fragment (CB columns x SB K blocks) is SB MFMAs on
+//      the same accumulator, the B operand masked so that MFMA s only sees the B columns of K block
+//      s (exact: the other columns contribute zero).
+// fp32 scales: each K block's (or each lane's K block's) partial is multiplied by
+// x_scale * w_scale into the accumulator; e8m0 scales are the MFMA's own scale operands.  The waves'
+// partial sums meet once in LDS, summed in wave order.
+template <int MT, int MODE, int NA, bool HASB, int SB, int RC>
+__global__ __launch_bounds__(512) void smallm_gemm_kernel(
     const void* __restrict__ a_src, int64_t lda, const void* __restrict__ sa_src,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
-    int64_t ldy, int M, int K, int CGW, int NWK, int NWC, int QW, uint8_t* __restrict__ q_dbg,
+    int64_t ldy, int M, int K, int R, int CB, int NWG, uint8_t* __restrict__ q_dbg,
     void* __restrict__ sx_dbg) {
-  using Cfg = GemmCfg<MT, C, NCG, NKG, MODE>;
-  constexpr int S = Cfg::kS, MP = Cfg::kMP;
+  using Cfg = GemmCfg<MT, RC, MODE>;
+  constexpr int MP = Cfg::kMP;
+  constexpr int NPASS = Cfg::kPasses;
+  constexpr int NV = Cfg::kPreq ? 2 : 4;  // 16-byte activation loads per lane and pass
+  constexpr int rowb = Cfg::kPreq ? 1 : 2;  // bytes per activation element
+  constexpr int NFB = HASB ? RC / SB : 1;  // remainder fragments per round
+  static_assert(!HASB || (RC % SB == 0), "a round holds whole remainder fragments");
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
-  uint8_t* stq = smem;
-  float* sts_f = (float*)(smem + Cfg::kStq);
-  uint8_t* sts_b = smem + Cfg::kStq;
-  float* red = (float*)(smem + Cfg::kRedOff);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
   const int KB = K >> 7;
-  const int KG = KB / S;
-  const int KC = NKG * NWK * S;     // K blocks per round
-  const int cg0 = blockIdx.x * CGW;
+  const int wg = blockIdx.x;
   const int m0 = blockIdx.y * MP;
   const int Mc = min(M - m0, MP);
-  const int s_l = (lane & 15) % S;  // K block (within a fragment) of this lane's B column
+  uint8_t* stq = smem + wave * Cfg::kWave;
+  float* sts_f = (float*)(stq + Cfg::kStq);
+  uint8_t* sts_b = stq + Cfg::kStq;
 
-  const int mw = wave - QW;
-  const int kq = (mw >= 0) ? mw % NWK : 0;
-  const int cq = (mw >= 0) ? mw / NWK : 0;
-  const uint32_t region = (uint32_t)CGW * (uint32_t)KG * 2048u;
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(wp + (int64_t)cg0 * KG * 2048), 0, (int)region, 0x00020000);
+  // this workgroup's packed bytes: the 16-column fragments, then the remainder fragments
+  const int cols = 16 * NA + CB;
+  const uint8_t* wreg = wp + (int64_t)wg * cols * K;
+  const uint32_t abytes = (uint32_t)(NA * KB) * 2048u;
+  const int NB = HASB ? CB * SB : 16;       // B columns of a remainder fragment
+  const uint32_t fbytes = (uint32_t)NB * 128u;
+  const uint32_t bbytes = HASB ? (uint32_t)(KB / SB) * fbytes : 0u;
+  const __amdgpu_buffer_rsrc_t wrA = __builtin_amdgcn_make_buffer_rsrc((void*)wreg, 0, (int)abytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrB = __builtin_amdgcn_make_buffer_rsrc((void*)(wreg + abytes), 0, (int)bbytes, 0x00020000);
+  const int nbA = (16 * wg) >> 7;                      // 128-column block of the 16-column group
+  const int nbB = (16 * NA * NWG + CB * wg) >> 7;      // and of the remainder group
 
-  v4f acc[NCG][MT];
-#pragma unroll
-  for (int j = 0; j < NCG; ++j)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // e8m0 with one column group: odd fragments accumulate separately, so that the MFMA chain of
-  // consecutive fragments is two independent chains (added once at the end)
-  v4f acc_odd[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc_odd[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const int kw0 = wave * R;
+  const int kw1 = min(kw0 + R, KB);
 
-  // Each role runs its own round loop (same number of barriers per round on both sides), so
-  // that values one role keeps across rounds take no registers in the other.
-  const int rounds = (KB + KC - 1) / KC;
-  if (mw >= 0) {
-    for (int rd = 0; rd < rounds; ++rd) {
-      const int kb0 = rd * KC;
-      const int KCr = min(KC, KB - kb0);
-      // ---- MFMA waves ----
-      // The lane index, formed afresh in every round where the compiler cannot see through it, so
-      // that the lane-dependent addresses are computed inside the round instead of held in
-      // registers across the whole loop (which would spill: a spill reload waits for every load
-      // in flight).
-      int ln;
-      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-      const int s_lr = (ln & 15) % S;  // K block (within a fragment) of this lane's B column
-      const int KGr = KCr / S;
-      // this wave's K groups of the round: a contiguous share [kg_lo, kg_lo + nkg)
-      const int kg_lo = kq * KGr / NWK;
-      const int nkg = (kq + 1) * KGr / NWK - kg_lo;
-      float swv[NKG][NCG];
-      int sbl[NKG][NCG];
-      u32x4 wr[NKG][NCG][2];
-      // Block scales: a fragment's S scales are contiguous and the same for the whole wave, so
-      // they are read with scalar loads (own counter: waiting for them never waits for the weight
-      // stream, and they take no vector registers); each lane then picks its own K block's.
+  // activations of the row chunk as a bounds-checked buffer (idle lanes read zeros past its end)
+  const uint32_t xbytes = (uint32_t)((int64_t)(Mc - 1) * lda * rowb + (int64_t)K * rowb);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)a_src + (int64_t)m0 * lda * rowb), 0, (int)xbytes, 0x00020000);
+  const uint32_t sbytes_x = (uint32_t)(Mc * KB) * (Cfg::kE8 ? 1u : 4u);
+  const __amdgpu_buffer_rsrc_t sxr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)sa_src + (int64_t)m0 * KB * (Cfg::kE8 ? 1 : 4)), 0, (int)sbytes_x, 0x00020000);
+  const uint32_t swbytes = Cfg::kE8 ? (uint32_t)((cols * NWG / 128) * KB) : 0u;  // the whole [N/128, K/128] array
+  const __amdgpu_buffer_rsrc_t swr = __builtin_amdgcn_make_buffer_rsrc((void*)sw, 0, (int)swbytes, 0x00020000);
+
+  v4f accA[MT], accA2[MT], accB[MT], accB2[MT];
 #pragma unroll
-      for (int i = 0; i < NKG; ++i)
-#pragma unroll
-        for (int j = 0; j < NCG; ++j) {
-          const int cg = min(cq + j * NWC, CGW - 1);
-          const int nb = ((cg0 + cg) * C) >> 7;  // 128-column block of the column group
-          const int kbs = __builtin_amdgcn_readfirstlane(min(kb0 + (kg_lo + i) * S, KB - S));
-          const int base = __builtin_amdgcn_readfirstlane(nb * KB + kbs);
-          if (Cfg::kE8) {
-            const uint8_t* sp = (const uint8_t*)sw + base;
-            uint32_t word = 0;
-#pragma unroll
-            for (int t = 0; t < (S < 4 ? S : 4); ++t) word |= (uint32_t)sp[t] << (8 * t);
-            if (S == 8) {
-              uint32_t hi = 0;
-#pragma unroll
-              for (int t = 4; t < 8; ++t) hi |= (uint32_t)sp[t] << (8 * (t - 4));
-              word = (s_lr < 4) ? word : hi;
-            }
-            sbl[i][j] = (int)((word >> (8 * (s_lr & 3))) & 0xFFu);
-          } else {
-            const float* sp = (const float*)sw + base;
-            float sc[S];
-#pragma unroll
-            for (int t = 0; t < S; ++t) sc[t] = sp[t];
-            float v = sc[0];
-#pragma unroll
-            for (int t = 1; t < S; ++t) v = (s_lr == t) ? sc[t] : v;
-            swv[i][j] = v;
-          }
-        }
-#pragma unroll
-      for (int i = 0; i < NKG; ++i)
-#pragma unroll
-        for (int j = 0; j < NCG; ++j) {
-          const int cg = cq + j * NWC;
-          const uint32_t off = (i < nkg && cg < CGW)
-                                   ? ((uint32_t)(cg * KG + kb0 / S + kg_lo + i) * 2048u + ln * 16u)
-                                   : region;
-          wr[i][j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 2));
-          wr[i][j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off + 1024u, 0, 2));
-        }
-      __syncthreads();  // activation bytes and scales of this round are staged
-#pragma unroll
-      for (int i = 0; i < NKG; ++i) {
-        // K group within the round; a slot past the wave's share has zero weights and reads a
-        // staged tile (finite bytes), so its products are exactly zero
-        const int kgr = min(kg_lo + i, KGr - 1);
-        // with eight fragments, shared tiles or two M tiles of multi-block fragments, keep the
-        // scheduler from hoisting the next K group's LDS reads over this one (their registers
-        // would not fit, and a spill reload waits for every load in flight)
-        if (NKG >= 8 || NCG > 1 || (MT == 2 && S >= 2)) __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NCG == 1) {
-          // one column group: each activation tile is read right before its MFMA
-          const v8i b = __builtin_bit_cast(
-              v8i, __builtin_shufflevector(wr[i][0][0], wr[i][0][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          v4f fa[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) fa[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const int kbr = kgr * S + s;  // K block within the round
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const int row = mt * 16 + (ln & 15);
-              const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
-              const u32x4 a0 = ap[0], a1 = ap[1];
-              const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-              if (Cfg::kE8) {
-                const int sa = (int)sts_b[kbr * MP + row];
-                const int sb = (S == 1 || s_lr == s) ? sbl[i][0] : 0;
-                v4f& dst = (i & 1) ? acc_odd[mt] : acc[0][mt];
-                dst = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, dst, 0, 0, 0, sa, 0, sb);
-              } else if (S == 1) {
-                fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 0, 0, 0);
-              } else {
-                const int sb = (s_lr == s) ? 127 : 0;
-                fa[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[mt], 0, 0, 0, 127, 0, sb);
-              }
-            }
-          }
-          if (!Cfg::kE8) {
-            const int kbl = kgr * S + s_lr;  // this ln's K block within the round
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[0][mt][e] = __builtin_fmaf(sx4[e] * swv[i][0], fa[mt][e], acc[0][mt][e]);
-            }
-          }
-        } else {
-          if constexpr (MT == 1) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              // the K group's S activation tiles, read from LDS once for all NCG column groups
-              const int row = mt * 16 + (ln & 15);
-              v8i a[S];
-              int sa[S];
-#pragma unroll
-              for (int s = 0; s < S; ++s) {
-                const int kbr = kgr * S + s;  // K block within the round
-                const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
-                const u32x4 a0 = ap[0], a1 = ap[1];
-                a[s] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                sa[s] = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
-              }
-              v4f sx4 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-              if (!Cfg::kE8) {
-                const int kbl = kgr * S + s_lr;  // this ln's K block within the round
-                sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
-              }
-              // fragments in groups of up to three, whose MFMA chains interleave (a dependent chain
-              // would wait for each MFMA's result), each group consumed as soon as its loads land
-              constexpr int JG = NCG < 3 ? NCG : 3;
-#pragma unroll
-              for (int j0 = 0; j0 < NCG; j0 += JG) {
-                v8i b[JG];
-                v4f fa[JG];
-#pragma unroll
-                for (int jj = 0; jj < JG; ++jj) {
-                  const int j = min(j0 + jj, NCG - 1);
-                  b[jj] = __builtin_bit_cast(
-                      v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                  fa[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-                }
-#pragma unroll
-                for (int s = 0; s < S; ++s)
-#pragma unroll
-                  for (int jj = 0; jj < JG; ++jj) {
-                    const int j = j0 + jj;
-                    if (j >= NCG) continue;
-                    if (Cfg::kE8) {
-                      const int sb = (S == 1 || s_lr == s) ? sbl[i][j] : 0;
-                      acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], acc[j][mt], 0, 0, 0, sa[s], 0, sb);
-                    } else if (S == 1) {
-                      fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 0, 0, 0);
-                    } else {
-                      const int sb = (s_lr == s) ? 127 : 0;
-                      fa[jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[s], b[jj], fa[jj], 0, 0, 0, 127, 0, sb);
-                    }
-                  }
-                if (!Cfg::kE8) {
-#pragma unroll
-                  for (int jj = 0; jj < JG; ++jj) {
-                    const int j = j0 + jj;
-                    if (j >= NCG) continue;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                      acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[jj][e], acc[j][mt][e]);
-                  }
-                }
-              }
-            }
-          } else {
-            // two M tiles: one activation tile at a time (the accumulators of both tiles are
-            // live), the NCG independent MFMA chains interleaved
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const int row = mt * 16 + (ln & 15);
-              v4f fa[NCG];
-#pragma unroll
-              for (int j = 0; j < NCG; ++j) fa[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-              for (int s = 0; s < S; ++s) {
-                const int kbr = kgr * S + s;  // K block within the round
-                const u32x4* ap = (const u32x4*)(stq + (kbr * MP + row) * kRowStride + (ln >> 4) * 32);
-                const u32x4 a0 = ap[0], a1 = ap[1];
-                const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                  (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                const int sa = Cfg::kE8 ? (int)sts_b[kbr * MP + row] : 127;
-#pragma unroll
-                for (int j = 0; j < NCG; ++j) {
-                  const v8i b = __builtin_bit_cast(
-                      v8i, __builtin_shufflevector(wr[i][j][0], wr[i][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                  if (Cfg::kE8) {
-                    const int sb = (S == 1 || s_lr == s) ? sbl[i][j] : 0;
-                    acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j][mt], 0, 0, 0, sa, 0, sb);
-                  } else if (S == 1) {
-                    fa[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[j], 0, 0, 0, 0, 0, 0);
-                  } else {
-                    const int sb = (s_lr == s) ? 127 : 0;
-                    fa[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, fa[j], 0, 0, 0, 127, 0, sb);
-                  }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
-              if (!Cfg::kE8) {
-                const int kbl = kgr * S + s_lr;  // this lane's K block within the round
-                const v4f sx4 = *(const v4f*)(sts_f + kbl * MP + mt * 16 + 4 * (ln >> 4));
-#pragma unroll
-                for (int j = 0; j < NCG; ++j)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    acc[j][mt][e] = __builtin_fmaf(sx4[e] * swv[i][j], fa[j][e], acc[j][mt][e]);
-              }
-            }
-          }
-        }
-      }
-      if (!Cfg::kRedOwn || rd + 1 < rounds) __syncthreads();  // staging buffer free for the next round
-    }
-    if (Cfg::kE8 && NCG == 1) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[0][mt] += acc_odd[mt];
-    }
-  } else {
-    // the quantisers' loads and VALU work issue ahead of the MFMA waves' on their SIMD: the MFMA
-    // waves only wait for their weights, while the staged activations gate every MFMA
-    __builtin_amdgcn_s_setprio(3);
-    for (int rd = 0; rd < rounds; ++rd) {
-      const int kb0 = rd * KC;
-      const int KCr = min(KC, KB - kb0);
-      // ---- quantising (or staging) waves: one DPP quad per 1x128 group, two passes in flight ----
-      const int grp = lane >> 2;  // this lane's group within a block of 16
-      const int c = lane & 3;
-      const int G = Mc * KCr;
-      constexpr int NV = Cfg::kPreq ? 2 : 4;                    // 16-byte loads per lane per pass
-      const int rowb = Cfg::kPreq ? 1 : 2;                        // bytes per activation element
-      // the workgroup's activation rows as a bounds-checked buffer: idle lanes and passes past the
-      // work use an offset past its end and fetch nothing
-      const uint32_t abytes = (uint32_t)((int64_t)(Mc - 1) * lda * rowb + (int64_t)KB * 128 * rowb);
-      const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const uint8_t*)a_src + (int64_t)m0 * lda * rowb), 0, (int)abytes, 0x00020000);
-      u32x4 xa[4], xb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { xa[i] = u32x4{0, 0, 0, 0}; xb[i] = u32x4{0, 0, 0, 0}; }
-#define SMALLM_QLOAD(v, b) do {                                                                   \
-      const int g_ = (b) * 16 + grp;                                                             \
-      const uint32_t off_ = (g_ < G) ? (uint32_t)(((int64_t)(g_ % Mc) * lda + (kb0 + g_ / Mc) * 128 + c * 32) * rowb) \
-                                     : abytes;                                                   \
-      _Pragma("unroll") for (int i_ = 0; i_ < NV; ++i_)                                          \
-        v[i_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off_ + 16u * i_, 0, 0)); \
-    } while (0)
-#define SMALLM_QPROC(v, b) do {                                                                   \
-      const int g_ = (b) * 16 + grp;                                                             \
-      const bool valid_ = g_ < G;                                                                \
-      const int kbl_ = valid_ ? g_ / Mc : 0;                                                     \
-      const int m_ = valid_ ? g_ % Mc : 0;                                                       \
-      u32x4 qv_[2];                                                                              \
-      float s_ = 0.0f;                                                                           \
-      uint32_t e_ = 0;                                                                           \
-      if (!Cfg::kPreq) {                                                                         \
-        if (Cfg::kE8) e_ = quant32_e8m0(v, qv_);                                                 \
-        else s_ = quant32_fp32(v, qv_);                                                          \
-      } else {                                                                                   \
-        qv_[0] = v[0];                                                                           \
-        qv_[1] = v[1];                                                                           \
-      }                                                                                          \
-      if (valid_) {                                                                              \
-        u32x4* dp_ = (u32x4*)(stq + (kbl_ * MP + m_) * kRowStride + c * 32);                    \
-        dp_[0] = qv_[0];                                                                         \
-        dp_[1] = qv_[1];                                                                         \
-        if (c == 0) {                                                                            \
-          if (Cfg::kPreq) {                                                                      \
-            if (Cfg::kE8) sts_b[kbl_ * MP + m_] = ((const uint8_t*)sa_src)[(int64_t)(m0 + m_) * KB + kb0 + kbl_]; \
-            else sts_f[kbl_ * MP + m_] = ((const float*)sa_src)[(int64_t)(m0 + m_) * KB + kb0 + kbl_];           \
-          } else {                                                                               \
-            if (Cfg::kE8) sts_b[kbl_ * MP + m_] = (uint8_t)e_;                                   \
-            else sts_f[kbl_ * MP + m_] = s_;                                                     \
-          }                                                                                      \
-        }                                                                                        \
-      }                                                                                          \
-    } while (0)
-      // Block b of 16 groups: groups 16 b .. 16 b + 15, one per DPP quad of a wave.  Wave w takes
-      // blocks w, QW + w, 2 QW + w, ... alternating between its two buffers; the buffer processed
-      // next holds the smaller block index, so once it is past the end the other one is too.
-      const int nblk = (G + 15) >> 4;
-      int b0 = wave, b1 = QW + wave;
-      SMALLM_QLOAD(xa, b0);
-      SMALLM_QLOAD(xb, b1);
-      while (b0 < nblk) {
-        SMALLM_QPROC(xa, b0);
-        b0 += 2 * QW;
-        SMALLM_QLOAD(xa, b0);
-        if (b1 >= nblk) break;
-        SMALLM_QPROC(xb, b1);
-        b1 += 2 * QW;
-        SMALLM_QLOAD(xb, b1);
-      }
-#undef SMALLM_QLOAD
-#undef SMALLM_QPROC
-      __syncthreads();  // staged: the MFMA waves read it now
-      if (!Cfg::kPreq && blockIdx.x == 0) {
-        // debug copy of the quantised bytes and scales this round used
-        const int qt = tid;  // 0 .. 64*QW-1
-        if (q_dbg != nullptr) {
-          for (int g = qt; g < Mc * KCr * 8; g += QW * 64) {
-            const int row = g / (KCr * 8), rem = g % (KCr * 8), kbl = rem / 8, part16 = rem % 8;
-            *(u32x4*)(q_dbg + (int64_t)(m0 + row) * K + (kb0 + kbl) * 128 + part16 * 16) =
-                *(const u32x4*)(stq + (kbl * MP + row) * kRowStride + part16 * 16);
-          }
-        }
-        if (sx_dbg != nullptr) {
-          for (int g = qt; g < Mc * KCr; g += QW * 64) {
-            const int row = g / KCr, kbl = g % KCr;
-            if (Cfg::kE8) ((uint8_t*)sx_dbg)[(int64_t)(m0 + row) * KB + kb0 + kbl] = sts_b[kbl * MP + row];
-            else ((float*)sx_dbg)[(int64_t)(m0 + row) * KB + kb0 + kbl] = sts_f[kbl * MP + row];
-          }
-        }
-      }
-      if (!Cfg::kRedOwn || rd + 1 < rounds) __syncthreads();
-    }
+  for (int mt = 0; mt < MT; ++mt) {
+    accA[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    accA2[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    accB[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    accB2[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // ---- cross-wave and cross-lane reduction through LDS, fixed order ----
-  // (lane and thread index formed again here rather than held across the rounds)
-  int lane_e;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
-  const int tid_e = wave * 64 + lane_e;
-  constexpr int RP = Cfg::kRedPitch;
-  if (mw >= 0) {
+  for (int kr = kw0; kr < kw1; kr += RC) {
+    // the lane index, formed afresh in every round where the compiler cannot see through it, so
+    // that lane-derived addresses are computed inside the round instead of held in registers
+    // across it (a spill reload would wait for every load in flight)
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int nk = min(RC, kw1 - kr);   // K blocks of this round; the others are masked
+    const int G = Mc * RC;              // groups of the round (row-major over its K blocks)
+    const int grp = ln >> 2, c = ln & 3;
+    const int jl = ln & 15;                 // B column of this lane
+    const int sl = jl & (SB - 1);           // its K block within a remainder fragment
+    const bool bcol = jl < NB;
+    const uint32_t boff = (uint32_t)(((ln >> 4) * NB + jl) * 16);
+
+    // ---- 1. activation loads, then the weight stream ----
+    // weight block scales of the round's K blocks, first in the queue (index clamped into the row:
+    // blocks past the wave's range multiply zero weights)
+    float swA[RC], swB[RC];
+    int ewA[RC], ewB[RC];
 #pragma unroll
-    for (int j = 0; j < NCG; ++j)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[((mw * NCG + j) * MT + mt) * RP + e * 64 + lane_e] = acc[j][mt][e];
-  }
-  // One output per thread and pass, consecutive threads on consecutive columns of a row.  A
-  // column's S K-block partials sit in S consecutive lanes, read as one vector per MFMA wave.
-  // The first output's indices are formed before the barrier, off the critical path.
-  const unsigned ncols = (unsigned)(CGW * C);
-  const unsigned nthreads = blockDim.x;  // > ncols
-  unsigned row = (unsigned)tid_e / ncols;
-  unsigned col = (unsigned)tid_e - row * ncols;
-  const unsigned drow = nthreads / ncols, dcol = nthreads - drow * ncols;
-  const int kstride = NCG * MT * RP;
-  __syncthreads();
-  while (row < (unsigned)Mc) {
-    const unsigned cgw = col / C, cc = col % C;
-    const unsigned j = cgw / (unsigned)NWC, cqo = cgw - j * (unsigned)NWC;
-    const unsigned mt = row >> 4, r = row & 15, e = r & 3;
-    const unsigned lbase = (r >> 2) * 16 + cc * S;  // lanes of the column's S K blocks
-    const float* rp = red + ((cqo * NWK * NCG + j) * MT + mt) * RP + e * 64 + lbase;
-    float sum = 0.0f;
-#pragma unroll 4
-    for (int k = 0; k < NWK; ++k, rp += kstride) {
-      if constexpr (S >= 4) {
-#pragma unroll
-        for (int s4 = 0; s4 < S; s4 += 4) {
-          const v4f v = *(const v4f*)(rp + s4);
-          sum += v[0]; sum += v[1]; sum += v[2]; sum += v[3];
-        }
-      } else if constexpr (S == 2) {
-        const v2f v = *(const v2f*)rp;
-        sum += v[0]; sum += v[1];
+    for (int i = 0; i < RC; ++i) {
+      const int kb = min(kr + i, KB - 1);
+      if (!Cfg::kE8) {
+        swA[i] = NA ? sload_f32((const float*)sw + nbA * KB + kb) : 0.0f;
+        swB[i] = HASB ? sload_f32((const float*)sw + nbB * KB + kb) : 0.0f;
       } else {
-        sum += rp[0];
+        ewA[i] = NA ? __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b8(swr, (uint32_t)(nbA * KB + kb), 0, 0)) : 0;
+        ewB[i] = HASB ? __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b8(swr, (uint32_t)(nbB * KB + kb), 0, 0)) : 0;
       }
     }
-    y[(int64_t)(m0 + row) * ldy + (int64_t)(cg0 + cgw) * C + cc] = bf16_rne(sum);
-    row += drow;
-    col += dcol;
-    if (col >= ncols) { col -= ncols; ++row; }
+
+    u32x4 xv[NPASS][NV];
+    uint32_t xs[NPASS];
+    // activation loads of passes [P0, P1)
+    auto load_act = [&](auto P0c, auto P1c) {
+      constexpr int P0 = decltype(P0c)::value, P1 = decltype(P1c)::value;
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        if (p < P0 || p >= P1) continue;
+        if (p * 16 < G) {
+          const int g = p * 16 + grp;
+          const int m = g / RC, kbl = g & (RC - 1);
+          const bool valid = g < G && kbl < nk;
+          const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * 32) * rowb) : xbytes;
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            xv[p][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0));
+          if (Cfg::kPreq) {
+            const uint32_t so = valid ? (uint32_t)(m * KB + kr + kbl) * (Cfg::kE8 ? 1u : 4u) : sbytes_x;
+            xs[p] = Cfg::kE8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sxr, so, 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b32(sxr, so, 0, 0);
+          }
+        }
+      }
+    };
+    // quantisation (or staging) of passes [P0, P1) into this wave's LDS
+    auto quant_act = [&](auto P0c, auto P1c) {
+      constexpr int P0 = decltype(P0c)::value, P1 = decltype(P1c)::value;
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        if (p < P0 || p >= P1) continue;
+        if (p * 16 < G) {
+          const int g = p * 16 + grp;
+          const int m = g / RC, kbl = g & (RC - 1);
+          u32x4 qv[2];
+          float sc = 0.0f;
+          uint32_t eb = 0;
+          if constexpr (!Cfg::kPreq) {
+            if constexpr (Cfg::kE8) eb = quant32_e8m0(xv[p], qv);
+            else sc = quant32_fp32(xv[p], qv);
+          } else {
+            qv[0] = xv[p][0];
+            qv[1] = xv[p][1];
+            if (Cfg::kE8) eb = xs[p];
+            else sc = __uint_as_float(xs[p]);
+          }
+          // K blocks past the wave's range (a short last round) are staged too: their loads
+          // returned zeros, so the MFMAs on them see zero codes and scales instead of stale LDS
+          if (g < G) {
+            u32x4* dp = (u32x4*)(stq + (kbl * MP + m) * kRowStride + c * 32);
+            dp[0] = qv[0];
+            dp[1] = qv[1];
+            if (c == 0) {
+              if (Cfg::kE8) sts_b[kbl * MP + m] = (uint8_t)eb;
+              else sts_f[kbl * MP + m] = sc;
+            }
+          }
+        }
+      }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using CH = std::integral_constant<int, NPASS / MT>;
+    using CN = std::integral_constant<int, NPASS>;
+    // MT = 2: the second 16-row tile is loaded after the first one is quantised (its registers
+    // would not fit beside the first tile's and the weights)
+    load_act(C0{}, CH{});
+    // the remainder fragments first: every K block of the round has an MFMA on them
+    u32x4 wa[RC][2], wb[NFB][2];
+#pragma unroll
+    for (int f = 0; f < NFB; ++f) {
+      if (HASB) {
+        const uint32_t off = (f * SB < nk && bcol) ? (uint32_t)((kr / SB) + f) * fbytes + boff : bbytes;
+        wb[f][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, off, 0, 2));
+        wb[f][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, off + (fbytes >> 1), 0, 2));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      if (NA) {
+        const uint32_t off = (i < nk) ? (uint32_t)(kr + i) * 2048u + (uint32_t)ln * 16u : abytes;
+        wa[i][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, off, 0, 2));
+        wa[i][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, off + 1024u, 0, 2));
+      }
+    }
+    // ---- 2. quantise (or stage) the round's activations into this wave's LDS ----
+    quant_act(C0{}, CH{});
+    if (MT == 2) {
+      load_act(CH{}, CN{});
+      quant_act(CH{}, CN{});
+    }
+    // the staged rows are read back by other lanes of this wave: LDS executes a wave's accesses
+    // in order, so only the compiler must not move the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (!Cfg::kPreq && wg == 0 && (q_dbg != nullptr || sx_dbg != nullptr)) {
+      // debug copies of the bytes and scales this round used (workgroup 0 only), from the staging area
+      for (int t = ln; t < Mc * nk * 8; t += 64) {
+        const int row = t / (nk * 8), rem = t - row * nk * 8, kbl = rem >> 3, part = rem & 7;
+        if (q_dbg != nullptr)
+          *(u32x4*)(q_dbg + (int64_t)(m0 + row) * K + (kr + kbl) * 128 + part * 16) =
+              *(const u32x4*)(stq + (kbl * MP + row) * kRowStride + part * 16);
+        if (sx_dbg != nullptr && part == 0) {
+          if (Cfg::kE8) ((uint8_t*)sx_dbg)[(int64_t)(m0 + row) * KB + kr + kbl] = sts_b[kbl * MP + row];
+          else ((float*)sx_dbg)[(int64_t)(m0 + row) * KB + kr + kbl] = sts_f[kbl * MP + row];
+        }
+      }
+    }
+
+    // ---- 3. MFMAs: the remainder fragments' chains, then the 16-column fragments in K order, each
+    // as soon as its loads have landed ----
+    // A remainder fragment's MFMA for its K block s sees only the B columns of that block (the
+    // others are masked to zero), so in the fp32 modes its result is scaled like a 16-column
+    // fragment's: lanes of other K blocks hold exact zeros and add nothing.
+    auto tile = [&](int i, int mt, v8i& at, v4f& sx4, int& sa) {
+      const int row = mt * 16 + jl;
+      const u32x4* ap = (const u32x4*)(stq + (i * MP + row) * kRowStride + (ln >> 4) * 32);
+      const u32x4 a0 = ap[0], a1 = ap[1];
+      at = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      if (Cfg::kE8) sa = (int)sts_b[i * MP + row];
+      else sx4 = *(const v4f*)(sts_f + i * MP + mt * 16 + 4 * (ln >> 4));
+    };
+    if (HASB) {
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        if (MT == 2) __builtin_amdgcn_sched_barrier(0);  // one K block's tiles live at a time
+        const int f = i / SB, s = i % SB;
+        v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[f][0], wb[f][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (SB > 1) {
+          const uint32_t bmask = (sl == s) ? 0xFFFFFFFFu : 0u;  // lanes of K block s
+#pragma unroll
+          for (int d = 0; d < 8; ++d) b[d] = (int)((uint32_t)b[d] & bmask);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v8i at;
+          v4f sx4;
+          int sa;
+          tile(i, mt, at, sx4, sa);
+          if (Cfg::kE8) {
+            v4f& acc = (i & 1) ? accB2[mt] : accB[mt];
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, acc, 0, 0, 0, sa, 0, ewB[i]);
+          } else {
+            const v4f fb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                            0, 0, 0, 127, 0, 127);
+            const float sc = swB[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accB[mt][e] = __builtin_fmaf(sx4[e] * sc, fb[e], accB[mt][e]);
+          }
+        }
+      }
+    }
+    if (NA) {
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        if (MT == 2) __builtin_amdgcn_sched_barrier(0);
+        const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wa[i][0], wa[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v8i at;
+          v4f sx4;
+          int sa;
+          tile(i, mt, at, sx4, sa);
+          if (Cfg::kE8) {
+            v4f& acc = (i & 1) ? accA2[mt] : accA[mt];
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, acc, 0, 0, 0, sa, 0, ewA[i]);
+          } else {
+            const v4f fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                            0, 0, 0, 127, 0, 127);
+            const float sc = swA[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accA[mt][e] = __builtin_fmaf(sx4[e] * sc, fa[e], accA[mt][e]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- partial sums into this wave's LDS (its staging area is no longer read), then the sum ----
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* red = (float*)stq;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    v4f pa = accA[mt];
+    if (Cfg::kE8) pa += accA2[mt];
+    v4f pb = accB[mt];
+    if (Cfg::kE8) pb += accB2[mt];
+    if (HASB && SB > 1) {
+      // the SB K-block partials of a remainder column sit in SB neighbouring lanes: fold them into
+      // the first, in a fixed order
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] += dpp_f32_xor1(pb[e]);
+        if (SB > 2) pb[e] += dpp_f32_xor2(pb[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (NA) red[((0 * MT + mt) * 4 + e) * 64 + lane] = pa[e];
+      if (HASB) red[((1 * MT + mt) * 4 + e) * 64 + lane] = pb[e];
+    }
+  }
+  __syncthreads();
+  const int na16 = 16 * NA;
+  const int nout = Mc * cols;
+  for (int t = tid; t < nout; t += blockDim.x) {
+    const int row = t / cols, ci = t - row * cols;
+    const int mt = row >> 4, r = row & 15, e = r & 3;
+    const bool inA = ci < na16;
+    const int part = inA ? 0 : 1;
+    const int li = (r >> 2) * 16 + (inA ? ci : (ci - na16) * SB);
+    const float* rp = (const float*)smem + ((part * MT + mt) * 4 + e) * 64 + li;
+    float v[kMaxWaves];
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; ++w) v[w] = (w < nwaves) ? rp[w * (Cfg::kWave / 4)] : -0.0f;  // x + -0 == x
+    float sum = v[0];
+#pragma unroll
+    for (int w = 1; w < kMaxWaves; ++w) sum += v[w];
+    const int col = inA ? 16 * wg + ci : na16 * NWG + CB * wg + (ci - na16);
+    y[(int64_t)(m0 + row) * ldy + col] = bf16_rne(sum);
   }
 }
 
@@ -1132,147 +1049,97 @@ int launch_status() { return hipGetLastError() == hipSuccess ? SMALLM_OK : SMALL
 
 constexpr int kTargetWGs = 256;  // one workgroup per CU of the MI355X
 
-// MFMA waves that share one column group when a workgroup owns CGW of them.
-int waves_per_group(int CGW) { return CGW >= 3 ? 1 : 4 / CGW; }
-
-// Column groups per workgroup for C-column groups (1 when they do not split evenly over 256).
-int groups_per_wg(int N, int C) {
-  const int CG = N / C;
-  if (CG % kTargetWGs != 0) return 1;
-  int nwg = kTargetWGs, CGW = CG / nwg;
-  while (CGW > kMaxMfmaWaves && CG % (2 * nwg) == 0) { nwg *= 2; CGW = CG / nwg; }
-  return CGW > kMaxMfmaWaves ? 1 : CGW;
-}
-
-// Columns per group of the packed layout for an [N, K] weight: the widest C whose column-group
-// count is a multiple of 256 (equal weight bytes per CU), whose K-blocks per fragment divide
-// K / 128, and whose rounds fit the 32 staged K blocks; 16 when none is.
-int layout_columns(int N, int K) {
-  const int KB = K / 128;
-  for (int c : {16, 8, 4, 2}) {
-    const int S = 16 / c;
-    if (KB % S != 0 || (N / c) % kTargetWGs != 0) continue;
-    if (S * waves_per_group(groups_per_wg(N, c)) * 4 > kKCMax) continue;
-    return c;
-  }
-  return 16;
-}
-
-uint32_t layout_id_for(int N, int K) { return 0x46380200u | (uint32_t)layout_columns(N, K); }
-
-struct Plan {
-  int C, CGW, nwg, NWK, NWC, NCG, NKG, NWM, KC, QW;
+// The packed layout and the launch it implies for an [N, K] weight.
+struct Layout {
+  int nwg;     // workgroups along N
+  int na;      // 16-column groups per workgroup (0 or 1)
+  int cb;      // remainder columns per workgroup (0, 2, 4 or 8)
+  int sb;      // K blocks per remainder fragment
+  int r;       // K blocks per wave
+  int rc;      // K blocks per round of a wave
+  int nw;      // waves per workgroup
 };
 
-// Quantising waves for a round of `groups` 1x128 groups next to nwm MFMA waves: about two
-// 16-group passes per wave, as 2, 4, 8 or 12 waves, and a multiple of 4 when more than 2 so that
-// every SIMD (wave w runs on SIMD w % 4) carries the same share of the quantiser's VALU work.
-int quant_waves(int groups, int nwm) {
-  const int need = (groups + 31) / 32;
-  const int qw = need <= 2 ? 2 : (need <= 4 ? 4 : (need <= 8 ? 8 : 12));
-  const int room = 16 - nwm;
-  return min(qw, room >= 4 ? room / 4 * 4 : 2);
-}
-
-Plan make_plan(int M, int N, int K) {
-  Plan p;
-  p.C = layout_columns(N, K);
-  const int S = 16 / p.C;
+// Waves split K: each takes r K blocks (the smallest power of two with r * 8 >= K / 128), in
+// rounds of at most 4.  Columns: N a multiple of 4096 gives one 16-column group per workgroup
+// (N / 16 workgroups, a multiple of 256); N = 256 (16 a + c) with a <= 1 and c in {2, 4, 8}
+// gives 256 workgroups, each with a 16-column groups and a c-column remainder group (the pages'
+// 5120, 4608 and 2048-column shards: every CU streams the same bytes); any other N falls back to
+// one 16-column group per workgroup.
+Layout layout_for(int N, int K) {
   const int KB = K / 128;
-  const int KG = KB / S;
-  const int Mr = min(M, 32);  // rows per workgroup
-  p.CGW = groups_per_wg(N, p.C);
-  p.nwg = (N / p.C) / p.CGW;
-  // One M tile: waves that share their activation tiles between NCG = 5 or 3 column groups, one
-  // K group per wave and round, when that still gives at least 4 MFMA waves; else (and for two M
-  // tiles, whose accumulators would not fit) one column group per wave.  NWK is the largest
-  // divisor of the K groups that fits, so that every round is full.
-  p.NCG = 0;
-  for (int ncg : {5, 3}) {
-    if (p.CGW % ncg != 0 || ncg * 8 + S * 8 + ncg * 4 > 100) continue;  // registers
-    const int nwc = p.CGW / ncg;
-    const int cap = min(kMaxMfmaWaves / nwc, kKCMax / S);
-    int nwk = 0;
-    for (int d = 1; d <= cap; ++d)
-      if (KG % d == 0) nwk = d;
-    if (nwk * nwc < 4) continue;
-    // When the quantising waves that fit beside nwk * nwc MFMA waves would still take five or
-    // more passes each, the next smaller divisor (as long as it needs at most two rounds) frees
-    // waves for the quantiser: its VALU work, not the weight stream, is then what the kernel waits for.
-    const int g = Mr * min(KB, nwk * S);
-    const int qw = quant_waves(g, nwk * nwc);
-    const int passes = (g + 16 * qw - 1) / (16 * qw) * ((KB + nwk * S - 1) / (nwk * S));
-    if (passes >= 5) {
-      int d = nwk - 1;
-      while (d >= 1 && KG % d != 0) --d;
-      if (d >= 1 && (KB + d * S - 1) / (d * S) <= 2) nwk = d;
+  Layout L;
+  int r = 1;
+  while (r * kMaxWaves < KB) r <<= 1;
+  L.r = r;
+  L.rc = r < 4 ? r : 4;
+  L.nw = (KB + r - 1) / r;
+  L.na = 1;
+  L.cb = 0;
+  L.sb = 1;
+  L.nwg = N / 16;
+  if (N % 4096 != 0 && N % 256 == 0) {
+    const int units = N / 256, a = units / 16, c = units % 16;
+    if (a <= 1 && (c == 2 || c == 4 || c == 8)) {
+      const int sb = min(16 / c, L.rc);
+      if (KB % sb == 0) {
+        L.na = a;
+        L.cb = c;
+        L.sb = sb;
+        L.nwg = kTargetWGs;
+      }
     }
-    p.NCG = ncg; p.NKG = 1; p.NWC = nwc; p.NWK = nwk;
-    break;
   }
-  if (p.NCG == 0) {
-    p.NCG = 1;
-    p.NWC = p.CGW;
-    p.NWK = waves_per_group(p.CGW);
-    p.NKG = (S * p.NWK * 8 <= kKCMax && KG >= 8 * p.NWK) ? 8 : 4;
-  }
-  p.NWM = p.NWK * p.NWC;
-  p.KC = p.NKG * p.NWK * S;
-  p.QW = quant_waves(Mr * min(KB, p.KC), p.NWM);
-  return p;
+  return L;
 }
 
-template <int MODE, int MT, int C>
-void launch_c(const Plan& pl, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
+uint32_t layout_id_for(int N, int K) {
+  const Layout L = layout_for(N, K);
+  return 0x46390000u | ((uint32_t)L.na << 12) | ((uint32_t)L.cb << 4) | (uint32_t)L.sb;
+}
+
+template <int MODE, int MT, int NA, bool HASB, int SB, int RC>
+void launch_k(const Layout& L, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
               const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K, uint8_t* q_dbg,
               void* sx_dbg) {
-  const dim3 block(64 * (pl.QW + pl.NWM));
-#define SMALLM_LAUNCH(ncg, nkg)                                                                          \
-  hipLaunchKernelGGL((smallm_gemm_kernel<MT, C, ncg, nkg, MODE>), grid, block, 0, stream, a, lda, sa, wp, \
-                     sw, y, ldy, M, K, pl.CGW, pl.NWK, pl.NWC, pl.QW, q_dbg, sx_dbg)
-  if constexpr (C != 2) {
-    if (pl.NCG == 5) { SMALLM_LAUNCH(5, 1); return; }
+  hipLaunchKernelGGL((smallm_gemm_kernel<MT, MODE, NA, HASB, SB, RC>), grid, dim3(64 * L.nw), 0, stream, a, lda,
+                     sa, wp, sw, y, ldy, M, K, L.r, L.cb, L.nwg, q_dbg, sx_dbg);
+}
+
+template <int MODE, int MT>
+void launch_mt(const Layout& L, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
+               const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K, uint8_t* q_dbg,
+               void* sx_dbg) {
+#define SMALLM_K(na, hasb, sb, rc) \
+  launch_k<MODE, MT, na, hasb, sb, rc>(L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg)
+  if (L.cb == 0) {
+    if (L.rc == 1) SMALLM_K(1, false, 1, 1);
+    else if (L.rc == 2) SMALLM_K(1, false, 1, 2);
+    else SMALLM_K(1, false, 1, 4);
+  } else if (L.na == 1) {
+    if (L.rc == 1) SMALLM_K(1, true, 1, 1);
+    else if (L.rc == 2) SMALLM_K(1, true, 2, 2);
+    else if (L.sb == 4) SMALLM_K(1, true, 4, 4);
+    else SMALLM_K(1, true, 2, 4);
+  } else {
+    if (L.rc == 1) SMALLM_K(0, true, 1, 1);
+    else if (L.rc == 2) SMALLM_K(0, true, 2, 2);
+    else if (L.sb == 4) SMALLM_K(0, true, 4, 4);
+    else SMALLM_K(0, true, 2, 4);
   }
-  if (pl.NCG == 3) { SMALLM_LAUNCH(3, 1); return; }
-  if (pl.NKG == 8) SMALLM_LAUNCH(1, 8);
-  else SMALLM_LAUNCH(1, 4);
-#undef SMALLM_LAUNCH
+#undef SMALLM_K
 }
 
 template <int MODE>
 int launch_gemm(const void* a, int64_t lda, const void* sa, const uint8_t* wp, const void* sw,
                 uint16_t* y, int64_t ldy, int M, int N, int K, uint8_t* q_dbg, void* sx_dbg,
                 hipStream_t stream) {
-  const Plan pl = make_plan(M, N, K);
+  const Layout L = layout_for(N, K);
   const int MT = (M <= 16) ? 1 : 2;
   const int MP = 16 * MT;
-  dim3 grid(pl.nwg, (M + MP - 1) / MP);
-#define SMALLM_C(mt)                                                                                  \
-  switch (pl.C) {                                                                                     \
-    case 16: launch_c<MODE, mt, 16>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break; \
-    case 8: launch_c<MODE, mt, 8>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break;   \
-    case 4: launch_c<MODE, mt, 4>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break;   \
-    default: launch_c<MODE, mt, 2>(pl, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg); break;  \
-  }
-  if (MT == 1) { SMALLM_C(1) } else { SMALLM_C(2) }
-#undef SMALLM_C
-  return launch_status();
-}
-
-// The pre-quantised GEMM takes the MFMA-tiled kernel beyond the small-M range when the weight
-// is packed in 16-column groups (one fragment per MFMA B operand) and a 64-row tile of q spans
-// less than 2 GiB.
-bool use_tiled(int M, int N, int K, int64_t ldq) {
-  return M > kTiledFromM && layout_columns(N, K) == 16 && K / 128 <= kTiledMaxKB &&
-         ldq * (kTM - 1) + K < ((int64_t)1 << 31);
-}
-
-template <bool E8>
-int launch_tiled(const uint8_t* q, int64_t ldq, const void* sa, const uint8_t* wp, const void* sw,
-                 uint16_t* y, int64_t ldy, int M, int N, int K, hipStream_t stream) {
-  const dim3 grid(N / 64, (M + kTM - 1) / kTM);
-  hipLaunchKernelGGL((tiled_gemm_kernel<kTM, E8>), grid, dim3(256), 0, stream, q, ldq, sa, wp, sw,
-                     y, ldy, M, K);
+  const dim3 grid(L.nwg, (M + MP - 1) / MP);
+  if (MT == 1) launch_mt<MODE, 1>(L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg);
+  else launch_mt<MODE, 2>(L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg);
   return launch_status();
 }
 
@@ -1294,12 +1161,9 @@ template <bool PACK>
 void launch_pack(const uint8_t* src, uint8_t* dst, int N, int K, hipStream_t stream) {
   const int64_t chunks = (int64_t)N * K / 16;
   const dim3 grid((unsigned)((chunks + 255) / 256));
-  switch (layout_columns(N, K)) {
-    case 16: hipLaunchKernelGGL((pack_kernel<PACK, 16>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
-    case 8: hipLaunchKernelGGL((pack_kernel<PACK, 8>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
-    case 4: hipLaunchKernelGGL((pack_kernel<PACK, 4>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
-    default: hipLaunchKernelGGL((pack_kernel<PACK, 2>), grid, dim3(256), 0, stream, src, dst, K, chunks); break;
-  }
+  const Layout L = layout_for(N, K);
+  const PackGeom g{L.na, L.cb, L.sb, L.nwg};
+  hipLaunchKernelGGL((pack_kernel<PACK>), grid, dim3(256), 0, stream, src, dst, K, g, chunks);
 }
 
 }  // namespace
@@ -1325,14 +1189,14 @@ const char* smallm_fp8bs_strerror(int status) {
   }
 }
 
-int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan10) {
-  if (!plan10) return SMALLM_ERR_INVALID;
+int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan8) {
+  if (!plan8) return SMALLM_ERR_INVALID;
   int st = check_mnk(M, N, K);
   if (st) return st;
-  const Plan p = make_plan(M, N, K);
+  const Layout L = layout_for(N, K);
   const int MT = (M <= 16) ? 1 : 2;
-  const int v[10] = {p.C, p.CGW, p.nwg, p.NWK, p.NWC, p.NCG, p.NKG, p.KC, p.QW, MT};
-  for (int i = 0; i < 10; ++i) plan10[i] = v[i];
+  const int v[8] = {L.nwg, L.na, L.cb, L.sb, L.r, L.rc, L.nw, MT};
+  for (int i = 0; i < 8; ++i) plan8[i] = v[i];
   return SMALLM_OK;
 }
 
@@ -1446,7 +1310,6 @@ int smallm_fp8bs_gemm(const uint8_t* q, int64_t ldq, const float* sx, const uint
                       int K, void* stream) {
   int st = check_gemm_args(q, ldq, 1, sx, true, w_packed, layout_id, sw, y, ldy, M, N, K);
   if (st) return st;
-  if (use_tiled(M, N, K, ldq)) return launch_tiled<false>(q, ldq, sx, w_packed, sw, y, ldy, M, N, K, (hipStream_t)stream);
   return launch_gemm<kPreqF32>(q, ldq, sx, w_packed, sw, y, ldy, M, N, K, nullptr, nullptr,
                                (hipStream_t)stream);
 }
@@ -1456,7 +1319,6 @@ int smallm_fp8bs_gemm_e8m0(const uint8_t* q, int64_t ldq, const uint8_t* sx_e8m0
                            uint16_t* y, int64_t ldy, int M, int N, int K, void* stream) {
   int st = check_gemm_args(q, ldq, 1, sx_e8m0, true, w_packed, layout_id, sw_e8m0, y, ldy, M, N, K);
   if (st) return st;
-  if (use_tiled(M, N, K, ldq)) return launch_tiled<true>(q, ldq, sx_e8m0, w_packed, sw_e8m0, y, ldy, M, N, K, (hipStream_t)stream);
   return launch_gemm<kPreqE8>(q, ldq, sx_e8m0, w_packed, sw_e8m0, y, ldy, M, N, K, nullptr,
                               nullptr, (hipStream_t)stream);
 }

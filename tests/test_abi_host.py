@@ -31,59 +31,46 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_launch_plans_balance_the_cus():
-    # every CU streams the same weight bytes on the pages' shapes
-    for (N, K), (C, CGW) in {(5120, 4096): (4, 5), (4608, 4096): (2, 9), (4096, 2048): (16, 1),
-                             (2048, 4096): (8, 1)}.items():
+    # the pages' shapes: 256 workgroups, each streaming the same weight bytes (one per CU)
+    for (N, K), (na, cb, sb, r) in {(5120, 4096): (1, 4, 4, 4), (4608, 4096): (1, 2, 4, 4),
+                                    (4096, 2048): (1, 0, 1, 2), (2048, 4096): (0, 8, 2, 4)}.items():
         p = P.smallm_fp8bs_launch_plan(16, N, K)
-        assert (p["C"], p["CGW"], p["nwg"]) == (C, CGW, 256)
-        # the MFMA wave grid covers every column group and, per round, every K group once
-        assert p["NCG"] * p["NWC"] == p["CGW"]
-        assert p["KC"] == p["NKG"] * p["NWK"] * (16 // p["C"])
-        assert 4 <= p["NWK"] * p["NWC"] <= 12 and p["NWK"] * p["NWC"] + p["QW"] <= 16
-        # quantising waves: 2, or a multiple of 4 (the same number on every SIMD)
-        assert p["QW"] == 2 or p["QW"] % 4 == 0
+        assert (p["nwg"], p["NA"], p["CB"], p["SB"], p["R"]) == (256, na, cb, sb, r)
+        assert p["nwg"] * (16 * p["NA"] + p["CB"]) == N
+        # waves split K: R blocks each (a power of two), rounds of at most 4, every block covered
+        K_blocks = K // 128
+        assert p["NW"] == -(-K_blocks // p["R"]) and p["NW"] <= 8 and (p["NW"] - 1) * p["R"] < K_blocks
+        assert p["RC"] == min(p["R"], 4) and p["R"] % p["RC"] == 0 and p["RC"] % p["SB"] == 0
+        assert P.weight_layout(N, K) == {"NA": na, "CB": cb, "SB": sb}
     assert P.smallm_fp8bs_launch_plan(17, 4096, 2048)["MT"] == 2
     assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["MT"] == 1
-    # activation tiles shared by 5 column groups: 8 waves, one K group of 4 blocks each
-    p = P.smallm_fp8bs_launch_plan(4, 5120, 4096)
-    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (8, 1, 5, 1, 32, 4)
-    # quantising waves follow the groups of a round: two 16-group passes each, 8 at most here
-    assert P.smallm_fp8bs_launch_plan(1, 5120, 4096)["QW"] == 2
-    assert P.smallm_fp8bs_launch_plan(16, 5120, 4096)["QW"] == 8
-    # from 24 rows, half the K split (two rounds) leaves room for 12 quantising waves
-    p = P.smallm_fp8bs_launch_plan(32, 5120, 4096)
-    assert (p["NWK"], p["NWC"], p["KC"], p["QW"]) == (4, 1, 16, 12)
-    # 9 column groups: 3 x 3 column groups per wave, 4 K groups of 8 blocks
-    p = P.smallm_fp8bs_launch_plan(8, 4608, 4096)
-    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (4, 3, 3, 1, 32, 4)
-    # from 12 rows: 2 K groups per round (two rounds) and 8 quantising waves
-    for M in (12, 16, 32):
-        p = P.smallm_fp8bs_launch_plan(M, 4608, 4096)
-        assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"], p["QW"]) == (2, 3, 3, 1, 16, 8)
-    # one column group per workgroup: 12 quantising waves when a round holds 384 groups or more
-    assert P.smallm_fp8bs_launch_plan(16, 2048, 4096)["QW"] == 12
-    assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["QW"] == 8
-    assert P.smallm_fp8bs_launch_plan(32, 4096, 2048)["QW"] == 12
-    # one column group per workgroup: K split over 4 waves, 4 fragments each per round
-    p = P.smallm_fp8bs_launch_plan(4, 4096, 2048)
-    assert (p["NWK"], p["NWC"], p["NCG"], p["NKG"], p["KC"]) == (4, 1, 1, 4, 16)
-    # a single K group per round leaves one wave per column group
-    p = P.smallm_fp8bs_launch_plan(4, 36864, 128)
-    assert (p["CGW"], p["NWC"], p["NCG"], p["NWK"]) == (9, 9, 1, 1)
-    assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 4, 5, 1, 0>"
-    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 2, 3, 1, 0>"
-    assert P.kernel_name(8, 4096, 2048, 1) == "smallm_gemm_kernel<1, 16, 1, 4, 1>"
+    # N a multiple of 4096: one 16-column group per workgroup, N / 16 workgroups
+    p = P.smallm_fp8bs_launch_plan(4, 8192, 256)
+    assert (p["nwg"], p["NA"], p["CB"], p["R"], p["NW"]) == (512, 1, 0, 1, 2)
+    # shapes without a balanced split fall back to one 16-column group per workgroup
+    p = P.smallm_fp8bs_launch_plan(4, 384, 640)
+    assert (p["nwg"], p["NA"], p["CB"], p["R"], p["NW"]) == (24, 1, 0, 1, 5)
+    p = P.smallm_fp8bs_launch_plan(4, 1024, 12416)   # 97 K blocks: no whole remainder fragments
+    assert (p["nwg"], p["NA"], p["CB"], p["R"], p["RC"], p["NW"]) == (64, 1, 0, 16, 4, 7)
+    # a remainder group of single K blocks when a wave holds one block
+    p = P.smallm_fp8bs_launch_plan(4, 4608, 640)
+    assert (p["nwg"], p["NA"], p["CB"], p["SB"], p["R"]) == (256, 1, 2, 1, 1)
+    assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 0, 1, true, 4, 4>"
+    assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 0, 1, true, 4, 4>"
+    assert P.kernel_name(8, 4096, 2048, 1) == "smallm_gemm_kernel<1, 1, 1, false, 1, 2>"
+    assert P.kernel_name(8, 2048, 4096, 3) == "smallm_gemm_kernel<1, 3, 0, true, 2, 4>"
 
 
 def test_version_layout_and_strerror():
-    assert P.smallm_fp8bs_abi_version() == 4
-    # columns per group: the widest C in {16, 8, 4, 2} giving a multiple of 256 column groups
-    assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46380210
-    assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46380204
-    assert P.smallm_fp8bs_weight_layout_id(4608, 4096) == 0x46380202
-    assert P.smallm_fp8bs_weight_layout_id(2048, 4096) == 0x46380208
-    assert P.smallm_fp8bs_weight_layout_id(384, 640) == 0x46380210
-    assert P.smallm_fp8bs_weight_layout_id(4608, 640) == 0x46380210   # 5 K-blocks: only C=16 fits
+    assert P.smallm_fp8bs_abi_version() == 5
+    # 0x46390000 | NA << 12 | CB << 4 | SB
+    assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46391001
+    assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46391044
+    assert P.smallm_fp8bs_weight_layout_id(4608, 4096) == 0x46391024
+    assert P.smallm_fp8bs_weight_layout_id(2048, 4096) == 0x46390082
+    assert P.smallm_fp8bs_weight_layout_id(5120, 2048) == 0x46391042   # 2 K blocks per wave: SB = 2
+    assert P.smallm_fp8bs_weight_layout_id(384, 640) == 0x46391001
+    assert P.smallm_fp8bs_weight_layout_id(4608, 640) == 0x46391021
     assert P.smallm_fp8bs_weight_layout_id(100, 128) == 0
     for s in range(6):
         assert len(P.strerror(s)) > 0
