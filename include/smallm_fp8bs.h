@@ -55,6 +55,7 @@ extern "C" {
 #define SMALLM_FP8BS_MOE_MAX_E 4096      /* experts */
 #define SMALLM_FP8BS_MOE_MAX_H 16384     /* hidden size */
 #define SMALLM_FP8BS_MOE_MAX_I 2048      /* intermediate size per expert */
+#define SMALLM_FP8BS_MOE_NOALLOC_MAX_BYTES ((size_t)4 << 20) /* workspace of smallm_fp8bs_moe_noalloc */
 
 typedef enum {
   SMALLM_OK = 0,
@@ -256,6 +257,22 @@ int smallm_fp8bs_moe(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, co
                      const uint8_t* w2_packed, const float* sw2, uint32_t layout_id, int E, int H,
                      int I, void* workspace, size_t workspace_bytes, uint16_t* y, int64_t ldy,
                      void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture that must not
+ * call hipMalloc, tight serving loops, harnesses that forbid allocation): smallm_fp8bs_moe with the
+ * workspace held in a static device array of SMALLM_FP8BS_MOE_NOALLOC_MAX_BYTES inside the
+ * library, one per GPU, kept until the process ends (its device address is looked up once per
+ * device, on the first call there).  The call allocates nothing.  Same arguments, formulas, limits
+ * and results as smallm_fp8bs_moe without the workspace, plus: SMALLM_ERR_SHAPE (before anything
+ * is enqueued) when smallm_fp8bs_moe_workspace_bytes(T, S, H, I) exceeds that size.  Every call on
+ * a GPU uses that GPU's one array, so calls that overlap on one GPU (several streams, several host
+ * threads) race and must be serialised by the caller; the array needs no initialisation between
+ * calls (the layer writes every byte it reads).  h is not returned. */
+int smallm_fp8bs_moe_noalloc(const uint16_t* x, int64_t ldx, const int32_t* topk_ids,
+                             const float* topk_w, int T, int S, const uint8_t* w13_packed,
+                             const float* sw13, const uint8_t* w2_packed, const float* sw2,
+                             uint32_t layout_id, int E, int H, int I, uint16_t* y, int64_t ldy,
+                             void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * The same MoE layer with MXFP4 expert weights

@@ -54,6 +54,7 @@ EXPORTS = (
     "smallm_fp8bs_moe_workspace_bytes",
     "smallm_fp8bs_moe_splits",
     "smallm_fp8bs_moe",
+    "smallm_fp8bs_moe_noalloc",
     "smallm_fp8bs_moe_mxfp4_layout_id",
     "smallm_fp8bs_moe_mxfp4_pack",
     "smallm_fp8bs_moe_mxfp4_unpack",
@@ -123,6 +124,7 @@ def lib():
         "smallm_fp8bs_moe_workspace_bytes": (ctypes.c_size_t, [I, I, I, I]),
         "smallm_fp8bs_moe_splits": (I, [I, I]),
         "smallm_fp8bs_moe": (I, [P, I64, P, P, I, I, P, P, P, P, U32, I, I, I, P, ctypes.c_size_t, P, I64, P]),
+        "smallm_fp8bs_moe_noalloc": (I, [P, I64, P, P, I, I, P, P, P, P, U32, I, I, I, P, I64, P]),
         "smallm_fp8bs_moe_mxfp4_layout_id": (U32, []),
         "smallm_fp8bs_moe_mxfp4_pack": (I, [P, P, P, P, I, I, I, I, P]),
         "smallm_fp8bs_moe_mxfp4_unpack": (I, [P, P, P, P, I, I, I, I, P]),
@@ -538,6 +540,28 @@ def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, work
                                   _ptr(sw13), _ptr(w2_packed), _ptr(sw2), lid, E, H, I, _ptr(workspace),
                                   workspace.numel(), _ptr(y), y.stride(0), _stream(stream)), "smallm_fp8bs_moe")
     return y, moe_h_view(workspace, T, S, I)
+
+
+MOE_NOALLOC_MAX_BYTES = 4 << 20
+
+
+def smallm_fp8bs_moe_noalloc(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, y=None, layout_id=None,
+                             stream=None):
+    """smallm_fp8bs_moe with the library's own static workspace (the C entry point allocates
+    nothing; pass y to avoid the output allocation here too).  Returns y."""
+    T, S, E, H, I = _moe_common(x, topk_ids, topk_w, w13_packed, w2_packed, False)
+    for t_, n_, shp in ((sw13, "sw13", (E, 2 * I // 128, H // 128)), (sw2, "sw2", (E, H // 128, I // 128))):
+        if not isinstance(t_, torch.Tensor) or t_.dtype != torch.float32 or tuple(t_.shape) != shp:
+            raise ValueError(f"{n_} must be float32 {shp}")
+        if not t_.is_cuda:
+            raise ValueError(f"{n_} must be a device tensor")
+        _contig(t_, n_)
+    y = _out(y, T, H, x.device)
+    lid = smallm_fp8bs_moe_layout_id() if layout_id is None else layout_id
+    _check(lib().smallm_fp8bs_moe_noalloc(_ptr(x), x.stride(0), _ptr(topk_ids), _ptr(topk_w), T, S,
+                                          _ptr(w13_packed), _ptr(sw13), _ptr(w2_packed), _ptr(sw2), lid, E, H, I,
+                                          _ptr(y), y.stride(0), _stream(stream)), "smallm_fp8bs_moe_noalloc")
+    return y
 
 
 # ---------------------------------------------------------------------------------------------

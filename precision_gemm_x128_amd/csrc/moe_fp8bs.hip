@@ -40,6 +40,8 @@
 //    v_cvt_scalef32_pk_bf16_fp4 applies that power of two while converting (exact).
 
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <limits.h>
 #include <stdint.h>
 
@@ -694,6 +696,42 @@ int moe_call(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, const floa
   return launch_status();
 }
 
+// ---------------------------------------------------------------------------------------------
+// allocation-free variant: the workspace in a static device array
+// ---------------------------------------------------------------------------------------------
+
+constexpr size_t kMoeScratchBytes = SMALLM_FP8BS_MOE_NOALLOC_MAX_BYTES;  // largest workspace the variant takes
+constexpr int kMaxDevices = 64;
+
+// Each GPU the library runs on holds its own copy until the process ends.  In host code this name
+// is a host-side stand-in, never a device address: the per-device address comes from
+// hipGetSymbolAddress below.
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` runs on, looked up once per device with
+// that device current.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SMALLM_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return SMALLM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SMALLM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SMALLM_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return SMALLM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SMALLM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -740,6 +778,25 @@ int smallm_fp8bs_moe(const uint16_t* x, int64_t ldx, const int32_t* topk_ids, co
   return moe_call<false>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, nullptr, w2_packed, sw2,
                          nullptr, layout_id, kMoeLayoutId, E, H, I, workspace, workspace_bytes, y,
                          ldy, stream);
+}
+
+int smallm_fp8bs_moe_noalloc(const uint16_t* x, int64_t ldx, const int32_t* topk_ids,
+                             const float* topk_w, int T, int S, const uint8_t* w13_packed,
+                             const float* sw13, const uint8_t* w2_packed, const float* sw2,
+                             uint32_t layout_id, int E, int H, int I, uint16_t* y, int64_t ldy,
+                             void* stream) {
+  if (!sw13 || !sw2) return SMALLM_ERR_INVALID;
+  if (((uintptr_t)sw13 & 3u) || ((uintptr_t)sw2 & 3u)) return SMALLM_ERR_ALIGN;
+  const int st = smallm_fp8bs_moe_supported(T, S, E, H, I);
+  if (st) return st;
+  const size_t need = moe_workspace_bytes(T, S, H, I);
+  if (need > kMoeScratchBytes) return SMALLM_ERR_SHAPE;
+  void* ws = nullptr;
+  const int sst = scratch_for_stream((hipStream_t)stream, &ws);
+  if (sst) return sst;
+  return moe_call<false>(x, ldx, topk_ids, topk_w, T, S, w13_packed, sw13, nullptr, w2_packed, sw2,
+                         nullptr, layout_id, kMoeLayoutId, E, H, I, ws, kMoeScratchBytes, y, ldy,
+                         stream);
 }
 
 uint32_t smallm_fp8bs_moe_mxfp4_layout_id(void) { return kMoeFp4LayoutId; }
