@@ -88,10 +88,10 @@ int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx);
 
 /* Host-only description of the launch the GEMM entry points make for (M, N, K), for tools and
  * benchmarks.  plan8 receives, in order: the number of workgroups along N, NA, CB and SB (the
- * packed layout, as in smallm_fp8bs_weight_layout_id), R (K blocks per wave), RC (K blocks per
- * round of a wave), the waves per workgroup and MT (16-row M tiles per workgroup; M above 32
- * runs in 32-row chunks along the grid's second dimension).  Returns SMALLM_OK or the shape
- * error. */
+ * packed layout, as in smallm_fp8bs_weight_layout_id), R (K blocks per K range), RC (K blocks
+ * per round), NW (K ranges per workgroup; each range has an MFMA wave and a quantising wave, so
+ * a workgroup has 128 * NW threads) and MT (16-row M tiles per workgroup; M above 32 runs in
+ * 32-row chunks along the grid's second dimension).  Returns SMALLM_OK or the shape error. */
 int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan8);
 
 /* --------------------------------------------------------------------------------------------

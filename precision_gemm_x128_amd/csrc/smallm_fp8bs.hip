@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
 
 enum Mode { kFusedF32 = 0, kFusedE8 = 1, kPreqF32 = 2, kPreqE8 = 3 };
 
-constexpr int kMaxWaves = 8;  // waves per workgroup
+constexpr int kMaxWaves = 8;  // K ranges per workgroup (an MFMA wave and a quantising wave each)
 
 template <int MT, int RC, int MODE>
 struct GemmCfg {
@@ -532,7 +532,10 @@ struct GemmCfg {
   static constexpr int kSts = RC * kMP * 4;              // their scales (fp32, or e8m0 bytes)
   static constexpr int kRed = 2 * MT * 4 * 64 * 4;       // one wave's partial sums (both groups)
   static constexpr int kWave = ((kStq + kSts > kRed ? kStq + kSts : kRed) + 15) / 16 * 16;
-  static constexpr int kSmem = kMaxWaves * kWave;
+  // one 16-row tile: up to 8 K ranges; two tiles: up to 4 ranges of twice the blocks (512 threads,
+  // so that each wave has 256 registers)
+  static constexpr int kRanges = MT == 1 ? kMaxWaves : kMaxWaves / 2;
+  static constexpr int kSmem = kRanges * kWave;
 };
 
 // A wave-uniform fp32 value loaded through the scalar cache.
@@ -547,25 +550,41 @@ __device__ __forceinline__ float dpp_f32_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
 }
 
-// One workgroup per column share of the packed layout (one per CU for the pages' shapes).  Wave w
-// owns K blocks [w R, w R + R) of both of the workgroup's column groups and runs over them in
-// rounds of RC blocks:
-//   1. it loads the activation rows of the round's K blocks (bf16, or pre-quantised bytes and
-//      scales), then issues every weight fragment of the round as non-temporal 16-byte buffer
-//      loads, the activation loads first so that they are not queued behind the weight stream;
-//   2. it quantises the rows itself, a DPP quad of lanes per 1x128 group with 16 groups per pass
-//      (row-major over the round's K blocks, so that one pass covers 16 / RC rows), and stages the
-//      e4m3 bytes and scales in its own part of LDS; no other wave reads them, so there is no
-//      workgroup barrier before the MFMAs;
-//   3. each fragment is consumed as soon as its own loads have landed: a 16-column fragment is one
-//      16x16x128 MFMA per M tile; a remainder fragment (CB columns x SB K blocks) is SB MFMAs on
-//      the same accumulator, the B operand masked so that MFMA s only sees the B columns of K block
-//      s (exact: the other columns contribute zero).
-// fp32 scales: each K block's (or each lane's K block's) partial is multiplied by
-// x_scale * w_scale into the accumulator; e8m0 scales are the MFMA's own scale operands.  The waves'
-// partial sums meet once in LDS, summed in wave order.
+// LDS-only release / acquire between the waves of a workgroup: only LDS accesses are ordered, so
+// the fences wait for the LDS counter alone, never for loads in flight from memory.
+__device__ __forceinline__ void lds_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local"); }
+__device__ __forceinline__ void lds_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); }
+__device__ __forceinline__ void flag_set(uint32_t* f, uint32_t v) {
+  lds_release();
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void flag_wait(uint32_t* f, uint32_t v) {
+  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < v) __builtin_amdgcn_s_sleep(1);
+  lds_acquire();
+}
+
+// One workgroup per column share of the packed layout (one per CU for the pages' shapes).  K is
+// split into NW ranges of R blocks.  Each range has two waves, an MFMA wave (wave r) and a
+// quantising wave (wave NW + r), and both walk it in rounds of RC blocks:
+//   * the quantising wave loads the activation rows of the round's K blocks (bf16, or
+//     pre-quantised bytes and scales), quantises them (a DPP quad of lanes per 1x128 group, 16
+//     groups per pass, row-major over the round's K blocks, so one pass covers 16 / RC rows),
+//     stages the e4m3 bytes and scales in the range's part of LDS and raises the range's flag.  It
+//     runs at a higher wave priority, so that its VALU work issues ahead of the MFMA waves' on its
+//     SIMD;
+//   * the MFMA wave issues the round's weight block scales (scalar loads) and fragments
+//     (non-temporal 16-byte buffer loads, the remainder fragments first), waits for the flag, and
+//     consumes each fragment as soon as its loads have landed: a 16-column fragment is one
+//     16x16x128 MFMA per M tile; a remainder fragment (CB columns x SB K blocks) is SB MFMAs, the B
+//     operand masked so that MFMA s only sees the B columns of K block s (exact: the other columns
+//     contribute zero).
+// The two waves of a range meet only through its flags (ready: the round is staged; consumed: the
+// staging area may be reused), so the weight stream never waits for the quantiser and the
+// quantiser never waits for weight loads to be issued.  fp32 scales: each K block's partial is
+// multiplied by x_scale * w_scale into the accumulator; e8m0 scales are the MFMA's own scale
+// operands.  The MFMA waves' partial sums meet once in LDS, summed in range order.
 template <int MT, int MODE, int NA, bool HASB, int SB, int RC>
-__global__ __launch_bounds__(512) void smallm_gemm_kernel(
+__global__ __launch_bounds__(MT == 1 ? 1024 : 512) void smallm_gemm_kernel(
     const void* __restrict__ a_src, int64_t lda, const void* __restrict__ sa_src,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
     int64_t ldy, int M, int K, int R, int CB, int NWG, uint8_t* __restrict__ q_dbg,
@@ -578,130 +597,303 @@ __global__ __launch_bounds__(512) void smallm_gemm_kernel(
   constexpr int NFB = HASB ? RC / SB : 1;  // remainder fragments per round
   static_assert(!HASB || (RC % SB == 0), "a round holds whole remainder fragments");
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
+  __shared__ uint32_t ready[kMaxWaves], consumed[kMaxWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwaves = blockDim.x >> 6;
+  const int NW = blockDim.x >> 7;  // K ranges (two waves each)
   const int KB = K >> 7;
   const int wg = blockIdx.x;
   const int m0 = blockIdx.y * MP;
   const int Mc = min(M - m0, MP);
-  uint8_t* stq = smem + wave * Cfg::kWave;
+  const bool mfma_wave = wave < NW;
+  const int rg = mfma_wave ? wave : wave - NW;  // this wave's K range
+  uint8_t* stq = smem + rg * Cfg::kWave;
   float* sts_f = (float*)(stq + Cfg::kStq);
   uint8_t* sts_b = stq + Cfg::kStq;
-
-  // this workgroup's packed bytes: the 16-column fragments, then the remainder fragments
-  const int cols = 16 * NA + CB;
-  const uint8_t* wreg = wp + (int64_t)wg * cols * K;
-  const uint32_t abytes = (uint32_t)(NA * KB) * 2048u;
-  const int NB = HASB ? CB * SB : 16;       // B columns of a remainder fragment
-  const uint32_t fbytes = (uint32_t)NB * 128u;
-  const uint32_t bbytes = HASB ? (uint32_t)(KB / SB) * fbytes : 0u;
-  const __amdgpu_buffer_rsrc_t wrA = __builtin_amdgcn_make_buffer_rsrc((void*)wreg, 0, (int)abytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t wrB = __builtin_amdgcn_make_buffer_rsrc((void*)(wreg + abytes), 0, (int)bbytes, 0x00020000);
-  const int nbA = (16 * wg) >> 7;                      // 128-column block of the 16-column group
-  const int nbB = (16 * NA * NWG + CB * wg) >> 7;      // and of the remainder group
-
-  const int kw0 = wave * R;
+  const int kw0 = rg * R;
   const int kw1 = min(kw0 + R, KB);
+  const int cols = 16 * NA + CB;
 
-  // activations of the row chunk as a bounds-checked buffer (idle lanes read zeros past its end)
-  const uint32_t xbytes = (uint32_t)((int64_t)(Mc - 1) * lda * rowb + (int64_t)K * rowb);
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a_src + (int64_t)m0 * lda * rowb), 0, (int)xbytes, 0x00020000);
-  const uint32_t sbytes_x = (uint32_t)(Mc * KB) * (Cfg::kE8 ? 1u : 4u);
-  const __amdgpu_buffer_rsrc_t sxr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)sa_src + (int64_t)m0 * KB * (Cfg::kE8 ? 1 : 4)), 0, (int)sbytes_x, 0x00020000);
-  const uint32_t swbytes = Cfg::kE8 ? (uint32_t)((cols * NWG / 128) * KB) : 0u;  // the whole [N/128, K/128] array
-  const __amdgpu_buffer_rsrc_t swr = __builtin_amdgcn_make_buffer_rsrc((void*)sw, 0, (int)swbytes, 0x00020000);
-
-  v4f accA[MT], accA2[MT], accB[MT], accB2[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    accA[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    accA2[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    accB[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    accB2[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  if (tid < kMaxWaves) {
+    ready[tid] = 0;
+    consumed[tid] = 0;
   }
+  __syncthreads();  // the flags are cleared (before any load is issued)
 
-  for (int kr = kw0; kr < kw1; kr += RC) {
-    // the lane index, formed afresh in every round where the compiler cannot see through it, so
-    // that lane-derived addresses are computed inside the round instead of held in registers
-    // across it (a spill reload would wait for every load in flight)
-    int ln;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    const int nk = min(RC, kw1 - kr);   // K blocks of this round; the others are masked
-    const int G = Mc * RC;              // groups of the round (row-major over its K blocks)
-    const int grp = ln >> 2, c = ln & 3;
-    const int jl = ln & 15;                 // B column of this lane
-    const int sl = jl & (SB - 1);           // its K block within a remainder fragment
-    const bool bcol = jl < NB;
-    const uint32_t boff = (uint32_t)(((ln >> 4) * NB + jl) * 16);
-
-    // ---- 1. activation loads, then the weight stream ----
-    // weight block scales of the round's K blocks, first in the queue (index clamped into the row:
-    // blocks past the wave's range multiply zero weights)
-    float swA[RC], swB[RC];
-    int ewA[RC], ewB[RC];
+  if (mfma_wave) {
+    // ---- MFMA wave: the weight stream of the range and its MFMAs ----
+    v4f accA[MT], accA2[MT], accB[MT], accB2[MT];
 #pragma unroll
-    for (int i = 0; i < RC; ++i) {
-      const int kb = min(kr + i, KB - 1);
-      if (!Cfg::kE8) {
-        swA[i] = NA ? sload_f32((const float*)sw + nbA * KB + kb) : 0.0f;
-        swB[i] = HASB ? sload_f32((const float*)sw + nbB * KB + kb) : 0.0f;
-      } else {
-        ewA[i] = NA ? __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b8(swr, (uint32_t)(nbA * KB + kb), 0, 0)) : 0;
-        ewB[i] = HASB ? __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b8(swr, (uint32_t)(nbB * KB + kb), 0, 0)) : 0;
+    for (int mt = 0; mt < MT; ++mt) {
+      accA[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      accA2[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      accB[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      accB2[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const uint8_t* wreg = wp + (int64_t)wg * cols * K;
+    const uint32_t abytes = (uint32_t)(NA * KB) * 2048u;
+    const int NB = HASB ? CB * SB : 16;       // B columns of a remainder fragment
+    const uint32_t fbytes = (uint32_t)NB * 128u;
+    const uint32_t bbytes = HASB ? (uint32_t)(KB / SB) * fbytes : 0u;
+    const __amdgpu_buffer_rsrc_t wrA = __builtin_amdgcn_make_buffer_rsrc((void*)wreg, 0, (int)abytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrB = __builtin_amdgcn_make_buffer_rsrc((void*)(wreg + abytes), 0, (int)bbytes, 0x00020000);
+    const int nbA = (16 * wg) >> 7;                      // 128-column block of the 16-column group
+    const int nbB = (16 * NA * NWG + CB * wg) >> 7;      // and of the remainder group
+    const uint32_t swbytes = Cfg::kE8 ? (uint32_t)((cols * NWG / 128) * KB) : 0u;  // the whole [N/128, K/128] array
+    const __amdgpu_buffer_rsrc_t swr = __builtin_amdgcn_make_buffer_rsrc((void*)sw, 0, (int)swbytes, 0x00020000);
+    uint32_t rd = 0;
+    for (int kr = kw0; kr < kw1; kr += RC, ++rd) {
+      // the lane index, formed afresh in every round where the compiler cannot see through it, so
+      // that lane-derived addresses are computed inside the round instead of held in registers
+      // across it (a spill reload would wait for every load in flight)
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int nk = min(RC, kw1 - kr);   // K blocks of this round; the others are zero fragments
+      const int jl = ln & 15;             // B column of this lane
+      const int sl = jl & (SB - 1);       // its K block within a remainder fragment
+      const bool bcol = jl < NB;
+      const uint32_t boff = (uint32_t)(((ln >> 4) * NB + jl) * 16);
+      // weight block scales of the round's K blocks, first in the queue (index clamped into the row:
+      // blocks past the range multiply zero weights)
+      float swA[RC], swB[RC];
+      int ewA[RC], ewB[RC];
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        const int kb = min(kr + i, KB - 1);
+        if (!Cfg::kE8) {
+          swA[i] = NA ? sload_f32((const float*)sw + nbA * KB + kb) : 0.0f;
+          swB[i] = HASB ? sload_f32((const float*)sw + nbB * KB + kb) : 0.0f;
+        } else {
+          ewA[i] = NA ? __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b8(swr, (uint32_t)(nbA * KB + kb), 0, 0)) : 0;
+          ewB[i] = HASB ? __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_raw_buffer_load_b8(swr, (uint32_t)(nbB * KB + kb), 0, 0)) : 0;
+        }
+      }
+      // the remainder fragments first: every K block of the round has an MFMA on them
+      u32x4 wa[RC][2], wb[NFB][2];
+#pragma unroll
+      for (int f = 0; f < NFB; ++f) {
+        if (HASB) {
+          const uint32_t off = (f * SB < nk && bcol) ? (uint32_t)((kr / SB) + f) * fbytes + boff : bbytes;
+          wb[f][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, off, 0, 2));
+          wb[f][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, off + (fbytes >> 1), 0, 2));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        if (NA) {
+          const uint32_t off = (i < nk) ? (uint32_t)(kr + i) * 2048u + (uint32_t)ln * 16u : abytes;
+          wa[i][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, off, 0, 2));
+          wa[i][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, off + 1024u, 0, 2));
+        }
+      }
+      flag_wait(&ready[rg], rd + 1);  // the round's activations are staged
+      // A remainder fragment's MFMA for its K block s sees only the B columns of that block (the
+      // others are masked to zero), so in the fp32 modes its result is scaled like a 16-column
+      // fragment's: lanes of other K blocks hold exact zeros and add nothing.
+      auto tile = [&](int i, int mt, v8i& at, v4f& sx4, int& sa) {
+        const int row = mt * 16 + jl;
+        const u32x4* ap = (const u32x4*)(stq + (i * MP + row) * kRowStride + (ln >> 4) * 32);
+        const u32x4 a0 = ap[0], a1 = ap[1];
+        at = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        if (Cfg::kE8) sa = (int)sts_b[i * MP + row];
+        else sx4 = *(const v4f*)(sts_f + i * MP + mt * 16 + 4 * (ln >> 4));
+      };
+      // K block by K block: each activation tile is read from LDS once and feeds the remainder
+      // fragment's MFMA (the fragments issued first) and the 16-column fragment's
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        if (MT == 2) {  // one K block's tiles live at a time
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        v8i b = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        if (HASB) {
+          const int f = i / SB, s = i % SB;
+          b = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[f][0], wb[f][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (SB > 1) {
+            const uint32_t bmask = (sl == s) ? 0xFFFFFFFFu : 0u;  // lanes of K block s
+#pragma unroll
+            for (int d = 0; d < 8; ++d) b[d] = (int)((uint32_t)b[d] & bmask);
+          }
+        }
+        v8i a16 = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        if (NA) a16 = __builtin_bit_cast(v8i, __builtin_shufflevector(wa[i][0], wa[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v8i at;
+          v4f sx4;
+          int sa;
+          tile(i, mt, at, sx4, sa);
+          if (HASB) {
+            if (Cfg::kE8) {
+              v4f& acc = (i & 1) ? accB2[mt] : accB[mt];
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, acc, 0, 0, 0, sa, 0, ewB[i]);
+            } else {
+              const v4f fb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                              0, 0, 0, 127, 0, 127);
+              const float sc = swB[i];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) accB[mt][e] = __builtin_fmaf(sx4[e] * sc, fb[e], accB[mt][e]);
+            }
+          }
+          if (NA) {
+            if (Cfg::kE8) {
+              v4f& acc = (i & 1) ? accA2[mt] : accA[mt];
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, a16, acc, 0, 0, 0, sa, 0, ewA[i]);
+            } else {
+              const v4f fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, a16, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                              0, 0, 0, 127, 0, 127);
+              const float sc = swA[i];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) accA[mt][e] = __builtin_fmaf(sx4[e] * sc, fa[e], accA[mt][e]);
+            }
+          }
+        }
+      }
+      if (kr + RC < kw1) flag_set(&consumed[rg], rd + 1);  // the staging area may take the next round
+    }
+    // ---- the partial sums into the range's LDS (no longer read) ----
+    float* red = (float*)stq;
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    lds_release();
+    lds_acquire();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v4f pa = accA[mt];
+      if (Cfg::kE8) pa += accA2[mt];
+      v4f pb = accB[mt];
+      if (Cfg::kE8) pb += accB2[mt];
+      if (HASB && SB > 1) {
+        // the SB K-block partials of a remainder column sit in SB neighbouring lanes: fold them into
+        // the first, in a fixed order
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[e] += dpp_f32_xor1(pb[e]);
+          if (SB > 2) pb[e] += dpp_f32_xor2(pb[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (NA) red[((0 * MT + mt) * 4 + e) * 64 + lane] = pa[e];
+        if (HASB) red[((1 * MT + mt) * 4 + e) * 64 + lane] = pb[e];
       }
     }
-
-    u32x4 xv[NPASS][NV];
-    uint32_t xs[NPASS];
-    // activation loads of passes [P0, P1)
-    auto load_act = [&](auto P0c, auto P1c) {
-      constexpr int P0 = decltype(P0c)::value, P1 = decltype(P1c)::value;
+  } else {
+    // ---- quantising wave: the activations of the range, staged round by round ----
+    __builtin_amdgcn_s_setprio(3);
+    const uint32_t xbytes = (uint32_t)((int64_t)(Mc - 1) * lda * rowb + (int64_t)K * rowb);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)a_src + (int64_t)m0 * lda * rowb), 0, (int)xbytes, 0x00020000);
+    const uint32_t sbytes_x = (uint32_t)(Mc * KB) * (Cfg::kE8 ? 1u : 4u);
+    const __amdgpu_buffer_rsrc_t sxr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)sa_src + (int64_t)m0 * KB * (Cfg::kE8 ? 1 : 4)), 0, (int)sbytes_x, 0x00020000);
+    uint32_t rd = 0;
+    for (int kr = kw0; kr < kw1; kr += RC, ++rd) {
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int nk = min(RC, kw1 - kr);   // K blocks of this round; the others are staged as zeros
+      const int G = Mc * RC;              // groups of the round (row-major over its K blocks)
+      const int grp = ln >> 2, c = ln & 3;
+      u32x4 xv[NPASS][NV];
+      uint32_t xs[NPASS];
+      // activation loads of passes [P0, P1)
+      auto load_act = [&](int P0, int P1) {
 #pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        if (p < P0 || p >= P1) continue;
-        if (p * 16 < G) {
+        for (int p = 0; p < NPASS; ++p) {
+          if (p < P0 || p >= P1) continue;
+          if (p * 16 < G) {
+            const int g = p * 16 + grp;
+            const int m = g / RC, kbl = g & (RC - 1);
+            const bool valid = g < G && kbl < nk;
+            const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * 32) * rowb) : xbytes;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+              xv[p][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0));
+            if (Cfg::kPreq) {
+              const uint32_t so = valid ? (uint32_t)(m * KB + kr + kbl) * (Cfg::kE8 ? 1u : 4u) : sbytes_x;
+              xs[p] = Cfg::kE8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sxr, so, 0, 0)
+                               : __builtin_amdgcn_raw_buffer_load_b32(sxr, so, 0, 0);
+            }
+          }
+        }
+      };
+      // quantisation (or staging) of passes [P0, P1) into the range's LDS
+      auto quant_act = [&](int P0, int P1) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+          if (p < P0 || p >= P1) continue;
+          if (p * 16 < G) {
+            const int g = p * 16 + grp;
+            const int m = g / RC, kbl = g & (RC - 1);
+            u32x4 qv[2];
+            float sc = 0.0f;
+            uint32_t eb = 0;
+            if constexpr (!Cfg::kPreq) {
+              if constexpr (Cfg::kE8) eb = quant32_e8m0(xv[p], qv);
+              else sc = quant32_fp32(xv[p], qv);
+            } else {
+              qv[0] = xv[p][0];
+              qv[1] = xv[p][1];
+              if (Cfg::kE8) eb = xs[p];
+              else sc = __uint_as_float(xs[p]);
+            }
+            // K blocks past the range (a short last round) are staged too: their loads returned
+            // zeros, so the MFMAs on them see zero codes and scales instead of stale LDS
+            if (g < G) {
+              u32x4* dp = (u32x4*)(stq + (kbl * MP + m) * kRowStride + c * 32);
+              dp[0] = qv[0];
+              dp[1] = qv[1];
+              if (c == 0) {
+                if (Cfg::kE8) sts_b[kbl * MP + m] = (uint8_t)eb;
+                else sts_f[kbl * MP + m] = sc;
+              }
+            }
+          }
+        }
+      };
+      if constexpr (MT == 1) {
+        // one 16-row tile: every pass loaded up front
+        load_act(0, NPASS);
+        if (rd > 0) flag_wait(&consumed[rg], rd);  // the MFMA wave has read the previous round
+        quant_act(0, NPASS);
+      } else {
+        // two tiles: a loop with two passes in flight, each pass loaded while the one before it is
+        // quantised (the passes of a round would not fit in registers at once); passes past the
+        // round read zeros past the end of the buffer and are not staged
+        const int np = (G + 15) >> 4;
+        u32x4 xa[NV], xb[NV];
+        uint32_t sa_ = 0, sb_ = 0;
+        auto load1 = [&](int p, u32x4 (&v)[NV], uint32_t& sv) {
           const int g = p * 16 + grp;
           const int m = g / RC, kbl = g & (RC - 1);
           const bool valid = g < G && kbl < nk;
           const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * 32) * rowb) : xbytes;
 #pragma unroll
           for (int i = 0; i < NV; ++i)
-            xv[p][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0));
+            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0));
           if (Cfg::kPreq) {
             const uint32_t so = valid ? (uint32_t)(m * KB + kr + kbl) * (Cfg::kE8 ? 1u : 4u) : sbytes_x;
-            xs[p] = Cfg::kE8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sxr, so, 0, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b32(sxr, so, 0, 0);
+            sv = Cfg::kE8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sxr, so, 0, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b32(sxr, so, 0, 0);
           }
-        }
-      }
-    };
-    // quantisation (or staging) of passes [P0, P1) into this wave's LDS
-    auto quant_act = [&](auto P0c, auto P1c) {
-      constexpr int P0 = decltype(P0c)::value, P1 = decltype(P1c)::value;
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        if (p < P0 || p >= P1) continue;
-        if (p * 16 < G) {
+        };
+        auto quant1 = [&](int p, u32x4 (&v)[NV], uint32_t sv) {
           const int g = p * 16 + grp;
           const int m = g / RC, kbl = g & (RC - 1);
           u32x4 qv[2];
           float sc = 0.0f;
           uint32_t eb = 0;
           if constexpr (!Cfg::kPreq) {
-            if constexpr (Cfg::kE8) eb = quant32_e8m0(xv[p], qv);
-            else sc = quant32_fp32(xv[p], qv);
+            if constexpr (Cfg::kE8) eb = quant32_e8m0(v, qv);
+            else sc = quant32_fp32(v, qv);
           } else {
-            qv[0] = xv[p][0];
-            qv[1] = xv[p][1];
-            if (Cfg::kE8) eb = xs[p];
-            else sc = __uint_as_float(xs[p]);
+            qv[0] = v[0];
+            qv[1] = v[1];
+            if (Cfg::kE8) eb = sv;
+            else sc = __uint_as_float(sv);
           }
-          // K blocks past the wave's range (a short last round) are staged too: their loads
-          // returned zeros, so the MFMAs on them see zero codes and scales instead of stale LDS
           if (g < G) {
             u32x4* dp = (u32x4*)(stq + (kbl * MP + m) * kRowStride + c * 32);
             dp[0] = qv[0];
@@ -711,153 +903,37 @@ __global__ __launch_bounds__(512) void smallm_gemm_kernel(
               else sts_f[kbl * MP + m] = sc;
             }
           }
+        };
+        load1(0, xa, sa_);
+        load1(1, xb, sb_);
+        if (rd > 0) flag_wait(&consumed[rg], rd);  // the MFMA wave has read the previous round
+        for (int p = 0; p < np; p += 2) {
+          quant1(p, xa, sa_);
+          load1(p + 2, xa, sa_);
+          if (p + 1 < np) quant1(p + 1, xb, sb_);
+          load1(p + 3, xb, sb_);
         }
       }
-    };
-    using C0 = std::integral_constant<int, 0>;
-    using CH = std::integral_constant<int, NPASS / MT>;
-    using CN = std::integral_constant<int, NPASS>;
-    // MT = 2: the second 16-row tile is loaded after the first one is quantised (its registers
-    // would not fit beside the first tile's and the weights)
-    load_act(C0{}, CH{});
-    // the remainder fragments first: every K block of the round has an MFMA on them
-    u32x4 wa[RC][2], wb[NFB][2];
-#pragma unroll
-    for (int f = 0; f < NFB; ++f) {
-      if (HASB) {
-        const uint32_t off = (f * SB < nk && bcol) ? (uint32_t)((kr / SB) + f) * fbytes + boff : bbytes;
-        wb[f][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, off, 0, 2));
-        wb[f][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, off + (fbytes >> 1), 0, 2));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RC; ++i) {
-      if (NA) {
-        const uint32_t off = (i < nk) ? (uint32_t)(kr + i) * 2048u + (uint32_t)ln * 16u : abytes;
-        wa[i][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, off, 0, 2));
-        wa[i][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, off + 1024u, 0, 2));
-      }
-    }
-    // ---- 2. quantise (or stage) the round's activations into this wave's LDS ----
-    quant_act(C0{}, CH{});
-    if (MT == 2) {
-      load_act(CH{}, CN{});
-      quant_act(CH{}, CN{});
-    }
-    // the staged rows are read back by other lanes of this wave: LDS executes a wave's accesses
-    // in order, so only the compiler must not move the reads above the writes
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (!Cfg::kPreq && wg == 0 && (q_dbg != nullptr || sx_dbg != nullptr)) {
-      // debug copies of the bytes and scales this round used (workgroup 0 only), from the staging area
-      for (int t = ln; t < Mc * nk * 8; t += 64) {
-        const int row = t / (nk * 8), rem = t - row * nk * 8, kbl = rem >> 3, part = rem & 7;
-        if (q_dbg != nullptr)
-          *(u32x4*)(q_dbg + (int64_t)(m0 + row) * K + (kr + kbl) * 128 + part * 16) =
-              *(const u32x4*)(stq + (kbl * MP + row) * kRowStride + part * 16);
-        if (sx_dbg != nullptr && part == 0) {
-          if (Cfg::kE8) ((uint8_t*)sx_dbg)[(int64_t)(m0 + row) * KB + kr + kbl] = sts_b[kbl * MP + row];
-          else ((float*)sx_dbg)[(int64_t)(m0 + row) * KB + kr + kbl] = sts_f[kbl * MP + row];
-        }
-      }
-    }
-
-    // ---- 3. MFMAs: the remainder fragments' chains, then the 16-column fragments in K order, each
-    // as soon as its loads have landed ----
-    // A remainder fragment's MFMA for its K block s sees only the B columns of that block (the
-    // others are masked to zero), so in the fp32 modes its result is scaled like a 16-column
-    // fragment's: lanes of other K blocks hold exact zeros and add nothing.
-    auto tile = [&](int i, int mt, v8i& at, v4f& sx4, int& sa) {
-      const int row = mt * 16 + jl;
-      const u32x4* ap = (const u32x4*)(stq + (i * MP + row) * kRowStride + (ln >> 4) * 32);
-      const u32x4 a0 = ap[0], a1 = ap[1];
-      at = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-      if (Cfg::kE8) sa = (int)sts_b[i * MP + row];
-      else sx4 = *(const v4f*)(sts_f + i * MP + mt * 16 + 4 * (ln >> 4));
-    };
-    if (HASB) {
-#pragma unroll
-      for (int i = 0; i < RC; ++i) {
-        if (MT == 2) __builtin_amdgcn_sched_barrier(0);  // one K block's tiles live at a time
-        const int f = i / SB, s = i % SB;
-        v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[f][0], wb[f][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        if (SB > 1) {
-          const uint32_t bmask = (sl == s) ? 0xFFFFFFFFu : 0u;  // lanes of K block s
-#pragma unroll
-          for (int d = 0; d < 8; ++d) b[d] = (int)((uint32_t)b[d] & bmask);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v8i at;
-          v4f sx4;
-          int sa;
-          tile(i, mt, at, sx4, sa);
-          if (Cfg::kE8) {
-            v4f& acc = (i & 1) ? accB2[mt] : accB[mt];
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, acc, 0, 0, 0, sa, 0, ewB[i]);
-          } else {
-            const v4f fb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                            0, 0, 0, 127, 0, 127);
-            const float sc = swB[i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) accB[mt][e] = __builtin_fmaf(sx4[e] * sc, fb[e], accB[mt][e]);
+      if (!Cfg::kPreq && wg == 0 && (q_dbg != nullptr || sx_dbg != nullptr)) {
+        // debug copies of the bytes and scales this round used (workgroup 0 only), from the staging area
+        lds_release();
+        lds_acquire();
+        for (int t = ln; t < Mc * nk * 8; t += 64) {
+          const int row = t / (nk * 8), rem = t - row * nk * 8, kbl = rem >> 3, part = rem & 7;
+          if (q_dbg != nullptr)
+            *(u32x4*)(q_dbg + (int64_t)(m0 + row) * K + (kr + kbl) * 128 + part * 16) =
+                *(const u32x4*)(stq + (kbl * MP + row) * kRowStride + part * 16);
+          if (sx_dbg != nullptr && part == 0) {
+            if (Cfg::kE8) ((uint8_t*)sx_dbg)[(int64_t)(m0 + row) * KB + kr + kbl] = sts_b[kbl * MP + row];
+            else ((float*)sx_dbg)[(int64_t)(m0 + row) * KB + kr + kbl] = sts_f[kbl * MP + row];
           }
         }
       }
+      flag_set(&ready[rg], rd + 1);
     }
-    if (NA) {
-#pragma unroll
-      for (int i = 0; i < RC; ++i) {
-        if (MT == 2) __builtin_amdgcn_sched_barrier(0);
-        const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wa[i][0], wa[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v8i at;
-          v4f sx4;
-          int sa;
-          tile(i, mt, at, sx4, sa);
-          if (Cfg::kE8) {
-            v4f& acc = (i & 1) ? accA2[mt] : accA[mt];
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, acc, 0, 0, 0, sa, 0, ewA[i]);
-          } else {
-            const v4f fa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, b, v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                            0, 0, 0, 127, 0, 127);
-            const float sc = swA[i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) accA[mt][e] = __builtin_fmaf(sx4[e] * sc, fa[e], accA[mt][e]);
-          }
-        }
-      }
-    }
+    __builtin_amdgcn_s_setprio(0);
   }
 
-  // ---- partial sums into this wave's LDS (its staging area is no longer read), then the sum ----
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float* red = (float*)stq;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    v4f pa = accA[mt];
-    if (Cfg::kE8) pa += accA2[mt];
-    v4f pb = accB[mt];
-    if (Cfg::kE8) pb += accB2[mt];
-    if (HASB && SB > 1) {
-      // the SB K-block partials of a remainder column sit in SB neighbouring lanes: fold them into
-      // the first, in a fixed order
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] += dpp_f32_xor1(pb[e]);
-        if (SB > 2) pb[e] += dpp_f32_xor2(pb[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (NA) red[((0 * MT + mt) * 4 + e) * 64 + lane] = pa[e];
-      if (HASB) red[((1 * MT + mt) * 4 + e) * 64 + lane] = pb[e];
-    }
-  }
   __syncthreads();
   const int na16 = 16 * NA;
   const int nout = Mc * cols;
@@ -868,12 +944,12 @@ __global__ __launch_bounds__(512) void smallm_gemm_kernel(
     const int part = inA ? 0 : 1;
     const int li = (r >> 2) * 16 + (inA ? ci : (ci - na16) * SB);
     const float* rp = (const float*)smem + ((part * MT + mt) * 4 + e) * 64 + li;
-    float v[kMaxWaves];
+    float v[Cfg::kRanges];
 #pragma unroll
-    for (int w = 0; w < kMaxWaves; ++w) v[w] = (w < nwaves) ? rp[w * (Cfg::kWave / 4)] : -0.0f;  // x + -0 == x
+    for (int w = 0; w < Cfg::kRanges; ++w) v[w] = (w < NW) ? rp[w * (Cfg::kWave / 4)] : -0.0f;  // x + -0 == x
     float sum = v[0];
 #pragma unroll
-    for (int w = 1; w < kMaxWaves; ++w) sum += v[w];
+    for (int w = 1; w < Cfg::kRanges; ++w) sum += v[w];
     const int col = inA ? 16 * wg + ci : na16 * NWG + CB * wg + (ci - na16);
     y[(int64_t)(m0 + row) * ldy + col] = bf16_rne(sum);
   }
@@ -1099,33 +1175,40 @@ uint32_t layout_id_for(int N, int K) {
 }
 
 template <int MODE, int MT, int NA, bool HASB, int SB, int RC>
-void launch_k(const Layout& L, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
-              const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K, uint8_t* q_dbg,
-              void* sx_dbg) {
-  hipLaunchKernelGGL((smallm_gemm_kernel<MT, MODE, NA, HASB, SB, RC>), grid, dim3(64 * L.nw), 0, stream, a, lda,
-                     sa, wp, sw, y, ldy, M, K, L.r, L.cb, L.nwg, q_dbg, sx_dbg);
+void launch_k(int R, int nw, const Layout& L, dim3 grid, hipStream_t stream, const void* a, int64_t lda,
+              const void* sa, const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K,
+              uint8_t* q_dbg, void* sx_dbg) {
+  hipLaunchKernelGGL((smallm_gemm_kernel<MT, MODE, NA, HASB, SB, RC>), grid, dim3(128 * nw), 0, stream, a, lda,
+                     sa, wp, sw, y, ldy, M, K, R, L.cb, L.nwg, q_dbg, sx_dbg);
 }
 
+// The launch for the layout's K split: one 16-row tile takes the layout's ranges (r blocks in
+// rounds of rc), two tiles take ranges of 2 r blocks, also in rounds of rc (half as many waves
+// with twice the registers).  The remainder fragments' SB blocks divide the round.
 template <int MODE, int MT>
-void launch_mt(const Layout& L, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
-               const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, int K, uint8_t* q_dbg,
+void launch_mt(const Layout& L, int K, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
+               const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, uint8_t* q_dbg,
                void* sx_dbg) {
+  const int R = MT == 1 ? L.r : 2 * L.r;
+  const int KB = K / 128;
+  const int nw = (KB + R - 1) / R;
 #define SMALLM_K(na, hasb, sb, rc) \
-  launch_k<MODE, MT, na, hasb, sb, rc>(L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg)
+  launch_k<MODE, MT, na, hasb, sb, rc>(R, nw, L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg)
+  constexpr int X = 1;  // round length factor
   if (L.cb == 0) {
-    if (L.rc == 1) SMALLM_K(1, false, 1, 1);
-    else if (L.rc == 2) SMALLM_K(1, false, 1, 2);
-    else SMALLM_K(1, false, 1, 4);
+    if (L.rc == 1) SMALLM_K(1, false, 1, 1 * X);
+    else if (L.rc == 2) SMALLM_K(1, false, 1, 2 * X);
+    else SMALLM_K(1, false, 1, 4 * X);
   } else if (L.na == 1) {
-    if (L.rc == 1) SMALLM_K(1, true, 1, 1);
-    else if (L.rc == 2) SMALLM_K(1, true, 2, 2);
-    else if (L.sb == 4) SMALLM_K(1, true, 4, 4);
-    else SMALLM_K(1, true, 2, 4);
+    if (L.rc == 1) SMALLM_K(1, true, 1, 1 * X);
+    else if (L.rc == 2) SMALLM_K(1, true, 2, 2 * X);
+    else if (L.sb == 4) SMALLM_K(1, true, 4, 4 * X);
+    else SMALLM_K(1, true, 2, 4 * X);
   } else {
-    if (L.rc == 1) SMALLM_K(0, true, 1, 1);
-    else if (L.rc == 2) SMALLM_K(0, true, 2, 2);
-    else if (L.sb == 4) SMALLM_K(0, true, 4, 4);
-    else SMALLM_K(0, true, 2, 4);
+    if (L.rc == 1) SMALLM_K(0, true, 1, 1 * X);
+    else if (L.rc == 2) SMALLM_K(0, true, 2, 2 * X);
+    else if (L.sb == 4) SMALLM_K(0, true, 4, 4 * X);
+    else SMALLM_K(0, true, 2, 4 * X);
   }
 #undef SMALLM_K
 }
@@ -1138,8 +1221,8 @@ int launch_gemm(const void* a, int64_t lda, const void* sa, const uint8_t* wp, c
   const int MT = (M <= 16) ? 1 : 2;
   const int MP = 16 * MT;
   const dim3 grid(L.nwg, (M + MP - 1) / MP);
-  if (MT == 1) launch_mt<MODE, 1>(L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg);
-  else launch_mt<MODE, 2>(L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg);
+  if (MT == 1) launch_mt<MODE, 1>(L, K, grid, stream, a, lda, sa, wp, sw, y, ldy, M, q_dbg, sx_dbg);
+  else launch_mt<MODE, 2>(L, K, grid, stream, a, lda, sa, wp, sw, y, ldy, M, q_dbg, sx_dbg);
   return launch_status();
 }
 
@@ -1195,7 +1278,9 @@ int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan8) {
   if (st) return st;
   const Layout L = layout_for(N, K);
   const int MT = (M <= 16) ? 1 : 2;
-  const int v[8] = {L.nwg, L.na, L.cb, L.sb, L.r, L.rc, L.nw, MT};
+  const int KB = K / 128;
+  const int R = MT == 1 ? L.r : 2 * L.r;  // as launch_mt takes it
+  const int v[8] = {L.nwg, L.na, L.cb, L.sb, R, L.rc, (KB + R - 1) / R, MT};
   for (int i = 0; i < 8; ++i) plan8[i] = v[i];
   return SMALLM_OK;
 }
