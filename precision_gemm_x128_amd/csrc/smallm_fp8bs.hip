@@ -532,9 +532,8 @@ struct GemmCfg {
   static constexpr int kSts = RC * kMP * 4;              // their scales (fp32, or e8m0 bytes)
   static constexpr int kRed = 2 * MT * 4 * 64 * 4;       // one wave's partial sums (both groups)
   static constexpr int kWave = ((kStq + kSts > kRed ? kStq + kSts : kRed) + 15) / 16 * 16;
-  // one 16-row tile: up to 8 K ranges; two tiles: up to 4 ranges of twice the blocks (512 threads,
-  // so that each wave has 256 registers)
-  static constexpr int kRanges = MT == 1 ? kMaxWaves : kMaxWaves / 2;
+  // up to 8 K ranges of two waves each (1024 threads), for one or two 16-row tiles
+  static constexpr int kRanges = kMaxWaves;
   static constexpr int kSmem = kRanges * kWave;
 };
 
@@ -584,7 +583,7 @@ __device__ __forceinline__ void flag_wait(uint32_t* f, uint32_t v) {
 // multiplied by x_scale * w_scale into the accumulator; e8m0 scales are the MFMA's own scale
 // operands.  The MFMA waves' partial sums meet once in LDS, summed in range order.
 template <int MT, int MODE, int NA, bool HASB, int SB, int RC>
-__global__ __launch_bounds__(MT == 1 ? 1024 : 512) void smallm_gemm_kernel(
+__global__ __launch_bounds__(1024) void smallm_gemm_kernel(
     const void* __restrict__ a_src, int64_t lda, const void* __restrict__ sa_src,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
     int64_t ldy, int M, int K, int R, int CB, int NWG, uint8_t* __restrict__ q_dbg,
@@ -748,6 +747,12 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 512) void smallm_gemm_kernel(
 #pragma unroll
               for (int e = 0; e < 4; ++e) accA[mt][e] = __builtin_fmaf(sx4[e] * sc, fa[e], accA[mt][e]);
             }
+          }
+          if (MT == 2 && !Cfg::kE8) {
+            // two tiles: the block's scaled partials join the accumulators here, in the MFMAs' own
+            // block (deferring them past the round's last MFMA would hold every MFMA result of
+            // the round, more than a wave's 128 registers)
+            asm volatile("" : "+v"(accA[mt]), "+v"(accB[mt]));
           }
         }
       }
@@ -1182,33 +1187,31 @@ void launch_k(int R, int nw, const Layout& L, dim3 grid, hipStream_t stream, con
                      sa, wp, sw, y, ldy, M, K, R, L.cb, L.nwg, q_dbg, sx_dbg);
 }
 
-// The launch for the layout's K split: one 16-row tile takes the layout's ranges (r blocks in
-// rounds of rc), two tiles take ranges of 2 r blocks, also in rounds of rc (half as many waves
-// with twice the registers).  The remainder fragments' SB blocks divide the round.
+// The launch for the layout's K split: the layout's ranges of r blocks, in rounds of rc, for one
+// or two 16-row tiles.  The remainder fragments' SB blocks divide the round.
 template <int MODE, int MT>
 void launch_mt(const Layout& L, int K, dim3 grid, hipStream_t stream, const void* a, int64_t lda, const void* sa,
                const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, int M, uint8_t* q_dbg,
                void* sx_dbg) {
-  const int R = MT == 1 ? L.r : 2 * L.r;
+  const int R = L.r;
   const int KB = K / 128;
   const int nw = (KB + R - 1) / R;
 #define SMALLM_K(na, hasb, sb, rc) \
   launch_k<MODE, MT, na, hasb, sb, rc>(R, nw, L, grid, stream, a, lda, sa, wp, sw, y, ldy, M, K, q_dbg, sx_dbg)
-  constexpr int X = 1;  // round length factor
   if (L.cb == 0) {
-    if (L.rc == 1) SMALLM_K(1, false, 1, 1 * X);
-    else if (L.rc == 2) SMALLM_K(1, false, 1, 2 * X);
-    else SMALLM_K(1, false, 1, 4 * X);
+    if (L.rc == 1) SMALLM_K(1, false, 1, 1);
+    else if (L.rc == 2) SMALLM_K(1, false, 1, 2);
+    else SMALLM_K(1, false, 1, 4);
   } else if (L.na == 1) {
-    if (L.rc == 1) SMALLM_K(1, true, 1, 1 * X);
-    else if (L.rc == 2) SMALLM_K(1, true, 2, 2 * X);
-    else if (L.sb == 4) SMALLM_K(1, true, 4, 4 * X);
-    else SMALLM_K(1, true, 2, 4 * X);
+    if (L.rc == 1) SMALLM_K(1, true, 1, 1);
+    else if (L.rc == 2) SMALLM_K(1, true, 2, 2);
+    else if (L.sb == 4) SMALLM_K(1, true, 4, 4);
+    else SMALLM_K(1, true, 2, 4);
   } else {
-    if (L.rc == 1) SMALLM_K(0, true, 1, 1 * X);
-    else if (L.rc == 2) SMALLM_K(0, true, 2, 2 * X);
-    else if (L.sb == 4) SMALLM_K(0, true, 4, 4 * X);
-    else SMALLM_K(0, true, 2, 4 * X);
+    if (L.rc == 1) SMALLM_K(0, true, 1, 1);
+    else if (L.rc == 2) SMALLM_K(0, true, 2, 2);
+    else if (L.sb == 4) SMALLM_K(0, true, 4, 4);
+    else SMALLM_K(0, true, 2, 4);
   }
 #undef SMALLM_K
 }
@@ -1279,7 +1282,7 @@ int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan8) {
   const Layout L = layout_for(N, K);
   const int MT = (M <= 16) ? 1 : 2;
   const int KB = K / 128;
-  const int R = MT == 1 ? L.r : 2 * L.r;  // as launch_mt takes it
+  const int R = L.r;  // as launch_mt takes it
   const int v[8] = {L.nwg, L.na, L.cb, L.sb, R, L.rc, (KB + R - 1) / R, MT};
   for (int i = 0; i < 8; ++i) plan8[i] = v[i];
   return SMALLM_OK;

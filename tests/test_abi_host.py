@@ -43,6 +43,9 @@ def test_launch_plans_balance_the_cus():
         assert p["RC"] == min(p["R"], 4) and p["R"] % p["RC"] == 0 and p["RC"] % p["SB"] == 0
         assert P.weight_layout(N, K) == {"NA": na, "CB": cb, "SB": sb}
     assert P.smallm_fp8bs_launch_plan(17, 4096, 2048)["MT"] == 2
+    # two 16-row tiles keep the one-tile K split: 8 ranges of 4 blocks on 5120x4096
+    p32 = P.smallm_fp8bs_launch_plan(32, 5120, 4096)
+    assert (p32["R"], p32["RC"], p32["NW"]) == (4, 4, 8)
     assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["MT"] == 1
     # N a multiple of 4096: one 16-column group per workgroup, N / 16 workgroups
     p = P.smallm_fp8bs_launch_plan(4, 8192, 256)
