@@ -48,16 +48,27 @@ def test_launch_plans_balance_the_cus():
     assert (p32["R"], p32["RC"], p32["NW"]) == (4, 4, 8)
     assert P.smallm_fp8bs_launch_plan(16, 4096, 2048)["MT"] == 1
     # N a multiple of 4096: one 16-column group per workgroup, N / 16 workgroups
-    p = P.smallm_fp8bs_launch_plan(4, 8192, 256)
+    p = P.smallm_fp8bs_launch_plan(8, 8192, 256)
     assert (p["nwg"], p["NA"], p["CB"], p["R"], p["NW"]) == (512, 1, 0, 1, 2)
     # shapes without a balanced split fall back to one 16-column group per workgroup
-    p = P.smallm_fp8bs_launch_plan(4, 384, 640)
+    p = P.smallm_fp8bs_launch_plan(8, 384, 640)
     assert (p["nwg"], p["NA"], p["CB"], p["R"], p["NW"]) == (24, 1, 0, 1, 5)
-    p = P.smallm_fp8bs_launch_plan(4, 1024, 12416)   # 97 K blocks: no whole remainder fragments
+    p = P.smallm_fp8bs_launch_plan(8, 1024, 12416)   # 97 K blocks: no whole remainder fragments
     assert (p["nwg"], p["NA"], p["CB"], p["R"], p["RC"], p["NW"]) == (64, 1, 0, 16, 4, 7)
     # a remainder group of single K blocks when a wave holds one block
-    p = P.smallm_fp8bs_launch_plan(4, 4608, 640)
+    p = P.smallm_fp8bs_launch_plan(8, 4608, 640)
     assert (p["nwg"], p["NA"], p["CB"], p["SB"], p["R"]) == (256, 1, 2, 1, 1)
+    # up to 4 rows on a short K (<= 16 blocks) take ranges of twice the blocks
+    p = P.smallm_fp8bs_launch_plan(4, 4096, 2048)
+    assert (p["R"], p["RC"], p["NW"]) == (4, 4, 4)
+    p = P.smallm_fp8bs_launch_plan(5, 4096, 2048)
+    assert (p["R"], p["RC"], p["NW"]) == (2, 2, 8)
+    p = P.smallm_fp8bs_launch_plan(1, 384, 640)
+    assert (p["R"], p["RC"], p["NW"]) == (2, 2, 3)
+    p = P.smallm_fp8bs_launch_plan(1, 4608, 640)     # single-block remainder fragments: unchanged
+    assert (p["R"], p["RC"], p["NW"]) == (1, 1, 5)
+    p = P.smallm_fp8bs_launch_plan(4, 5120, 4096)    # 32 blocks: unchanged
+    assert (p["R"], p["RC"], p["NW"]) == (4, 4, 8)
     assert P.kernel_name(4, 5120, 4096) == "smallm_gemm_kernel<1, 0, 1, true, 4, 4>"
     assert P.kernel_name(32, 4608, 4096) == "smallm_gemm_kernel<2, 0, 1, true, 4, 4>"
     assert P.kernel_name(8, 4096, 2048, 1) == "smallm_gemm_kernel<1, 1, 1, false, 1, 2>"
