@@ -174,6 +174,8 @@ def gemm(q: np.ndarray, sx: np.ndarray, w8: np.ndarray, sw: np.ndarray, e8m0: bo
     M, K = q.shape
     N = w8.shape[0]
     n1 = N if n1 is None else n1
+    if not (0 <= n0 <= n1 <= N) or w8.shape[1] != K or sx.shape != (M, K // 128) or sw.shape != (N // 128, K // 128):
+        raise ValueError("gemm: column window or operand shapes out of range")
     ref = np.zeros((M, N), dtype=np.float64)
     if e8m0:
         sx = np.ascontiguousarray(sx, dtype=np.uint8)
@@ -203,6 +205,8 @@ def quant_gemm(x_bits: np.ndarray, w8: np.ndarray, sw: np.ndarray, e8m0: bool = 
     M, K = x_bits.shape
     N = w8.shape[0]
     n1 = N if n1 is None else n1
+    if not (0 <= n0 <= n1 <= N) or w8.shape[1] != K or np.shape(sw) != (N // 128, K // 128):
+        raise ValueError("quant_gemm: column window or operand shapes out of range")
     q = np.empty((M, K), dtype=np.uint8)
     sx = np.empty((M, K // 128), dtype=np.uint8 if e8m0 else np.float32)
     sw = np.ascontiguousarray(sw, dtype=np.uint8 if e8m0 else np.float32)

@@ -207,6 +207,10 @@ void oracle_quant_weight_fp32(const float* w, int64_t ldw, int N, int K, uint8_t
  * midpoint is irrational, so there are no ties.  Clamped to [-127, 127]; amax == 0 -> -127. */
 int oracle_e8m0_round_exponent(double amax) {
   if (amax == 0.0) return -127;
+  /* outside the search range the clamp decides: no fp32 amax lies below 448 * 2^-300, and an
+   * infinite one clamps to the top (a NaN amax has no exponent: treated like zero) */
+  if (!(amax >= ldexp(448.0, -300))) return -127;
+  if (isinf(amax)) return 127;
   int F = -300;
   while (!(ldexp(448.0, F) <= amax && amax < ldexp(448.0, F + 1))) ++F;
   int E = (amax * amax < 448.0 * 448.0 * ldexp(1.0, 2 * F + 1)) ? F : F + 1;

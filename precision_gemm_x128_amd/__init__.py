@@ -224,6 +224,33 @@ def _contig(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_exact(t, dtypes, shape, name, device=None):
+    """t must be a contiguous device tensor of exactly this shape and one of these dtypes (on the
+    given device when one is named): the kernels write or read it as a dense array of that shape,
+    and the C entry points cannot see sizes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_rows(t, M, K, name, device):
+    """t must be an [M, K] byte matrix on the device with unit column stride (any row pitch)."""
+    _need(t, _F8, name)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != (M, K):
+        raise ValueError(f"{name} must be ({M}, {K}), got {tuple(t.shape)}")
+
+
 _U8 = (torch.uint8,)
 _F8 = (torch.uint8, torch.float8_e4m3fn)
 _BF = (torch.bfloat16,)
@@ -240,6 +267,8 @@ def smallm_fp8bs_quant_weight(w, w8=None, sw=None, stream=None):
     N, K = w.shape
     w8 = torch.empty((N, K), dtype=torch.uint8, device=w.device) if w8 is None else w8
     sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device) if sw is None else sw
+    _need_exact(w8, _F8, (N, K), "w8", w.device)
+    _need_exact(sw, _F32, (N // 128, K // 128), "sw", w.device)
     _check(lib().smallm_fp8bs_quant_weight(_ptr(w), w.stride(0), _ptr(w8), _ptr(sw), N, K, _stream(stream)),
            "smallm_fp8bs_quant_weight")
     return w8, sw
@@ -251,6 +280,8 @@ def smallm_fp8bs_quant_weight_e8m0(w, w8=None, sw=None, stream=None):
     N, K = w.shape
     w8 = torch.empty((N, K), dtype=torch.uint8, device=w.device) if w8 is None else w8
     sw = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=w.device) if sw is None else sw
+    _need_exact(w8, _F8, (N, K), "w8", w.device)
+    _need_exact(sw, _U8, (N // 128, K // 128), "sw", w.device)
     _check(lib().smallm_fp8bs_quant_weight_e8m0(_ptr(w), w.stride(0), _ptr(w8), _ptr(sw), N, K, _stream(stream)),
            "smallm_fp8bs_quant_weight_e8m0")
     return w8, sw
@@ -262,6 +293,7 @@ def smallm_fp8bs_pack_weight(w8, out=None, stream=None):
     _contig(w8, "w8")
     N, K = w8.shape
     out = torch.empty((N, K), dtype=torch.uint8, device=w8.device) if out is None else out
+    _need_exact(out, _U8, (N, K), "out", w8.device)
     _check(lib().smallm_fp8bs_pack_weight(_ptr(w8), _ptr(out), N, K, _stream(stream)), "smallm_fp8bs_pack_weight")
     return out
 
@@ -271,6 +303,7 @@ def smallm_fp8bs_unpack_weight(w_packed, out=None, stream=None):
     _contig(w_packed, "w_packed")
     N, K = w_packed.shape
     out = torch.empty((N, K), dtype=torch.uint8, device=w_packed.device) if out is None else out
+    _need_exact(out, _F8, (N, K), "out", w_packed.device)
     _check(lib().smallm_fp8bs_unpack_weight(_ptr(w_packed), _ptr(out), N, K, _stream(stream)),
            "smallm_fp8bs_unpack_weight")
     return out
@@ -286,6 +319,8 @@ def smallm_fp8bs_quant(x, q=None, sx=None, stream=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
     sx = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if sx is None else sx
+    _need_rows(q, M, K, "q", x.device)
+    _need_exact(sx, _F32, (M, K // 128), "sx", x.device)
     _check(lib().smallm_fp8bs_quant(_ptr(x), x.stride(0), _ptr(q), q.stride(0), _ptr(sx), M, K, _stream(stream)),
            "smallm_fp8bs_quant")
     return q, sx
@@ -297,6 +332,8 @@ def smallm_fp8bs_quant_e8m0(x, q=None, sx=None, stream=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
     sx = torch.empty((M, K // 128), dtype=torch.uint8, device=x.device) if sx is None else sx
+    _need_rows(q, M, K, "q", x.device)
+    _need_exact(sx, _U8, (M, K // 128), "sx", x.device)
     _check(lib().smallm_fp8bs_quant_e8m0(_ptr(x), x.stride(0), _ptr(q), q.stride(0), _ptr(sx), M, K,
                                          _stream(stream)), "smallm_fp8bs_quant_e8m0")
     return q, sx
@@ -319,9 +356,11 @@ def _rmsnorm_quant(x, w, eps, y, q, sx, emit_y, emit_q, e8m0, stream):
         q = sx = None
     if y is not None:
         _need(y, _BF, "y")
+        if tuple(y.shape) != (M, H) or y.device != x.device:
+            raise ValueError(f"y must be [{M}, {H}] on {x.device}")
     if q is not None:
-        _need(q, _F8, "q")
-        _contig(sx, "sx")
+        _need_rows(q, M, H, "q", x.device)
+        _need_exact(sx, _U8 if e8m0 else _F32, (M, H // 128), "sx", x.device)
     fn = lib().smallm_fp8bs_rmsnorm_quant_e8m0 if e8m0 else lib().smallm_fp8bs_rmsnorm_quant
     _check(fn(_ptr(x), x.stride(0), _ptr(w), ctypes.c_float(eps), _ptr(y), y.stride(0) if y is not None else 0,
               _ptr(q), q.stride(0) if q is not None else 0, _ptr(sx), M, H, _stream(stream)),
@@ -348,6 +387,7 @@ def _check_weight(w_packed, sw, K, e8m0):
         raise ValueError(f"weight scales must be [{N // 128}, {K // 128}], got {tuple(sw.shape)}")
     if sw.dtype != (torch.uint8 if e8m0 else torch.float32):
         raise TypeError(f"weight scales must be {'uint8 (e8m0)' if e8m0 else 'float32'}, got {sw.dtype}")
+    _need_exact(sw, (sw.dtype,), (N // 128, K // 128), "weight scales", w_packed.device)
     return N
 
 
@@ -356,6 +396,7 @@ def _check_act_scales(sx, M, K, e8m0):
         raise ValueError(f"activation scales must be [{M}, {K // 128}], got {tuple(sx.shape)}")
     if sx.dtype != (torch.uint8 if e8m0 else torch.float32):
         raise TypeError(f"activation scales must be {'uint8 (e8m0)' if e8m0 else 'float32'}, got {sx.dtype}")
+    _need_exact(sx, (sx.dtype,), (M, K // 128), "activation scales")
 
 
 def _out(y, M, N, device):
@@ -364,7 +405,18 @@ def _out(y, M, N, device):
     _need(y, _BF, "y")
     if tuple(y.shape) != (M, N):
         raise ValueError(f"y must be [{M}, {N}], got {tuple(y.shape)}")
+    if y.device != device:
+        raise ValueError(f"y is on {y.device}, expected {device}")
     return y
+
+
+def _check_dbg(q_dbg, sx_dbg, M, K, e8m0, device):
+    """The fused kernels write the debug copies as dense arrays: q_dbg [M, K] bytes at row pitch K,
+    sx_dbg [M, K/128] (fp32, or e8m0 bytes)."""
+    if q_dbg is not None:
+        _need_exact(q_dbg, _F8, (M, K), "q_dbg", device)
+    if sx_dbg is not None:
+        _need_exact(sx_dbg, _U8 if e8m0 else _F32, (M, K // 128), "sx_dbg", device)
 
 
 def smallm_fp8bs_gemm(q, sx, w_packed, sw, y=None, layout_id=None, stream=None):
@@ -406,6 +458,7 @@ def smallm_fp8bs_quant_gemm(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, la
     M, K = x.shape
     N = _check_weight(w_packed, sw, K, False)
     y = _out(y, M, N, x.device)
+    _check_dbg(q_dbg, sx_dbg, M, K, False, x.device)
     lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_quant_gemm(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
                                          y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
@@ -420,6 +473,7 @@ def smallm_fp8bs_quant_gemm_e8m0(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=Non
     M, K = x.shape
     N = _check_weight(w_packed, sw, K, True)
     y = _out(y, M, N, x.device)
+    _check_dbg(q_dbg, sx_dbg, M, K, True, x.device)
     lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
     _check(lib().smallm_fp8bs_quant_gemm_e8m0(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
                                               y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
@@ -519,6 +573,8 @@ def _moe_workspace_arg(workspace, T, S, H, I, device):
         return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if not workspace.is_cuda:
+        raise ValueError("workspace must be a device tensor")
     return workspace
 
 
@@ -532,6 +588,8 @@ def smallm_fp8bs_moe(x, topk_ids, topk_w, w13_packed, sw13, w2_packed, sw2, work
     for t_, n_, shp in ((sw13, "sw13", (E, 2 * I // 128, H // 128)), (sw2, "sw2", (E, H // 128, I // 128))):
         if not isinstance(t_, torch.Tensor) or t_.dtype != torch.float32 or tuple(t_.shape) != shp:
             raise ValueError(f"{n_} must be float32 {shp}")
+        if not t_.is_cuda:
+            raise ValueError(f"{n_} must be a device tensor")
         _contig(t_, n_)
     workspace = _moe_workspace_arg(workspace, T, S, H, I, x.device)
     y = _out(y, T, H, x.device)
@@ -609,6 +667,8 @@ def smallm_fp8bs_moe_mxfp4(x, topk_ids, topk_w, w13_packed, s13_packed, w2_packe
     for t_, n_, shp in ((s13_packed, "s13_packed", (E, 2 * I, H // 32)), (s2_packed, "s2_packed", (E, H, I // 32))):
         if not isinstance(t_, torch.Tensor) or t_.dtype != torch.uint8 or tuple(t_.shape) != shp:
             raise ValueError(f"{n_} must be uint8 {shp}")
+        if not t_.is_cuda:
+            raise ValueError(f"{n_} must be a device tensor")
         _contig(t_, n_)
     workspace = _moe_workspace_arg(workspace, T, S, H, I, x.device)
     y = _out(y, T, H, x.device)

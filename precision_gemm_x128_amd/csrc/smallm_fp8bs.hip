@@ -11,25 +11,24 @@
 // linears" (power-of-two scales stored as e8m0 bytes, ue8m0 1x128 activation quant).  The code
 // is written for gfx950 only.  Design points of this implementation:
 //
-//  * Packed weight layout: every 16-column x 128-K block of W8 is one contiguous 2 KiB
-//    fragment stored in the lane order of the B operand of v_mfma_*_16x16x128_f8f6f4: lane
-//    l = 16*c + j holds column j and K bytes [32c, 32c+32) of the block, bytes 0..15 in the first
-//    KiB of the fragment and bytes 16..31 in the second.  A wave therefore fetches a fragment
-//    with two 16-byte non-temporal loads per lane, each covering 1 KiB contiguously.  Fragments
-//    of one 16-column tile are consecutive along K.
-//  * Work split: one workgroup (8 waves) owns NT 16-column tiles and all of K.  Waves 0-3
-//    quantise the activation rows for the workgroup (32 contiguous bf16 per lane, a quad of
-//    lanes per 1x128 group, the group amax reduced with two DPP quad permutes) and stage the
-//    e4m3 bytes in LDS; waves 4-7 issue their share of the weight stream up front, then run the
-//    MFMAs with the A operand read from LDS.  Keeping the weight loads and the activation loads
-//    in different waves keeps each wave's in-order load counter free of the other stream.
-//  * Quantisation is bit-exact with the IEEE definition q = RN(x / RN(amax / 448)): the
-//    quotient is formed from a correctly rounded reciprocal y = RN(1/sx) as q0 = x*y,
-//    r = fma(q0, sx, -x), q = fma(-r, y, q0), which equals the IEEE quotient for every bf16 x
-//    and every scale >= 2^-64 wherever the e4m3 code depends on it (verified exhaustively),
-//    keeps the sign of zero, and falls back to a true division for smaller scales.  The fp8
-//    encoding uses the hardware round-to-nearest-even conversion, which is exact below 464.
-//  * Deterministic reduction: per-wave fp32 partials are summed through LDS in a fixed order.
+//  * Packed weight layout: the columns are dealt to workgroups (one per CU for the pages' shapes),
+//    each owning NA (0 or 1) group of 16 columns and a remainder group of CB (0, 2, 4 or 8)
+//    columns, stored contiguously.  A 16-column x 128-K block is one 2 KiB fragment in the lane
+//    order of the B operand of v_mfma_scale_f32_16x16x128_f8f6f4 (lane l = 16 c + j holds column
+//    j and K bytes [32 c, 32 c + 32): bytes 0..15 in the fragment's first KiB, 16..31 in its
+//    second), so a wave fetches it with two coalesced 16-byte non-temporal loads per lane.  A
+//    remainder fragment packs SB = 16 / CB consecutive K blocks of the CB columns the same way.
+//  * Work split: a workgroup owns its columns and all of K; K is cut into up to 8 ranges, each
+//    with an MFMA wave (weight stream + MFMAs) and a quantising wave (activation loads, 1x128
+//    group amax over a DPP quad of lanes, e4m3 codes and scales staged in LDS) that meet only
+//    through LDS flags.  The ranges' partial sums meet once in LDS and are reduced in a fixed
+//    order to bf16.
+//  * Quantisation is bit-exact with q = e4m3_rne(RN(x / s)), s = RN(amax / 448): the quotient
+//    is formed with a two-term reciprocal of s (a multiply and an FMA per element, after an
+//    exact 2^64 rescaling of a group whose scale is below 2^-64), proven on the CPU to give the
+//    code of the correctly rounded division for every pair of bf16 amax and x; the fp8 encoding
+//    is the hardware round-to-nearest-even conversion, exact below 464.
+//  * Deterministic reduction: per-range fp32 partials are summed through LDS in a fixed order.
 //
 // Build flags (see the package's build module): --offload-arch=gfx950 -O3 -ffp-contract=off,
 // no fast-math, fp32 denormals kept, packed-fp32 instructions disabled.
@@ -52,7 +51,6 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 512;                // 8 waves: 4 quantise, 4 MFMA
 constexpr int kRowStride = 144;              // LDS row pitch of the staged e4m3 rows (128 + 16 pad)
 
 // ---------------------------------------------------------------------------------------------
