@@ -84,6 +84,8 @@ def time_config(P, torch, np, synthgen, dev, N, K, Ms, copies, reps, e8m0=False,
         sws.append(sw)
         del w, w8
     out, ys = {}, {}
+    # the streaming-read floor over the same 24 weight buffers, same graph shape
+    out["floor"] = graph_us(torch, lambda i: P.smallm_fp8bs_read_floor(wps[i]), copies, reps)
     for M in Ms:
         x = torch.from_numpy(synthgen.gen_x(M, K, seed=0, outliers=outliers).view(np.int16).copy()).to(dev).view(torch.bfloat16)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -295,22 +297,26 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
     fusion (RMSNorm with the quantisation, then the GEMM on pre-quantised input) on 5120x4096."""
     res = {}
 
-    def entry(N, K, M, us, e8m0=False):
+    def entry(N, K, M, us, e8m0=False, floor=None):
         b = P.algorithmic_bytes(M, N, K, e8m0)
         gbs = b / (us * 1e-6) / 1e9
-        return {"us_per_call": round(us, 3), "GB_s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
-                "kernel": P.kernel_name(M, N, K, 1 if e8m0 else 0)}
+        e = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+             "kernel": P.kernel_name(M, N, K, 1 if e8m0 else 0)}
+        if floor is not None:
+            e["read_floor_us"] = round(floor, 3)
+            e["time_over_floor"] = round(us / floor, 3)
+        return e
 
     t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, [4], copies, reps)
-    res["single_4096x2048_m4"] = entry(4096, 2048, 4, t[4])
+    res["single_4096x2048_m4"] = entry(4096, 2048, 4, t[4], floor=t["floor"])
     for N, K in ((4608, 4096), (4096, 2048)):
         t, _ = time_config(P, torch, np, synthgen, dev, N, K, list(M_SWEEP), copies, reps, outliers=True)
-        res[f"sweep_{N}x{K}_outliers"] = {str(M): entry(N, K, M, t[M]) for M in M_SWEEP}
+        res[f"sweep_{N}x{K}_outliers"] = {str(M): entry(N, K, M, t[M], floor=t["floor"]) for M in M_SWEEP}
         log(f"[bench] {N}x{K} outliers: " + " ".join(f"M={M} {t[M]:.2f}us" for M in M_SWEEP))
     # 24 copies of an 8 MiB weight (192 MiB) fit in the 256 MB MALL: the same sweep over 64 copies
     # (512 MiB) shows whether the 24-copy figures were helped by it
     t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, list(M_SWEEP), 64, reps, outliers=True)
-    res["sweep_4096x2048_outliers_64copies"] = {str(M): entry(4096, 2048, M, t[M]) for M in M_SWEEP}
+    res["sweep_4096x2048_outliers_64copies"] = {str(M): entry(4096, 2048, M, t[M], floor=t["floor"]) for M in M_SWEEP}
     log("[bench] 4096x2048 outliers, 64 copies: " + " ".join(f"M={M} {t[M]:.2f}us" for M in M_SWEEP))
     big = (33, 48, 64, 128, 256)
     t, _ = time_config(P, torch, np, synthgen, dev, 4096, 2048, list(big), copies, reps)
@@ -330,7 +336,8 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
         d = {}
         for M in ms:
             rel = float(((ye[M] - yf[M]).abs().max() / yf[M].abs().max()).item())
-            d[str(M)] = {"fp32_scales": entry(N, K, M, tf[M]), "e8m0_scales": entry(N, K, M, te[M], True),
+            d[str(M)] = {"fp32_scales": entry(N, K, M, tf[M], floor=tf["floor"]),
+                         "e8m0_scales": entry(N, K, M, te[M], True, floor=te["floor"]),
                          "max_abs_diff_over_max_abs": round(rel, 5)}
         res[f"e8m0_vs_fp32_{N}x{K}"] = d
         log(f"[bench] {N}x{K} e8m0 vs fp32: " + " ".join(f"M={M} {te[M]:.2f}/{tf[M]:.2f}us" for M in ms))
@@ -354,6 +361,8 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times): the "
                          "reference kernel for scaling HBM byte counters, then exit")
+    ap.add_argument("--only-m", type=int, default=0,
+                    help="profiling runs: time this one M of the sweep only (no configs, no CPU leg)")
     ap.add_argument("--moe-only", action="store_true",
                     help="only time the MoE layers (as in the other workloads) and print them as JSON")
     args = ap.parse_args()
@@ -382,6 +391,10 @@ def main():
         log(f"[bench] copied {args.calib_copy_mib} MiB three times")
         return
     N, K, copies = args.N, args.K, args.copies
+    global M_SWEEP
+    if args.only_m:
+        M_SWEEP = (args.only_m,)
+        args.no_configs = args.no_cpu = True
     P.lib()
     if args.moe_only:
         print(json.dumps({"moe": moe_sweeps(P, torch, np, synthgen, dev, max(1, args.reps))}))
@@ -418,6 +431,12 @@ def main():
             for i in range(copies):
                 P.smallm_fp8bs_quant_gemm(xs[M], wps[i], sws[i], y=ys[M])
         graphs[M] = g
+    # read floor: the library's plain streaming read over the same 24 weight buffers, one launch
+    # per buffer in a graph (the achievable time for the weight bytes alone)
+    gread = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gread):
+        for i in range(copies):
+            P.smallm_fp8bs_read_floor(wps[i])
     # launch floor: the same number of trivial launches in a graph
     tiny = torch.zeros(1, device=dev)
     gfloor = torch.cuda.CUDAGraph()
@@ -480,6 +499,19 @@ def main():
     torch.cuda.synchronize()
     floor_us = a.elapsed_time(b) * 1e3 / (reps * copies)
     log(f"[bench] trivial-kernel launch floor in a graph: {floor_us:.3f} us/launch")
+    gread.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        gread.replay()
+    b.record()
+    torch.cuda.synchronize()
+    read_floor_us = a.elapsed_time(b) * 1e3 / (reps * copies)
+    log(f"[bench] streaming-read floor of the {N}x{K} weight bytes: {read_floor_us:.3f} us/launch "
+        f"({N * K / (read_floor_us * 1e-6) / 1e9:.0f} GB/s)")
+    for M in M_SWEEP:
+        sweep[str(M)]["time_over_read_floor"] = round(sweep[str(M)]["us_per_call"] / read_floor_us, 3)
 
     # ---- roofline of the dominant kernel instantiation (largest share of the step's time) ----
     by_kernel = {}
@@ -495,7 +527,10 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom),
                 "kernel": dom, "avg_launch_us": round(d["us"] / d["launches"], 3),
-                "launch_ms": [m for m in M_SWEEP if sweep[str(m)]["kernel"] == dom]}
+                "launch_ms": [m for m in M_SWEEP if sweep[str(m)]["kernel"] == dom],
+                "floor_us": round(read_floor_us, 3),
+                "frac_of_floor": round(read_floor_us / (d["us"] / d["launches"]), 4),
+                "floor_kernel": "read_floor_kernel (library streaming read of the same weight bytes)"}
 
     # ---- pages' kernel on the same workload (same hardware): context ratio ----
     pages_step_us = sum(PAGES_FUSED_US[M] for M in M_SWEEP)
@@ -534,6 +569,7 @@ def main():
                    "calls_per_step": copies * len(M_SWEEP), "parallelism": "single GPU"},
         "sweep": sweep,
         "launch_floor_us": round(floor_us, 3),
+        "read_floor_us": round(read_floor_us, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "configs": configs,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMALLM_FP8BS_ABI_VERSION 5
+#define SMALLM_FP8BS_ABI_VERSION 6
 #define SMALLM_FP8BS_MAX_M 256
 #define SMALLM_FP8BS_RMS_MAX_M (1 << 20) /* rows of one producer call */
 #define SMALLM_FP8BS_RMS_MAX_H 16384     /* values per row of one producer call */
@@ -93,6 +93,14 @@ int smallm_fp8bs_supported(int M, int N, int K, int64_t ldx);
  * a workgroup has 128 * NW threads) and MT (16-row M tiles per workgroup; M above 32 runs in
  * 32-row chunks along the grid's second dimension).  Returns SMALLM_OK or the shape error. */
 int smallm_fp8bs_launch_plan(int M, int N, int K, int* plan8);
+
+/* Roofline reference, not part of the method: stream `bytes` (1 .. 2^30) of device memory at buf
+ * (16-byte aligned) through the GPU with plain non-temporal 16-byte loads, one workgroup per CU,
+ * each reading a contiguous share with every load issued before any is consumed -- the launch
+ * shape that reads a weight-sized buffer fastest on this part.  Its time over the same bytes (a
+ * packed weight) is the achievable floor the GEMM is measured against.  sink: device memory of
+ * at least 2048 uint32 that the kernel practically never writes.  Returns a status. */
+int smallm_fp8bs_read_floor(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /* --------------------------------------------------------------------------------------------
  * Load-time weight preparation (not on the per-token path)

@@ -35,6 +35,7 @@ EXPORTS = (
     "smallm_fp8bs_strerror",
     "smallm_fp8bs_supported",
     "smallm_fp8bs_launch_plan",
+    "smallm_fp8bs_read_floor",
     "smallm_fp8bs_quant_weight",
     "smallm_fp8bs_quant_weight_e8m0",
     "smallm_fp8bs_pack_weight",
@@ -105,6 +106,7 @@ def lib():
         "smallm_fp8bs_strerror": (ctypes.c_char_p, [I]),
         "smallm_fp8bs_supported": (I, [I, I, I, I64]),
         "smallm_fp8bs_launch_plan": (I, [I, I, I, P]),
+        "smallm_fp8bs_read_floor": (I, [P, I64, P, P]),
         "smallm_fp8bs_quant_weight": (I, [P, I64, P, P, I, I, P]),
         "smallm_fp8bs_quant_weight_e8m0": (I, [P, I64, P, P, I, I, P]),
         "smallm_fp8bs_pack_weight": (I, [P, P, I, I, P]),
@@ -479,6 +481,21 @@ def smallm_fp8bs_quant_gemm_e8m0(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=Non
                                               y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
            "smallm_fp8bs_quant_gemm_e8m0")
     return y
+
+
+_floor_sink = {}
+
+
+def smallm_fp8bs_read_floor(buf, stream=None):
+    """Stream every byte of the device tensor buf with the library's plain streaming-read kernel
+    (a roofline reference, not part of the method)."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    sink = _floor_sink.get(buf.device)
+    if sink is None:
+        sink = _floor_sink[buf.device] = torch.zeros(2048, dtype=torch.int32, device=buf.device)
+    _check(lib().smallm_fp8bs_read_floor(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                         _stream(stream)), "smallm_fp8bs_read_floor")
 
 
 def algorithmic_bytes(M: int, N: int, K: int, e8m0: bool = False) -> int:

@@ -1126,6 +1126,43 @@ int check_mnk(int M, int N, int K) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SMALLM_OK : SMALLM_ERR_HIP; }
 
+// ---------------------------------------------------------------------------------------------
+// streaming-read reference (the achievable HBM read time of a buffer, for the roofline)
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kFloorWGs = 256;    // one workgroup per CU
+constexpr int kFloorWaves = 8;
+constexpr int kFloorLoads = 10;   // 16-byte loads per lane in flight (a 20 MiB buffer: all of them)
+
+// Workgroup g reads its contiguous share of `bytes` in 1 KiB units (a wave-wide 16-byte load per
+// unit), wave w taking units w, w + 8, ..., kFloorLoads at a time, every load issued before any is
+// consumed; non-temporal, bounds-checked (units past the end read zeros).  The loaded words are
+// folded into one value per wave that is written out only if it equals a constant no random data
+// produces, so the loads cannot be dropped and nothing else is written.
+__global__ __launch_bounds__(64 * kFloorWaves) void read_floor_kernel(const uint8_t* __restrict__ buf,
+                                                                      uint32_t bytes, uint32_t units,
+                                                                      uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)buf, 0, (int)bytes, 0x00020000);
+  const uint32_t base = (blockIdx.x * units + (uint32_t)wave) * 1024u + (uint32_t)lane * 16u;
+  const uint32_t nu = (units > (uint32_t)wave) ? (units - (uint32_t)wave + kFloorWaves - 1) / kFloorWaves : 0u;
+  u32x4 x = u32x4{0u, 0u, 0u, 0u};
+  for (uint32_t b = 0; b < nu; b += kFloorLoads) {
+    u32x4 r[kFloorLoads];
+#pragma unroll
+    for (int j = 0; j < kFloorLoads; ++j) {
+      const uint32_t i = b + (uint32_t)j;
+      const uint32_t off = (i < nu) ? base + i * (kFloorWaves * 1024u) : bytes;
+      r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+    }
+#pragma unroll
+    for (int j = 0; j < kFloorLoads; ++j) x ^= r[j];
+  }
+  const uint32_t v = x[0] ^ x[1] ^ x[2] ^ x[3];
+  if (v == 0x9E3779B9u) sink[blockIdx.x * kFloorWaves + wave] = v;
+}
+
 constexpr int kTargetWGs = 256;  // one workgroup per CU of the MI355X
 
 // The packed layout and the launch it implies for an [N, K] weight.
@@ -1268,6 +1305,16 @@ void launch_pack(const uint8_t* src, uint8_t* dst, int N, int K, hipStream_t str
 extern "C" {
 
 int smallm_fp8bs_abi_version(void) { return SMALLM_FP8BS_ABI_VERSION; }
+
+int smallm_fp8bs_read_floor(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return SMALLM_ERR_INVALID;
+  if (bytes <= 0 || bytes > ((int64_t)1 << 30)) return SMALLM_ERR_SHAPE;
+  if (((uintptr_t)buf & 15) != 0) return SMALLM_ERR_ALIGN;
+  const uint32_t units = (uint32_t)((bytes + (int64_t)kFloorWGs * 1024 - 1) / ((int64_t)kFloorWGs * 1024));
+  hipLaunchKernelGGL(read_floor_kernel, dim3(kFloorWGs), dim3(64 * kFloorWaves), 0, (hipStream_t)stream,
+                     (const uint8_t*)buf, (uint32_t)bytes, units, sink);
+  return launch_status();
+}
 
 uint32_t smallm_fp8bs_weight_layout_id(int N, int K) {
   if (N <= 0 || K <= 0 || (N & 127) || (K & 127)) return 0;

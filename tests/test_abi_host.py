@@ -76,7 +76,7 @@ def test_launch_plans_balance_the_cus():
 
 
 def test_version_layout_and_strerror():
-    assert P.smallm_fp8bs_abi_version() == 5
+    assert P.smallm_fp8bs_abi_version() == 6
     # 0x46390000 | NA << 12 | CB << 4 | SB
     assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46391001
     assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46391044
@@ -89,6 +89,16 @@ def test_version_layout_and_strerror():
     for s in range(6):
         assert len(P.strerror(s)) > 0
     assert P.strerror(99) == "unknown status"
+
+
+def test_read_floor_rejects_bad_arguments_before_launch():
+    L = P.lib()
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: every case fails its host check
+    assert L.smallm_fp8bs_read_floor(None, 1024, fake, None) == 1
+    assert L.smallm_fp8bs_read_floor(fake, 1024, None, None) == 1
+    assert L.smallm_fp8bs_read_floor(fake, 0, fake, None) == 2
+    assert L.smallm_fp8bs_read_floor(fake, (1 << 30) + 1, fake, None) == 2
+    assert L.smallm_fp8bs_read_floor(ctypes.c_void_p(0x10008), 1024, fake, None) == 3
 
 
 @pytest.mark.parametrize("M,N,K,ldx,expect", [

@@ -127,3 +127,16 @@ def test_moe_rejects_host_scales():
         P.smallm_fp8bs_moe(x, ids, tw, w13, sw13, w2, sw2.cpu())
     with pytest.raises(ValueError, match="device tensor"):
         P.smallm_fp8bs_moe(x, ids, tw, w13, sw13, w2, sw2, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+@pytest.mark.gpu
+def test_read_floor_streams_without_writing():
+    # the roofline reference kernel: reads every byte (ragged sizes too) and leaves the sink alone
+    for nbytes in (16, 1 << 20, (20 << 20) + 4096):
+        buf = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda:0")
+        P.smallm_fp8bs_read_floor(buf)
+        torch.cuda.synchronize()
+    sink = P._floor_sink[torch.device("cuda:0")]
+    assert int(sink.abs().sum().item()) == 0
+    with pytest.raises(ValueError):
+        P.smallm_fp8bs_read_floor(torch.zeros(64, dtype=torch.uint8))
