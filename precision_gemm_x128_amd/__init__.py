@@ -46,6 +46,9 @@ EXPORTS = (
     "smallm_fp8bs_gemm_e8m0",
     "smallm_fp8bs_quant_gemm",
     "smallm_fp8bs_quant_gemm_e8m0",
+    "smallm_fp8bs_quant_gemm_workspace_bytes",
+    "smallm_fp8bs_quant_gemm_ws",
+    "smallm_fp8bs_quant_gemm_e8m0_ws",
     "smallm_fp8bs_rmsnorm_quant",
     "smallm_fp8bs_rmsnorm_quant_e8m0",
     "smallm_fp8bs_moe_layout_id",
@@ -117,6 +120,9 @@ def lib():
         "smallm_fp8bs_gemm_e8m0": (I, [P, I64, P, P, U32, P, P, I64, I, I, I, P]),
         "smallm_fp8bs_quant_gemm": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
         "smallm_fp8bs_quant_gemm_e8m0": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, P, P]),
+        "smallm_fp8bs_quant_gemm_workspace_bytes": (ctypes.c_size_t, [I, I, I]),
+        "smallm_fp8bs_quant_gemm_ws": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, ctypes.c_size_t, P]),
+        "smallm_fp8bs_quant_gemm_e8m0_ws": (I, [P, I64, P, U32, P, P, I64, I, I, I, P, ctypes.c_size_t, P]),
         "smallm_fp8bs_rmsnorm_quant": (I, [P, I64, P, ctypes.c_float, P, I64, P, I64, P, I, I, P]),
         "smallm_fp8bs_rmsnorm_quant_e8m0": (I, [P, I64, P, ctypes.c_float, P, I64, P, I64, P, I, I, P]),
         "smallm_fp8bs_moe_layout_id": (U32, []),
@@ -452,37 +458,6 @@ def smallm_fp8bs_gemm_e8m0(q, sx, w_packed, sw, y=None, layout_id=None, stream=N
     return y
 
 
-def smallm_fp8bs_quant_gemm(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, layout_id=None, stream=None):
-    """Fused path: bf16 x [M, K], packed weight [N, K], fp32 sw [N/128, K/128] -> bf16 y [M, N]."""
-    _need(x, _BF, "x")
-    _need(w_packed, _U8, "w_packed")
-    _contig(sw, "sw")
-    M, K = x.shape
-    N = _check_weight(w_packed, sw, K, False)
-    y = _out(y, M, N, x.device)
-    _check_dbg(q_dbg, sx_dbg, M, K, False, x.device)
-    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
-    _check(lib().smallm_fp8bs_quant_gemm(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
-                                         y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
-           "smallm_fp8bs_quant_gemm")
-    return y
-
-
-def smallm_fp8bs_quant_gemm_e8m0(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, layout_id=None, stream=None):
-    _need(x, _BF, "x")
-    _need(w_packed, _U8, "w_packed")
-    _contig(sw, "sw")
-    M, K = x.shape
-    N = _check_weight(w_packed, sw, K, True)
-    y = _out(y, M, N, x.device)
-    _check_dbg(q_dbg, sx_dbg, M, K, True, x.device)
-    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
-    _check(lib().smallm_fp8bs_quant_gemm_e8m0(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y),
-                                              y.stride(0), M, N, K, _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)),
-           "smallm_fp8bs_quant_gemm_e8m0")
-    return y
-
-
 _floor_sink = {}
 
 
@@ -496,6 +471,53 @@ def smallm_fp8bs_read_floor(buf, stream=None):
         sink = _floor_sink[buf.device] = torch.zeros(2048, dtype=torch.int32, device=buf.device)
     _check(lib().smallm_fp8bs_read_floor(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                          _stream(stream)), "smallm_fp8bs_read_floor")
+
+
+def smallm_fp8bs_quant_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K))
+
+
+def _fused(x, w_packed, sw, y, q_dbg, sx_dbg, layout_id, stream, workspace, e8m0):
+    _need(x, _BF, "x")
+    _need(w_packed, _U8, "w_packed")
+    _contig(sw, "sw")
+    M, K = x.shape
+    N = _check_weight(w_packed, sw, K, e8m0)
+    y = _out(y, M, N, x.device)
+    _check_dbg(q_dbg, sx_dbg, M, K, e8m0, x.device)
+    lid = smallm_fp8bs_weight_layout_id(N, K) if layout_id is None else layout_id
+    sfx = "_e8m0" if e8m0 else ""
+    need = smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K)
+    if need and q_dbg is None and sx_dbg is None:
+        # beyond the small-M range: quantisation into a workspace, then the tiled GEMM
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if (workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous()
+                or not workspace.is_cuda or workspace.device != x.device):
+            raise ValueError("workspace must be a contiguous 1-D uint8 tensor on the device of x")
+        fn = getattr(lib(), "smallm_fp8bs_quant_gemm" + sfx + "_ws")
+        _check(fn(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y), y.stride(0), M, N, K,
+                  _ptr(workspace), workspace.numel(), _stream(stream)), "smallm_fp8bs_quant_gemm" + sfx + "_ws")
+        return y
+    fn = getattr(lib(), "smallm_fp8bs_quant_gemm" + sfx)
+    _check(fn(_ptr(x), x.stride(0), _ptr(w_packed), lid, _ptr(sw), _ptr(y), y.stride(0), M, N, K,
+              _ptr(q_dbg), _ptr(sx_dbg), _stream(stream)), "smallm_fp8bs_quant_gemm" + sfx)
+    return y
+
+
+def smallm_fp8bs_quant_gemm(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, layout_id=None, stream=None,
+                            workspace=None):
+    """Fused path: bf16 x [M, K], packed weight [N, K], fp32 sw [N/128, K/128] -> bf16 y [M, N].
+    Beyond 32 rows (without debug copies) it takes the quant + tiled GEMM path through a workspace
+    (allocated here when none is given, smallm_fp8bs_quant_gemm_workspace_bytes long); with q_dbg /
+    sx_dbg it always runs the fused kernel, which writes the quantised bytes and scales it used."""
+    return _fused(x, w_packed, sw, y, q_dbg, sx_dbg, layout_id, stream, workspace, False)
+
+
+def smallm_fp8bs_quant_gemm_e8m0(x, w_packed, sw, y=None, q_dbg=None, sx_dbg=None, layout_id=None, stream=None,
+                                 workspace=None):
+    """As smallm_fp8bs_quant_gemm with e8m0 scales (sw uint8 [N/128, K/128])."""
+    return _fused(x, w_packed, sw, y, q_dbg, sx_dbg, layout_id, stream, workspace, True)
 
 
 def algorithmic_bytes(M: int, N: int, K: int, e8m0: bool = False) -> int:

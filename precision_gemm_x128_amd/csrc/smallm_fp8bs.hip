@@ -555,9 +555,11 @@ __device__ __forceinline__ void flag_set(uint32_t* f, uint32_t v) {
   lds_release();
   __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void flag_wait(uint32_t* f, uint32_t v) {
-  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < v) __builtin_amdgcn_s_sleep(1);
+__device__ __forceinline__ uint32_t flag_wait(uint32_t* f, uint32_t v) {
+  uint32_t x;
+  while ((x = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < v) __builtin_amdgcn_s_sleep(1);
   lds_acquire();
+  return x;  // the count observed (at least v)
 }
 
 // One workgroup per column share of the packed layout (one per CU for the pages' shapes).  K is
@@ -959,157 +961,296 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// GEMM on pre-quantised input beyond the small-M range: MFMA-tiled, for 16-column layouts
+// GEMM on pre-quantised input beyond the small-M range: MFMA-tiled over M and the packed columns
 // ---------------------------------------------------------------------------------------------
 
-constexpr int kTiledFromM = 32;  // M above which the pre-quantised GEMM is tiled
-constexpr int kTM = 32;          // rows per workgroup tile of the tiled kernel
+constexpr int kTiledRegions = 4;  // packed column regions per workgroup (one wave each)
 constexpr int kTiledMaxKB = 128;  // K blocks the tiled kernel takes (e8m0 weight scales in two registers)
-constexpr int kTD = 8;        // weight fragments in flight per wave (K blocks ahead)
-constexpr int kTPitch = 144;  // LDS pitch of a staged 128-byte activation row (conflict-free reads)
+constexpr int kTPitch = 144;      // LDS pitch of a staged 128-byte activation row (conflict-free reads)
 
-// Workgroup tile: TM rows x 64 columns, four waves, wave w owning column group 4 x + w (16
-// columns) for all TM rows.  Per K block the tile's TM x 128 activation bytes and their scales
-// are staged in LDS by the 256 threads (TM / 2 bytes each; two buffers, one barrier per K block);
-// each wave streams its own fragments kTD K blocks ahead and runs one
-// 16x16x128 MFMA per 16-row subtile (the activation bytes are fetched kTD K blocks ahead too).
-// fp32 scales: each K block's partial is multiplied by
-// sx[row, kb] * sw[n/128, kb] into the accumulator; e8m0: the scales are the MFMA's scale
-// operands and one accumulator runs over K.  Every wave owns whole outputs: no reduction.
-template <int TM, bool E8>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(
+constexpr int kTSlots = 8;         // LDS ring of staged K blocks
+
+// Workgroup tile: TM rows x 4 packed column regions (the small-M kernel's per-workgroup column
+// shares: 16 NA + CB columns each).  512 threads in two roles that meet only through LDS counters:
+//   * waves 4..7 (loaders) stage the tile's activation bytes and row scales, K block by K block,
+//     into a ring of kTSlots LDS slots, D blocks of loads ahead in registers; each raises the
+//     slot's ready count after its quarter of the rows, and reuses a slot only after the four
+//     MFMA waves have counted it consumed;
+//   * waves 0..3 (MFMA waves) own one region each and stream its fragments TDW K blocks ahead (the
+//     16-column fragment of every K block; a remainder fragment every SB blocks); per K block and
+//     16-row subtile, one 16x16x128 MFMA on the 16-column fragment and one on the remainder
+//     fragment with the B operand masked to the lanes of that K block (the others are exact
+//     zeros), as the small-M kernel does.
+// fp32 scales: each K block's partial is multiplied by sx[row, kb] * sw[n/128, kb] into the
+// accumulator; e8m0: the scales are the MFMA's scale operands.  A remainder column's SB K-block
+// partials sit in SB neighbouring lanes and are folded at the end in a fixed order.  Every MFMA
+// wave owns whole outputs: no reduction.  A wave of a region past the last mirrors the last one
+// (its loads and counts keep the ring moving) and writes nothing.
+template <int TM, bool E8, int NA, bool HASB, int SB>
+__global__ __launch_bounds__(512) void tiled_gemm_kernel(
     const uint8_t* __restrict__ q, int64_t ldq, const void* __restrict__ sa,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
-    int64_t ldy, int M, int K) {
+    int64_t ldy, int M, int K, int CB, int NWG) {
   constexpr int NSUB = TM / 16;   // 16-row MFMA subtiles
-  constexpr int TPR = 256 / TM;   // staging threads per row
-  constexpr int BPT = 128 / TPR;  // staged bytes per thread
-  constexpr int NLA = BPT / 16;   // 16-byte loads per thread
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][TM * kTPitch];
-  __shared__ uint32_t sS[2][TM];
+  constexpr int TPR = 256 / TM;   // loader threads per row
+  constexpr int BPT = 128 / TPR;  // staged bytes per loader thread and K block
+  constexpr int NLA = BPT / 16;   // 16-byte loads per loader thread and K block
+  constexpr int D = 8;            // K blocks of activation loads in flight per loader
+  constexpr int TDW = 8;          // K blocks of weight fragments in flight per MFMA wave
+  constexpr int BG = 1;           // K blocks an MFMA wave takes per step
+  constexpr int NBS = HASB ? TDW / SB : 1;  // remainder fragment slots
+  constexpr int SLOT = TM * kTPitch + TM * 4;  // staged rows, then their scales
+  static_assert(TDW % SB == 0, "the weight pipeline holds whole remainder fragments");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kTSlots * SLOT];
+  __shared__ uint32_t ready[kTSlots], consumed[kTSlots];
+  __shared__ uint32_t swl[kTiledRegions][2][kTiledMaxKB];  // weight block scales of the 4 regions
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K >> 7;
-  const int cg = blockIdx.x * 4 + wave;
+  // K blocks processed: rounded up to a whole number of pipeline steps, so that every loop
+  // iteration issues the same loads and the waits inside it are exact (the extra blocks are zero
+  // weights and zero activations)
+  const int KBp = (KB + 7) & ~7;
   const int m0 = blockIdx.y * TM;
   const int Mt = min(TM, M - m0);
-  const int nb = (cg * 16) >> 7;
-
-  // the tile's activation rows as a bounds-checked buffer; rows past M and K blocks past the end
-  // use an offset beyond it and read zeros without touching memory
-  const uint32_t abytes = (uint32_t)((int64_t)(Mt - 1) * ldq + K);
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(q + (int64_t)m0 * ldq), 0, (int)abytes, 0x00020000);
-  const uint32_t wbytes = (uint32_t)KB * 2048u;
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(wp + (int64_t)cg * KB * 2048), 0, (int)wbytes, 0x00020000);
-  const int srow = tid / TPR, sch = tid % TPR;  // staging: row and chunk of this thread
-  // per-thread bases: a row past the tile starts beyond the buffers, so every K block of it
-  // reads zeros; the weight offsets of K blocks past the end are beyond their buffer too
-  const uint32_t arow = (srow < Mt) ? (uint32_t)((int64_t)srow * ldq + sch * BPT) : abytes;
-  const uint32_t sbytes = (uint32_t)(Mt * KB) * (E8 ? 1u : 4u);
-  const uint32_t srowb = (srow < Mt) ? (uint32_t)(srow * KB) * (E8 ? 1u : 4u) : sbytes;
-  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)sa + (int64_t)m0 * KB * (E8 ? 1 : 4)), 0, (int)sbytes, 0x00020000);
-
-  u32x4 ab[kTD][NLA];
-  uint32_t asc[kTD];
-  u32x4 wb[kTD][2];
-#define TILED_LOAD_A(slot, kb) do {                                                               \
-    const uint32_t o_ = arow + (uint32_t)(kb) * 128u;                                              \
-    _Pragma("unroll") for (int l_ = 0; l_ < NLA; ++l_)                                             \
-      ab[slot][l_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o_ + 16u * l_, 0, 0)); \
-    const uint32_t so_ = srowb + (uint32_t)(kb) * (E8 ? 1u : 4u);                                 \
-    if (E8) asc[slot] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(srsrc, so_, 0, 0);             \
-    else asc[slot] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, so_, 0, 0);                          \
-  } while (0)
-#define TILED_LOAD_W(slot, kb) do {                                                               \
-    const uint32_t o_ = (uint32_t)(kb) * 2048u + (uint32_t)lane * 16u;                              \
-    wb[slot][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, o_, 0, 2)); \
-    wb[slot][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, o_ + 1024u, 0, 2)); \
-  } while (0)
-
-  // e8m0 weight scales of the column group's row of blocks, one byte per lane (K blocks 0..63 and
-  // 64..127; past the row: zeros), loaded before everything else and taken per K block with
-  // readlane, so no load sits on the MFMA's path
-  uint32_t swb0 = 0u, swb1 = 0u;
-  if (E8) {
-    const __amdgpu_buffer_rsrc_t swsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)sw + (int64_t)nb * KB), 0, KB, 0x00020000);
-    swb0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsrc, (uint32_t)lane, 0, 0);
-    swb1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsrc, (uint32_t)lane + 64u, 0, 0);
+  if (tid < kTSlots) {
+    ready[tid] = 0;
+    consumed[tid] = 0;
   }
-  // prologue in the loop's own issue order (per K block: activation bytes, scale, weights), so
-  // that every wait in the loop counts the same loads behind it
-#pragma unroll
-  for (int d = 0; d < kTD; ++d) {
-    TILED_LOAD_A(d, d);
-    TILED_LOAD_W(d, d);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  v4f acc[NSUB];
-#pragma unroll
-  for (int i = 0; i < NSUB; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  __syncthreads();
 
-  for (int kb0 = 0; kb0 < KB; kb0 += kTD) {
+  if (wave >= 4) {
+    // ---- loaders: the activation tile, K block by K block, into the ring ----
+    const int lt = tid - 256;
+    const int srow = lt / TPR, sch = lt % TPR;
+    const uint32_t abytes = (uint32_t)((int64_t)(Mt - 1) * ldq + K);
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + (int64_t)m0 * ldq), 0, (int)abytes, 0x00020000);
+    const uint32_t arow = (srow < Mt) ? (uint32_t)((int64_t)srow * ldq + sch * BPT) : abytes;
+    const uint32_t sbytes = (uint32_t)(Mt * KB) * (E8 ? 1u : 4u);
+    const uint32_t srowb = (srow < Mt) ? (uint32_t)(srow * KB) * (E8 ? 1u : 4u) : sbytes;
+    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)sa + (int64_t)m0 * KB * (E8 ? 1 : 4)), 0, (int)sbytes, 0x00020000);
+    // loader w also fetches the weight block scales of region 4 x + w (A and remainder rows of
+    // blocks, one per lane, K blocks 0..63 and 64..127) for its MFMA wave, and puts them in LDS
+    // before its first ready count, so the MFMA waves read them from LDS, never from memory
+    const int lw = wave - 4;
+    const int lreg = min((int)blockIdx.x * kTiledRegions + lw, NWG - 1);
+    const int lnbA = (16 * lreg) >> 7, lnbB = (16 * NA * NWG + CB * lreg) >> 7;
+    constexpr uint32_t es = E8 ? 1u : 4u;
+    const __amdgpu_buffer_rsrc_t swsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)sw + (int64_t)lnbA * KB * es), 0, NA ? KB * (int)es : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t swsB = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)sw + (int64_t)lnbB * KB * es), 0, HASB ? KB * (int)es : 0, 0x00020000);
+    uint32_t sv[4];
 #pragma unroll
-    for (int u = 0; u < kTD; ++u) {
-      const int kb = kb0 + u;
-      if (kb >= KB) break;  // uniform
-      const int buf = u & 1;  // kb0 is a multiple of kTD (even): buffer and slots follow u
-      // stage K block kb (its rows' last readers, at kb - 2, are past the previous barrier)
-      u32x4* dst = (u32x4*)(&sA[buf][srow * kTPitch + sch * BPT]);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t k = (uint32_t)lane + 64u * h;
+      sv[h] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsA, k, 0, 0) : __builtin_amdgcn_raw_buffer_load_b32(swsA, k * 4u, 0, 0);
+      sv[2 + h] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsB, k, 0, 0) : __builtin_amdgcn_raw_buffer_load_b32(swsB, k * 4u, 0, 0);
+    }
+    u32x4 ab[D][NLA];
+    uint32_t asc[D];
+    // rows past M and K blocks past the end read zeros past the end of the buffers
+    auto load = [&](int slot, int kb) {
+      const uint32_t o = (kb < KB) ? arow + (uint32_t)kb * 128u : abytes;
 #pragma unroll
-      for (int l = 0; l < NLA; ++l) dst[l] = ab[u][l];
-      sS[buf][srow] = asc[u];  // the threads of a row store the same value
-      __syncthreads();
-      TILED_LOAD_A(u, kb + kTD);
-      const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[u][0], wb[u][1], 0, 1, 2, 3, 4, 5, 6, 7));
-      if (E8) {
-        const int sb = (kb < 64) ? __builtin_amdgcn_readlane((int)swb0, kb) : __builtin_amdgcn_readlane((int)swb1, kb - 64);
+      for (int l = 0; l < NLA; ++l)
+        ab[slot][l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o + 16u * l, 0, 0));
+      const uint32_t so = (kb < KB) ? srowb + (uint32_t)kb * (E8 ? 1u : 4u) : sbytes;
+      asc[slot] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(srsrc, so, 0, 0)
+                     : __builtin_amdgcn_raw_buffer_load_b32(srsrc, so, 0, 0);
+    };
 #pragma unroll
-        for (int i = 0; i < NSUB; ++i) {
-          const int r = i * 16 + (lane & 15);
-          const u32x4* ap = (const u32x4*)(&sA[buf][r * kTPitch + (lane >> 4) * 32]);
-          const u32x4 a0 = ap[0], a1 = ap[1];
-          const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i], 0, 0, 0, (int)sS[buf][r], 0, sb);
-        }
-      } else {
-        const float swv = ((const float*)sw)[nb * KB + kb];
-        v4f fa[NSUB];
+    for (int d = 0; d < D; ++d) load(d, d);
 #pragma unroll
-        for (int i = 0; i < NSUB; ++i) {
-          const int r = i * 16 + (lane & 15);
-          const u32x4* ap = (const u32x4*)(&sA[buf][r * kTPitch + (lane >> 4) * 32]);
-          const u32x4 a0 = ap[0], a1 = ap[1];
-          const v8i a = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          fa[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-        }
+    for (int h = 0; h < 2; ++h) {
+      swl[lw][0][lane + 64 * h] = sv[h];
+      swl[lw][1][lane + 64 * h] = sv[2 + h];
+    }
+    for (int kb0 = 0; kb0 < KBp; kb0 += D) {
 #pragma unroll
-        for (int i = 0; i < NSUB; ++i) {
-          const v4f sx4 = v4f{__uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 0]),
-                              __uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 1]),
-                              __uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 2]),
-                              __uint_as_float(sS[buf][i * 16 + 4 * (lane >> 4) + 3])};
+      for (int u = 0; u < D; ++u) {
+        const int kb = kb0 + u;
+        {
+          const int sl = kb % kTSlots, gen = kb / kTSlots;
+          if (gen > 0) flag_wait(&consumed[sl], 4u * (uint32_t)gen);  // the slot's last block is read
+          uint8_t* slot = ring + sl * SLOT;
+          u32x4* dst = (u32x4*)(slot + srow * kTPitch + sch * BPT);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_fmaf(sx4[e] * swv, fa[i][e], acc[i][e]);
+          for (int l = 0; l < NLA; ++l) dst[l] = ab[u][l];
+          if (sch == 0) ((uint32_t*)(slot + TM * kTPitch))[srow] = asc[u];
+          lds_release();
+          if (lane == 0) __hip_atomic_fetch_add(&ready[sl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          load(u, kb + D);
         }
       }
-      TILED_LOAD_W(u, kb + kTD);
+    }
+    return;
+  }
+
+  // ---- MFMA waves: one packed region each ----
+  const int reg = min((int)blockIdx.x * kTiledRegions + wave, NWG - 1);
+  const bool owner = (int)(blockIdx.x * kTiledRegions + wave) < NWG;
+  const int cols = 16 * NA + CB;
+  const int NB = HASB ? CB * SB : 16;  // B columns of a remainder fragment
+  const int jl = lane & 15;
+  const int sl = jl & (SB - 1);        // K block of this lane within a remainder fragment
+  const bool bcol = jl < NB;
+  const uint8_t* wreg = wp + (int64_t)reg * cols * K;
+  const uint32_t wabytes = (uint32_t)(NA * KB) * 2048u;
+  const uint32_t fbytes = (uint32_t)NB * 128u;
+  const uint32_t wbbytes = HASB ? (uint32_t)(KB / SB) * fbytes : 0u;
+  const __amdgpu_buffer_rsrc_t wrA = __builtin_amdgcn_make_buffer_rsrc((void*)wreg, 0, (int)wabytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrB = __builtin_amdgcn_make_buffer_rsrc((void*)(wreg + wabytes), 0, (int)wbbytes, 0x00020000);
+  const uint32_t boff = bcol ? (uint32_t)(((lane >> 4) * NB + jl) * 16) : wbbytes;
+  const int nbA = (16 * reg) >> 7;                    // 128-column block of the 16-column group
+  const int nbB = (16 * NA * NWG + CB * reg) >> 7;    // and of the remainder group
+  u32x4 wa[TDW][2], wb[NBS][2];
+  // weight loads through the caches (not non-temporal): the row tiles of one column tile run on
+  // one XCD and read the same fragments, so all but the first are L2 hits
+  auto load_wa = [&](int slot, int kb) {
+    if (NA) {
+      const uint32_t o = (kb < KB) ? (uint32_t)kb * 2048u + (uint32_t)lane * 16u : wabytes;
+      wa[slot][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, o, 0, 0));
+      wa[slot][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrA, o + 1024u, 0, 0));
+    }
+  };
+  auto load_wb = [&](int slot, int f) {
+    if (HASB) {
+      const uint32_t o = (f * SB < KB && bcol) ? (uint32_t)f * fbytes + boff : wbbytes;
+      wb[slot][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, o, 0, 0));
+      wb[slot][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, o + (fbytes >> 1), 0, 0));
+    }
+  };
+  const uint32_t* swr = &swl[wave][0][0];  // this region's weight block scales (LDS, from its loader)
+#pragma unroll
+  for (int d = 0; d < TDW; ++d) {
+    load_wa(d, d);
+    if (d % SB == 0) load_wb(d / SB, d / SB);
+  }
+  v4f accA[NSUB], accB[NSUB];
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) {
+    accA[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    accB[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // K blocks in steps of BG, each step's operands read, multiplied and scaled together
+  for (int kb0 = 0; kb0 < KBp; kb0 += TDW) {
+#pragma unroll
+    for (int u = 0; u < TDW; u += BG) {
+      const int kb = kb0 + u;
+      {
+        v8i at[BG][NSUB];
+        int sar[BG][NSUB];
+        v4f sx4[BG][NSUB];
+        v8i bA[BG], bB[BG];
+        int ea[BG], eb[BG];
+        // the step's last block staged by all four loaders (each stages in order, so the earlier
+        // ones are too)
+        flag_wait(&ready[(kb + BG - 1) % kTSlots], 4u * (uint32_t)((kb + BG - 1) / kTSlots + 1));
+#pragma unroll
+        for (int h = 0; h < BG; ++h) {
+          const int s = (kb + h) % kTSlots;
+          const uint8_t* slot = ring + s * SLOT;
+          const uint32_t* ss = (const uint32_t*)(slot + TM * kTPitch);
+#pragma unroll
+          for (int i = 0; i < NSUB; ++i) {
+            const int r = i * 16 + jl;
+            const u32x4* ap = (const u32x4*)(slot + r * kTPitch + (lane >> 4) * 32);
+            const u32x4 a0 = ap[0], a1 = ap[1];
+            at[h][i] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            if (E8) sar[h][i] = (int)ss[r];
+            else sx4[h][i] = *(const v4f*)(ss + i * 16 + 4 * (lane >> 4));
+          }
+          bA[h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          bB[h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          if (NA) bA[h] = __builtin_bit_cast(v8i, __builtin_shufflevector(wa[u + h][0], wa[u + h][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (HASB) {
+            bB[h] = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[(u + h) / SB][0], wb[(u + h) / SB][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            if (SB > 1) {
+              const uint32_t bmask = (sl == (u + h) % SB) ? 0xFFFFFFFFu : 0u;  // lanes of this K block
+#pragma unroll
+              for (int d = 0; d < 8; ++d) bB[h][d] = (int)((uint32_t)bB[h][d] & bmask);
+            }
+          }
+          const int k = kb + h;  // past the row: the loader stored zeros
+          ea[h] = NA ? (int)swr[k] : 0;
+          eb[h] = HASB ? (int)swr[kTiledMaxKB + k] : 0;
+        }
+        if (E8) {
+#pragma unroll
+          for (int h = 0; h < BG; ++h)
+#pragma unroll
+            for (int i = 0; i < NSUB; ++i) {
+              if (NA) accA[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bA[h], accA[i], 0, 0, 0, sar[h][i], 0, ea[h]);
+              if (HASB) accB[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bB[h], accB[i], 0, 0, 0, sar[h][i], 0, eb[h]);
+            }
+        } else {
+#pragma unroll
+          for (int h = 0; h < BG; ++h) {
+            v4f fa[NSUB], fb[NSUB];
+#pragma unroll
+            for (int i = 0; i < NSUB; ++i) {
+              if (NA) fa[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bA[h], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                                0, 0, 0, 127, 0, 127);
+              if (HASB) fb[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bB[h], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                                  0, 0, 0, 127, 0, 127);
+            }
+            const float swA = __int_as_float(ea[h]), swB = __int_as_float(eb[h]);  // the fp32 scales' bits
+#pragma unroll
+            for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (NA) accA[i][e] = __builtin_fmaf(sx4[h][i][e] * swA, fa[i][e], accA[i][e]);
+                if (HASB) accB[i][e] = __builtin_fmaf(sx4[h][i][e] * swB, fb[i][e], accB[i][e]);
+              }
+          }
+        }
+        // the step's results join the accumulators in the MFMAs' own basic block
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i) asm volatile("" : "+v"(accA[i]), "+v"(accB[i]));
+        lds_release();  // this wave's reads of the step's slots are done
+        if (lane == 0) {
+#pragma unroll
+          for (int h = 0; h < BG; ++h)
+            __hip_atomic_fetch_add(&consumed[(kb + h) % kTSlots], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+#pragma unroll
+        for (int h = 0; h < BG; ++h) {
+          load_wa(u + h, kb + h + TDW);
+          if ((u + h) % SB == SB - 1) load_wb((u + h) / SB, (kb + h + TDW) / SB);  // the slot's last use was this block
+        }
+      }
     }
   }
-#undef TILED_LOAD_A
-#undef TILED_LOAD_W
-  // output: lane l holds column l % 16 of the wave's group, rows 4 (l / 16) + e of each subtile
-  const int col = cg * 16 + (lane & 15);
+  // 16 wait states on every path before the accumulators are read (the loop ends in branches)
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i)
+  for (int i = 0; i < NSUB; ++i) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(accA[i]), "+v"(accB[i]));
+  if (!owner) return;
+  // output: lane l holds MFMA column l % 16, rows 4 (l / 16) + e of each subtile
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) {
+    v4f pb = accB[i];
+    if (HASB && SB > 1) {
+      // the SB K-block partials of a remainder column sit in SB neighbouring lanes: fold them
+      // into the first, in a fixed order
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] += dpp_f32_xor1(pb[e]);
+        if (SB > 2) pb[e] += dpp_f32_xor2(pb[e]);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = i * 16 + 4 * (lane >> 4) + e;
-      if (r < Mt) y[(int64_t)(m0 + r) * ldy + col] = bf16_rne(acc[i][e]);
+      if (r < Mt) {
+        if (NA) y[(int64_t)(m0 + r) * ldy + 16 * reg + jl] = bf16_rne(accA[i][e]);
+        if (HASB && bcol && sl == 0)
+          y[(int64_t)(m0 + r) * ldy + 16 * NA * NWG + CB * reg + jl / SB] = bf16_rne(pb[e]);
+      }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1263,11 +1404,56 @@ void launch_mt(const Layout& L, int K, dim3 grid, hipStream_t stream, const void
 #undef SMALLM_K
 }
 
+constexpr int kTiledFromM = 32;  // M above which the pre-quantised GEMM is tiled
+
+// Rows per workgroup tile of the tiled kernel at M rows.
+int tiled_tm(int M) { return M <= 64 ? 32 : 64; }
+
+// The tiled kernel takes the shape: at most 128 K blocks (its e8m0 weight scales sit in two
+// registers) and a tile's activation rows inside a 32-bit buffer offset.
+bool tiled_ok(int M, int K, int64_t ldq) {
+  return M > kTiledFromM && K / 128 <= kTiledMaxKB &&
+         (ldq * (tiled_tm(M) - 1) + K) < ((int64_t)1 << 31);
+}
+
+template <bool E8, int TM>
+void launch_tiled_tm(const Layout& L, int M, int K, const uint8_t* q, int64_t ldq, const void* sa,
+                     const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  const dim3 grid((L.nwg + kTiledRegions - 1) / kTiledRegions, (M + TM - 1) / TM);
+#define TILED_K(na, hasb, sb)                                                                        \
+  hipLaunchKernelGGL((tiled_gemm_kernel<TM, E8, na, hasb, sb>), grid, dim3(512), 0, stream, q, ldq, \
+                     sa, wp, sw, y, ldy, M, K, L.cb, L.nwg)
+  if (L.cb == 0) TILED_K(1, false, 1);
+  else if (L.na == 1) {
+    if (L.sb == 1) TILED_K(1, true, 1);
+    else if (L.sb == 2) TILED_K(1, true, 2);
+    else TILED_K(1, true, 4);
+  } else {
+    if (L.sb == 1) TILED_K(0, true, 1);
+    else if (L.sb == 2) TILED_K(0, true, 2);
+    else TILED_K(0, true, 4);
+  }
+#undef TILED_K
+}
+
+template <bool E8>
+void launch_tiled(const Layout& L, int M, int K, const uint8_t* q, int64_t ldq, const void* sa,
+                  const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  if (tiled_tm(M) == 32) launch_tiled_tm<E8, 32>(L, M, K, q, ldq, sa, wp, sw, y, ldy, stream);
+  else launch_tiled_tm<E8, 64>(L, M, K, q, ldq, sa, wp, sw, y, ldy, stream);
+}
+
 template <int MODE>
 int launch_gemm(const void* a, int64_t lda, const void* sa, const uint8_t* wp, const void* sw,
                 uint16_t* y, int64_t ldy, int M, int N, int K, uint8_t* q_dbg, void* sx_dbg,
                 hipStream_t stream) {
   const Layout L = layout_for(N, K);
+  if ((MODE & 2) && tiled_ok(M, K, lda)) {
+    // pre-quantised input beyond the small-M range: every weight fragment is read by
+    // ceil(M / TM) workgroups instead of ceil(M / 32) small-M workgroups
+    launch_tiled<(MODE & 1) != 0>(L, M, K, (const uint8_t*)a, lda, sa, wp, sw, y, ldy, stream);
+    return launch_status();
+  }
   const int MT = (M <= 16) ? 1 : 2;
   const int MP = 16 * MT;
   const dim3 grid(L.nwg, (M + MP - 1) / MP);
@@ -1487,6 +1673,61 @@ int smallm_fp8bs_quant_gemm_e8m0(const uint16_t* x, int64_t ldx, const uint8_t* 
   if (q_dbg && !aligned16(q_dbg)) return SMALLM_ERR_ALIGN;
   return launch_gemm<kFusedE8>(x, ldx, nullptr, w_packed, sw_e8m0, y, ldy, M, N, K, q_dbg,
                                (void*)sx_dbg_e8m0, (hipStream_t)stream);
+}
+
+// Rows up to which the fused kernel (in 32-row chunks above 32) beats the standalone quantisation
+// plus the tiled GEMM: measured on the pages' shapes (5120x4096, 4608x4096, 4096x2048, 2048x4096),
+// graph replay over 24 cold weight copies -- at 33 rows the two 32-row chunks are faster on all
+// four, from 48 rows the quant + tiled pair.
+constexpr int kFusedUpToM = 40;
+
+size_t smallm_fp8bs_quant_gemm_workspace_bytes(int M, int N, int K) {
+  if (check_mnk(M, N, K) != SMALLM_OK || M <= kFusedUpToM || !tiled_ok(M, K, K)) return 0;
+  const size_t qb = ((size_t)M * K + 255) / 256 * 256;
+  return qb + (size_t)M * (K / 128) * 4;
+}
+
+// Beyond the small-M range with a workspace: the standalone quantisation into the workspace (q
+// at pitch K, then the scales 256-byte aligned), then the tiled GEMM on it.  Otherwise the fused
+// kernel (in 32-row chunks above 32 rows).
+static int quant_gemm_ws(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, uint32_t layout_id,
+                         const void* sw, uint16_t* y, int64_t ldy, int M, int N, int K, void* workspace,
+                         size_t workspace_bytes, bool e8, void* stream) {
+  int st = check_gemm_args(x, ldx, 2, nullptr, false, w_packed, layout_id, sw, y, ldy, M, N, K);
+  if (st) return st;
+  const size_t need = smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K);
+  if (need == 0) {
+    return e8 ? launch_gemm<kFusedE8>(x, ldx, nullptr, w_packed, sw, y, ldy, M, N, K, nullptr, nullptr,
+                                      (hipStream_t)stream)
+              : launch_gemm<kFusedF32>(x, ldx, nullptr, w_packed, sw, y, ldy, M, N, K, nullptr, nullptr,
+                                       (hipStream_t)stream);
+  }
+  if (!workspace) return SMALLM_ERR_INVALID;
+  if (workspace_bytes < need) return SMALLM_ERR_SHAPE;
+  if (((uintptr_t)workspace & 255) != 0) return SMALLM_ERR_ALIGN;
+  uint8_t* q = (uint8_t*)workspace;
+  void* sx = q + ((size_t)M * K + 255) / 256 * 256;
+  st = quant_common(x, ldx, q, K, sx, M, K, e8, stream);
+  if (st) return st;
+  const Layout L = layout_for(N, K);
+  if (e8) launch_tiled<true>(L, M, K, q, K, sx, w_packed, sw, y, ldy, (hipStream_t)stream);
+  else launch_tiled<false>(L, M, K, q, K, sx, w_packed, sw, y, ldy, (hipStream_t)stream);
+  return launch_status();
+}
+
+int smallm_fp8bs_quant_gemm_ws(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                               uint32_t layout_id, const float* sw, uint16_t* y, int64_t ldy, int M,
+                               int N, int K, void* workspace, size_t workspace_bytes, void* stream) {
+  return quant_gemm_ws(x, ldx, w_packed, layout_id, sw, y, ldy, M, N, K, workspace, workspace_bytes,
+                       false, stream);
+}
+
+int smallm_fp8bs_quant_gemm_e8m0_ws(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                    uint32_t layout_id, const uint8_t* sw_e8m0, uint16_t* y,
+                                    int64_t ldy, int M, int N, int K, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return quant_gemm_ws(x, ldx, w_packed, layout_id, sw_e8m0, y, ldy, M, N, K, workspace,
+                       workspace_bytes, true, stream);
 }
 
 }  // extern "C"

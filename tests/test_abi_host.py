@@ -76,7 +76,7 @@ def test_launch_plans_balance_the_cus():
 
 
 def test_version_layout_and_strerror():
-    assert P.smallm_fp8bs_abi_version() == 6
+    assert P.smallm_fp8bs_abi_version() == 7
     # 0x46390000 | NA << 12 | CB << 4 | SB
     assert P.smallm_fp8bs_weight_layout_id(4096, 2048) == 0x46391001
     assert P.smallm_fp8bs_weight_layout_id(5120, 4096) == 0x46391044
@@ -89,6 +89,24 @@ def test_version_layout_and_strerror():
     for s in range(6):
         assert len(P.strerror(s)) > 0
     assert P.strerror(99) == "unknown status"
+
+
+def test_workspace_entry_sizes_and_host_checks():
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(32, 4096, 2048) == 0      # the fused kernel
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(40, 4096, 2048) == 0      # two fused chunks
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(41, 4096, 2048) == (41 * 2048 + 255) // 256 * 256 + 41 * 16 * 4
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(256, 5120, 4096) == 256 * 4096 + 256 * 32 * 4
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(64, 4096, 128 * 129) == 0   # K past the tiled kernel
+    L = P.lib()
+    fake = ctypes.c_void_p(0x100000)          # never dereferenced: every case fails a host check
+    M, N, K = 64, 4096, 2048
+    lid = P.smallm_fp8bs_weight_layout_id(N, K)
+    need = P.smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K)
+    for fn in (L.smallm_fp8bs_quant_gemm_ws, L.smallm_fp8bs_quant_gemm_e8m0_ws):
+        assert fn(fake, K, fake, lid, fake, fake, N, M, N, K, None, need, None) == 1
+        assert fn(fake, K, fake, lid, fake, fake, N, M, N, K, fake, need - 1, None) == 2
+        assert fn(fake, K, fake, lid, fake, fake, N, M, N, K, ctypes.c_void_p(0x100010), need, None) == 3
+        assert fn(fake, K, fake, lid + 1, fake, fake, N, M, N, K, fake, need, None) == 4
 
 
 def test_read_floor_rejects_bad_arguments_before_launch():

@@ -45,6 +45,16 @@ def test_check_dbg_validates_both_copies():
         P._check_dbg(None, torch.zeros((4, 2), dtype=torch.float32), 4, 256, True, torch.device("cpu"))
 
 
+def test_binding_wraps_the_entry_points():
+    # every C entry point the header declares is reachable from Python: a wrapper of the same name,
+    # or (the workspace variants) through the wrapper that dispatches to it
+    via = {"smallm_fp8bs_quant_gemm_ws": "smallm_fp8bs_quant_gemm",
+           "smallm_fp8bs_quant_gemm_e8m0_ws": "smallm_fp8bs_quant_gemm_e8m0",
+           "smallm_fp8bs_strerror": "strerror"}
+    for name in P.EXPORTS:
+        assert callable(getattr(P, via.get(name, name), None)), name
+
+
 def test_need_rejects_host_activations():
     with pytest.raises(ValueError, match="device tensor"):
         P._need(torch.zeros((4, 256), dtype=torch.bfloat16), (torch.bfloat16,), "x")

@@ -412,6 +412,38 @@ def test_config_beyond_small_m(M):
     assert_within_tol(y2, ref, what=f"prequantised M={M}")
 
 
+@pytest.mark.parametrize("e8m0", [False, True])
+@pytest.mark.parametrize("M", [41, 64, 256])
+@pytest.mark.parametrize("N,K", [(5120, 4096), (4608, 4096), (4096, 2048), (2048, 4096)])
+def test_beyond_small_m_every_layout(N, K, M, e8m0):
+    """Past the small-M cap on each packed layout (16-column groups; 16 + 4, 16 + 2 and 8-column
+    remainder groups): the fused entry (quantisation into a workspace, then the tiled GEMM) over
+    the full output against the oracle, bit-equal to the two launches through the C entry points,
+    and the fused kernel's 32-row chunks (no workspace) within the same tolerance."""
+    note(f"beyond small M N={N} K={K} M={M} e8m0={e8m0}")
+    w8, sw, wp, swd = prepared_weight(N, K, seed=9, e8m0=e8m0)
+    x = synthgen.gen_x(M, K, seed=M + 3, outliers=True)
+    q_ref, sx_ref, ref = oracle_ref(x, w8, sw, e8m0, [(0, N)])
+    xd = to_dev_bf16(x)
+    y = fused_fn(e8m0)(xd, wp, swd)
+    qf = P.smallm_fp8bs_quant_e8m0 if e8m0 else P.smallm_fp8bs_quant
+    gf = P.smallm_fp8bs_gemm_e8m0 if e8m0 else P.smallm_fp8bs_gemm
+    q, sx = qf(xd)
+    y2 = gf(q, sx, wp, swd)
+    # the fused kernel in 32-row chunks: the C entry without a workspace
+    y3 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    fn = P.lib().smallm_fp8bs_quant_gemm_e8m0 if e8m0 else P.lib().smallm_fp8bs_quant_gemm
+    st = fn(P._ptr(xd), xd.stride(0), P._ptr(wp), P.smallm_fp8bs_weight_layout_id(N, K), P._ptr(swd), P._ptr(y3),
+            N, M, N, K, None, None, P._stream())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K) > 0
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert_within_tol(y, ref, what=f"fused N={N} K={K} M={M} e8m0={e8m0}")
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert_within_tol(y3, ref, what=f"fused chunks N={N} K={K} M={M} e8m0={e8m0}")
+
+
 @pytest.mark.parametrize("N,K", [(4096, 2048), (2048, 4096)])
 def test_config_e8m0_beside_fp32(N, K):
     """Power-of-two scales (weights rounded, activations rounded up, as e8m0 bytes) at M in
@@ -515,7 +547,8 @@ def test_two_kernel_path(M, e8m0):
 PREQ_CASES = [
     # (N, K, M): the GEMM on pre-quantised input beyond the small-M range
     (384, 640, 33), (384, 640, 100), (4096, 128, 64), (4096, 2048, 48), (4096, 2048, 256),
-    (4096, 4736, 77), (5120, 4096, 40), (2048, 4096, 96),
+    (4096, 4736, 77), (5120, 4096, 40), (2048, 4096, 96), (4608, 4096, 65), (4608, 640, 200),
+    (5120, 2048, 129), (1024, 12416, 48),
 ]
 
 
