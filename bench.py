@@ -190,7 +190,7 @@ def producer_pipeline(P, torch, np, synthgen, dev, copies, reps, N=5120, K=4096)
 
 def two_launch_beyond(P, torch, np, synthgen, dev, copies, reps, Ms, N=4096, K=2048):
     """Beyond the small-M range: the standalone quantisation, then the GEMM on pre-quantised
-    input (the MFMA-tiled kernel for this 16-column layout), each alone and back to back."""
+    input (the MFMA-tiled kernel), each alone and back to back."""
     wps, sws = [], []
     for i in range(copies):
         w = torch.from_numpy(synthgen.gen_w(N, K, seed=0, copy=i)).to(dev)
@@ -216,6 +216,52 @@ def two_launch_beyond(P, torch, np, synthgen, dev, copies, reps, Ms, N=4096, K=2
     del wps, sws
     torch.cuda.empty_cache()
     return d
+
+
+def crossover_beyond(P, torch, np, synthgen, dev, copies, reps):
+    """Past 32 rows on each of the pages' shapes: the fused kernel in 32-row chunks (the C entry
+    without a workspace) against the standalone quantisation plus the tiled GEMM (the workspace
+    entry), and the rows from which the library takes the second (the fused Python entry)."""
+    import ctypes
+    L = P.lib()
+    res = {}
+    for N, K in ((5120, 4096), (4608, 4096), (4096, 2048), (2048, 4096)):
+        wps, sws = [], []
+        for i in range(copies):
+            w = torch.from_numpy(synthgen.gen_w(N, K, seed=0, copy=i)).to(dev)
+            w8, sw = P.smallm_fp8bs_quant_weight(w)
+            wps.append(P.smallm_fp8bs_pack_weight(w8))
+            sws.append(sw)
+            del w, w8
+        lid = P.smallm_fp8bs_weight_layout_id(N, K)
+        d = {}
+        for M in (33, 48, 64, 128, 256):
+            x = torch.from_numpy(synthgen.gen_x(M, K, seed=0).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            need = P.smallm_fp8bs_quant_gemm_workspace_bytes(max(M, 41), N, K)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def chunks(i):
+                st = L.smallm_fp8bs_quant_gemm(P._ptr(x), K, P._ptr(wps[i]), lid, P._ptr(sws[i]), P._ptr(y), N, M, N, K,
+                                               None, None, P._stream())
+                assert st == 0, st
+
+            def two(i):
+                # the workspace entry's second path, called directly (it takes it from 41 rows)
+                q = ws[: M * K].view(M, K)
+                sx = ws[(M * K + 255) // 256 * 256:][: M * (K // 128) * 4].view(torch.float32).view(M, K // 128)
+                P.smallm_fp8bs_quant(x, q=q, sx=sx)
+                P.smallm_fp8bs_gemm(q, sx, wps[i], sws[i], y=y)
+            tc = graph_us(torch, chunks, copies, reps)
+            tt = graph_us(torch, two, copies, reps)
+            d[str(M)] = {"fused_32_row_chunks_us": round(tc, 3), "quant_then_tiled_us": round(tt, 3),
+                         "library_takes": "quant_then_tiled" if P.smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K) else "fused_32_row_chunks"}
+        res[f"{N}x{K}"] = d
+        log(f"[bench] {N}x{K} beyond 32 rows (chunks / quant+tiled): " +
+            " ".join(f"M={M} {d[str(M)]['fused_32_row_chunks_us']:.1f}/{d[str(M)]['quant_then_tiled_us']:.1f}" for M in (33, 48, 64, 128, 256)))
+        del wps, sws
+        torch.cuda.empty_cache()
+    return res
 
 
 def moe_sweeps(P, torch, np, synthgen, dev, reps, layers=MOE_LAYERS):
@@ -329,6 +375,7 @@ def config_sweeps(P, torch, np, synthgen, dev, copies, reps):
     res["beyond_small_m_4096x2048"] = d
     log("[bench] 4096x2048 M>32: " + " ".join(f"M={M} {t[M]:.2f}us" for M in big))
     res["beyond_small_m_4096x2048_two_launch"] = two_launch_beyond(P, torch, np, synthgen, dev, copies, reps, big)
+    res["beyond_small_m_crossover"] = crossover_beyond(P, torch, np, synthgen, dev, copies, reps)
     for N, K in ((4096, 2048), (2048, 4096)):
         ms = [1, 8, 32]
         tf, yf = time_config(P, torch, np, synthgen, dev, N, K, ms, copies, reps)
@@ -361,6 +408,9 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times): the "
                          "reference kernel for scaling HBM byte counters, then exit")
+    ap.add_argument("--beyond-only", action="store_true",
+                    help="only time the paths past 32 rows on the pages' shapes (fused chunks against quant + "
+                         "tiled GEMM) and print them as JSON")
     ap.add_argument("--only-m", type=int, default=0,
                     help="profiling runs: time this one M of the sweep only (no configs, no CPU leg)")
     ap.add_argument("--moe-only", action="store_true",
@@ -398,6 +448,10 @@ def main():
     P.lib()
     if args.moe_only:
         print(json.dumps({"moe": moe_sweeps(P, torch, np, synthgen, dev, max(1, args.reps))}))
+        return
+    if args.beyond_only:
+        print(json.dumps({"beyond_small_m_crossover": crossover_beyond(P, torch, np, synthgen, dev, copies,
+                                                                         max(1, args.reps))}))
         return
 
     # ---- inputs: 24 cold weight copies, quantised and packed on the device (load-time work) ----
