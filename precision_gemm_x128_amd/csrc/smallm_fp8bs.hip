@@ -964,134 +964,136 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
 // GEMM on pre-quantised input beyond the small-M range: MFMA-tiled over M and the packed columns
 // ---------------------------------------------------------------------------------------------
 
-constexpr int kTiledRegions = 4;  // packed column regions per workgroup (one wave each)
+constexpr int kTiledRegions = 4;  // packed column regions per workgroup
 constexpr int kTiledMaxKB = 128;  // K blocks the tiled kernel takes (e8m0 weight scales in two registers)
-constexpr int kTPitch = 144;      // LDS pitch of a staged 128-byte activation row (conflict-free reads)
+constexpr int kTThreads = 512;    // 8 waves: region w % 4, K half w / 4
+constexpr int kTP = 4;            // steps of loads in flight ahead of the one in use
 
-constexpr int kTSlots = 8;         // LDS ring of staged K blocks
+// Byte position of 16-byte chunk c of staged row r: rows are 128 bytes in LDS, chunks XOR-swizzled
+// so that the MFMA operand reads (16 rows at a time, two chunks per lane) hit distinct banks both
+// 8 and 16 lanes per LDS cycle.
+__device__ __forceinline__ int tswz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
 // Workgroup tile: TM rows x 4 packed column regions (the small-M kernel's per-workgroup column
-// shares: 16 NA + CB columns each).  512 threads in two roles that meet only through LDS counters:
-//   * waves 4..7 (loaders) stage the tile's activation bytes and row scales, K block by K block,
-//     into a ring of kTSlots LDS slots, D blocks of loads ahead in registers; each raises the
-//     slot's ready count after its quarter of the rows, and reuses a slot only after the four
-//     MFMA waves have counted it consumed;
-//   * waves 0..3 (MFMA waves) own one region each and stream its fragments TDW K blocks ahead (the
-//     16-column fragment of every K block; a remainder fragment every SB blocks); per K block and
-//     16-row subtile, one 16x16x128 MFMA on the 16-column fragment and one on the remainder
-//     fragment with the B operand masked to the lanes of that K block (the others are exact
-//     zeros), as the small-M kernel does.
-// fp32 scales: each K block's partial is multiplied by sx[row, kb] * sw[n/128, kb] into the
-// accumulator; e8m0: the scales are the MFMA's scale operands.  A remainder column's SB K-block
-// partials sit in SB neighbouring lanes and are folded at the end in a fixed order.  Every MFMA
-// wave owns whole outputs: no reduction.  A wave of a region past the last mirrors the last one
-// (its loads and counts keep the ring moving) and writes nothing.
+// shares: 16 NA + CB columns each).  K is cut into two halves of KBh blocks (zero-padded); wave w
+// multiplies region w % 4 over half w / 4, and all eight waves walk their halves in lockstep,
+// one step (block s of each half) at a time, meeting at one hardware barrier per step:
+//   * activations: every wave loads its share of a step's two TM x 128-byte blocks into registers
+//     kTP steps ahead (16 bytes a lane, a wave-wide load covering 8 whole rows) and writes them
+//     into one of two LDS slots one step ahead; the barrier publishes them, and also means every
+//     wave is done with the previous step, whose slot the next writes reuse;
+//   * weights: each wave streams its region's fragments of its half kTP steps ahead into
+//     registers (16-column fragment per block, a remainder fragment per SB blocks);
+//   * per step and 16-row subtile, one 16x16x128 MFMA on the 16-column fragment and one on the
+//     remainder fragment with the B operand masked to the lanes of that K block (the others are
+//     exact zeros), as the small-M kernel does.
+// Scales: every row scale of the tile and the regions' weight block scales are put into LDS at
+// the start.  fp32: each block's partial is multiplied by sx[row, kb] * sw[n/128, kb] into the
+// accumulator; e8m0: the scales are the MFMA's scale operands.  At the end the second half's
+// waves hand their accumulators to the first half's through LDS (first + second), which fold a
+// remainder column's SB K-block partials (neighbouring lanes) in a fixed order and write the
+// outputs.  The waves of a region past the last mirror the last one and write nothing.
 template <int TM, bool E8, int NA, bool HASB, int SB>
-__global__ __launch_bounds__(512) void tiled_gemm_kernel(
+__global__ __launch_bounds__(kTThreads) void tiled_gemm_kernel(
     const uint8_t* __restrict__ q, int64_t ldq, const void* __restrict__ sa,
     const uint8_t* __restrict__ wp, const void* __restrict__ sw, uint16_t* __restrict__ y,
     int64_t ldy, int M, int K, int CB, int NWG) {
-  constexpr int NSUB = TM / 16;   // 16-row MFMA subtiles
-  constexpr int TPR = 256 / TM;   // loader threads per row
-  constexpr int BPT = 128 / TPR;  // staged bytes per loader thread and K block
-  constexpr int NLA = BPT / 16;   // 16-byte loads per loader thread and K block
-  constexpr int D = 8;            // K blocks of activation loads in flight per loader
-  constexpr int TDW = 8;          // K blocks of weight fragments in flight per MFMA wave
-  constexpr int BG = 1;           // K blocks an MFMA wave takes per step
-  constexpr int NBS = HASB ? TDW / SB : 1;  // remainder fragment slots
-  constexpr int SLOT = TM * kTPitch + TM * 4;  // staged rows, then their scales
-  static_assert(TDW % SB == 0, "the weight pipeline holds whole remainder fragments");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kTSlots * SLOT];
-  __shared__ uint32_t ready[kTSlots], consumed[kTSlots];
-  __shared__ uint32_t swl[kTiledRegions][2][kTiledMaxKB];  // weight block scales of the 4 regions
+  constexpr int NSUB = TM / 16;           // 16-row MFMA subtiles
+  constexpr int NLD = TM / 32;            // activation loads per wave and step (2 TM x 8 chunks)
+  constexpr int SXP = TM + 4;             // LDS pitch of a K block's row scales (16-byte aligned)
+  constexpr int HALF = TM * 128;          // bytes of one staged K block
+  constexpr int SLOT = 2 * HALF;          // one step: block s of each half
+  constexpr int P = kTP;
+  constexpr int UJ = 2 * P;               // steps per loop iteration (the register slots cycle whole)
+  // remainder fragment slots: a fragment is loaded P steps before its first block, while the
+  // slot's previous fragment may still be in use (two sets of P / SB when SB > 1)
+  constexpr int NBS = !HASB ? 1 : SB == 1 ? P : 2 * P / SB;
+  static_assert(P % SB == 0, "remainder fragments are loaded at whole-fragment steps");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sxs[kTiledMaxKB * SXP];  // row scales, [kb][row]
+  __shared__ uint32_t swl[kTiledRegions][2][kTiledMaxKB];                  // weight block scales
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave & 3, kh = wave >> 2;  // region in the tile, K half
   const int KB = K >> 7;
-  // K blocks processed: rounded up to a whole number of pipeline steps, so that every loop
-  // iteration issues the same loads and the waits inside it are exact (the extra blocks are zero
-  // weights and zero activations)
-  const int KBp = (KB + 7) & ~7;
+  // blocks per half: a whole number of loop iterations (the padded blocks are zero weights and
+  // zero activations)
+  const int KBh = ((KB + 1) / 2 + UJ - 1) / UJ * UJ;
   const int m0 = blockIdx.y * TM;
   const int Mt = min(TM, M - m0);
-  if (tid < kTSlots) {
-    ready[tid] = 0;
-    consumed[tid] = 0;
-  }
-  __syncthreads();
+  constexpr uint32_t es = E8 ? 1u : 4u;
 
-  if (wave >= 4) {
-    // ---- loaders: the activation tile, K block by K block, into the ring ----
-    const int lt = tid - 256;
-    const int srow = lt / TPR, sch = lt % TPR;
-    const uint32_t abytes = (uint32_t)((int64_t)(Mt - 1) * ldq + K);
-    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (int64_t)m0 * ldq), 0, (int)abytes, 0x00020000);
-    const uint32_t arow = (srow < Mt) ? (uint32_t)((int64_t)srow * ldq + sch * BPT) : abytes;
-    const uint32_t sbytes = (uint32_t)(Mt * KB) * (E8 ? 1u : 4u);
-    const uint32_t srowb = (srow < Mt) ? (uint32_t)(srow * KB) * (E8 ? 1u : 4u) : sbytes;
-    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)sa + (int64_t)m0 * KB * (E8 ? 1 : 4)), 0, (int)sbytes, 0x00020000);
-    // loader w also fetches the weight block scales of region 4 x + w (A and remainder rows of
-    // blocks, one per lane, K blocks 0..63 and 64..127) for its MFMA wave, and puts them in LDS
-    // before its first ready count, so the MFMA waves read them from LDS, never from memory
-    const int lw = wave - 4;
-    const int lreg = min((int)blockIdx.x * kTiledRegions + lw, NWG - 1);
-    const int lnbA = (16 * lreg) >> 7, lnbB = (16 * NA * NWG + CB * lreg) >> 7;
-    constexpr uint32_t es = E8 ? 1u : 4u;
-    const __amdgpu_buffer_rsrc_t swsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)sw + (int64_t)lnbA * KB * es), 0, NA ? KB * (int)es : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t swsB = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)sw + (int64_t)lnbB * KB * es), 0, HASB ? KB * (int)es : 0, 0x00020000);
-    uint32_t sv[4];
+  // ---- scales into LDS (issued first; written after the first loads are on their way) ----
+  const int nsx = Mt * KB;
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)sa + (int64_t)m0 * KB * es), 0, nsx * (int)es, 0x00020000);
+  auto load_sx = [&](uint32_t (&v)[4], int e0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t k = (uint32_t)lane + 64u * h;
-      sv[h] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsA, k, 0, 0) : __builtin_amdgcn_raw_buffer_load_b32(swsA, k * 4u, 0, 0);
-      sv[2 + h] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsB, k, 0, 0) : __builtin_amdgcn_raw_buffer_load_b32(swsB, k * 4u, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + kTThreads * j + tid;
+      const uint32_t o = (e < nsx) ? (uint32_t)e * es : (uint32_t)nsx * es;
+      v[j] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(srsrc, o, 0, 0) : __builtin_amdgcn_raw_buffer_load_b32(srsrc, o, 0, 0);
     }
-    u32x4 ab[D][NLA];
-    uint32_t asc[D];
-    // rows past M and K blocks past the end read zeros past the end of the buffers
-    auto load = [&](int slot, int kb) {
-      const uint32_t o = (kb < KB) ? arow + (uint32_t)kb * 128u : abytes;
+  };
+  // unconditional stores (a conditional one lets the compiler sink its load past the loads issued
+  // after it): elements past the tile go to a pad entry nothing reads
+  auto store_sx = [&](const uint32_t (&v)[4], int e0) {
 #pragma unroll
-      for (int l = 0; l < NLA; ++l)
-        ab[slot][l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o + 16u * l, 0, 0));
-      const uint32_t so = (kb < KB) ? srowb + (uint32_t)kb * (E8 ? 1u : 4u) : sbytes;
-      asc[slot] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(srsrc, so, 0, 0)
-                     : __builtin_amdgcn_raw_buffer_load_b32(srsrc, so, 0, 0);
-    };
-#pragma unroll
-    for (int d = 0; d < D; ++d) load(d, d);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      swl[lw][0][lane + 64 * h] = sv[h];
-      swl[lw][1][lane + 64 * h] = sv[2 + h];
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + kTThreads * j + tid;
+      const int row = e / KB, kb = e - row * KB;
+      sxs[(e < nsx) ? kb * SXP + row : TM] = v[j];
     }
-    for (int kb0 = 0; kb0 < KBp; kb0 += D) {
+  };
+  // weight block scales: thread t takes region t / 128, row (A or remainder) (t / 64) % 2, K
+  // blocks lane and lane + 64
+  const int sreg = min((int)blockIdx.x * kTiledRegions + (tid >> 7), NWG - 1);
+  const int snb = ((tid >> 6) & 1) ? (16 * NA * NWG + CB * sreg) >> 7 : (16 * sreg) >> 7;
+  const bool sown = ((tid >> 6) & 1) ? HASB : (NA != 0);
+  const __amdgpu_buffer_rsrc_t swsr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)sw + (int64_t)snb * KB * es), 0, sown ? KB * (int)es : 0, 0x00020000);
+  uint32_t sv[2], xv[4];
 #pragma unroll
-      for (int u = 0; u < D; ++u) {
-        const int kb = kb0 + u;
-        {
-          const int sl = kb % kTSlots, gen = kb / kTSlots;
-          if (gen > 0) flag_wait(&consumed[sl], 4u * (uint32_t)gen);  // the slot's last block is read
-          uint8_t* slot = ring + sl * SLOT;
-          u32x4* dst = (u32x4*)(slot + srow * kTPitch + sch * BPT);
-#pragma unroll
-          for (int l = 0; l < NLA; ++l) dst[l] = ab[u][l];
-          if (sch == 0) ((uint32_t*)(slot + TM * kTPitch))[srow] = asc[u];
-          lds_release();
-          if (lane == 0) __hip_atomic_fetch_add(&ready[sl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          load(u, kb + D);
-        }
-      }
-    }
-    return;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t k = (uint32_t)lane + 64u * h;
+    sv[h] = E8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(swsr, k, 0, 0) : __builtin_amdgcn_raw_buffer_load_b32(swsr, k * 4u, 0, 0);
   }
+  load_sx(xv, 0);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- MFMA waves: one packed region each ----
-  const int reg = min((int)blockIdx.x * kTiledRegions + wave, NWG - 1);
-  const bool owner = (int)(blockIdx.x * kTiledRegions + wave) < NWG;
+  // ---- activations: wave w's load l of a step holds LDS bytes [(8 l + w) KiB, +1 KiB) of the
+  // slot: half h = (8 l + w) / (TM / 8), rows 8 ((8 l + w) % (TM / 8)) .. + 7, 16 bytes a lane
+  const uint32_t abytes = (uint32_t)((int64_t)(Mt - 1) * ldq + K);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(q + (int64_t)m0 * ldq), 0, (int)abytes, 0x00020000);
+  uint32_t arow[NLD];
+  int ahalf[NLD];
+#pragma unroll
+  for (int l = 0; l < NLD; ++l) {
+    const int u = 8 * l + wave;                    // KiB of the slot
+    ahalf[l] = u / (TM / 8);
+    const int row = (u % (TM / 8)) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);  // the chunk this lane's bytes hold
+    arow[l] = (row < Mt) ? (uint32_t)((int64_t)row * ldq + c * 16) : abytes;
+  }
+  u32x4 ar[P][NLD];
+  auto load_act = [&](int slot, int st) {
+#pragma unroll
+    for (int l = 0; l < NLD; ++l) {
+      const int kb = ahalf[l] * KBh + st;
+      const uint32_t o = (kb < KB) ? arow[l] + (uint32_t)kb * 128u : abytes;  // past the end: zeros
+      ar[slot][l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, o, 0, 0));
+    }
+  };
+  auto store_act = [&](int slot, int st) {
+    uint8_t* dst = ring + (st & 1) * SLOT + wave * 1024 + lane * 16;
+#pragma unroll
+    for (int l = 0; l < NLD; ++l) *(u32x4*)(dst + 8 * 1024 * l) = ar[slot][l];
+  };
+
+  // ---- weights of this wave's region and half ----
+  const int reg = min((int)blockIdx.x * kTiledRegions + rw, NWG - 1);
+  const bool owner = (int)(blockIdx.x * kTiledRegions + rw) < NWG;
   const int cols = 16 * NA + CB;
   const int NB = HASB ? CB * SB : 16;  // B columns of a remainder fragment
   const int jl = lane & 15;
@@ -1104,9 +1106,8 @@ __global__ __launch_bounds__(512) void tiled_gemm_kernel(
   const __amdgpu_buffer_rsrc_t wrA = __builtin_amdgcn_make_buffer_rsrc((void*)wreg, 0, (int)wabytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrB = __builtin_amdgcn_make_buffer_rsrc((void*)(wreg + wabytes), 0, (int)wbbytes, 0x00020000);
   const uint32_t boff = bcol ? (uint32_t)(((lane >> 4) * NB + jl) * 16) : wbbytes;
-  const int nbA = (16 * reg) >> 7;                    // 128-column block of the 16-column group
-  const int nbB = (16 * NA * NWG + CB * reg) >> 7;    // and of the remainder group
-  u32x4 wa[TDW][2], wb[NBS][2];
+  const int kb0 = kh * KBh;            // this wave's first K block
+  u32x4 wa[P][2], wb[NBS][2];
   // weight loads through the caches (not non-temporal): the row tiles of one column tile run on
   // one XCD and read the same fragments, so all but the first are L2 hits
   auto load_wa = [&](int slot, int kb) {
@@ -1123,111 +1124,135 @@ __global__ __launch_bounds__(512) void tiled_gemm_kernel(
       wb[slot][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrB, o + (fbytes >> 1), 0, 0));
     }
   };
-  const uint32_t* swr = &swl[wave][0][0];  // this region's weight block scales (LDS, from its loader)
+  // the first P steps, in the order every later step issues its loads (activations, 16-column
+  // fragment, remainder fragment at its first block)
 #pragma unroll
-  for (int d = 0; d < TDW; ++d) {
-    load_wa(d, d);
-    if (d % SB == 0) load_wb(d / SB, d / SB);
+  for (int t = 0; t < P; ++t) {
+    load_act(t, t);
+    load_wa(t, kb0 + t);
+    if (t % SB == 0) load_wb((t / SB) % NBS, (kb0 + t) / SB);
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) swl[tid >> 7][(tid >> 6) & 1][lane + 64 * h] = sv[h];
+  store_sx(xv, 0);
+  // a tile with more than 2048 scales (K beyond 4096 at 64 rows): the rest, waiting each batch
+  for (int e0 = 2048; e0 < nsx; e0 += 2048) {
+    load_sx(xv, e0);
+    store_sx(xv, e0);
+  }
+  // the padded K blocks: zero scales (their activations and weights are zeros too)
+  for (int e = tid; e < (2 * KBh - KB) * TM; e += kTThreads) sxs[(KB + e / TM) * SXP + e % TM] = 0u;
+  const uint32_t* swr = &swl[rw][0][0];
+  // step 0's activations into their slot, and step P's loads into the registers they leave
+  store_act(0, 0);
+  load_act(0, P);
+
   v4f accA[NSUB], accB[NSUB];
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
     accA[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     accB[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // K blocks in steps of BG, each step's operands read, multiplied and scaled together
-  for (int kb0 = 0; kb0 < KBp; kb0 += TDW) {
+  for (int s0 = 0; s0 < KBh; s0 += UJ) {
 #pragma unroll
-    for (int u = 0; u < TDW; u += BG) {
-      const int kb = kb0 + u;
-      {
-        v8i at[BG][NSUB];
-        int sar[BG][NSUB];
-        v4f sx4[BG][NSUB];
-        v8i bA[BG], bB[BG];
-        int ea[BG], eb[BG];
-        // the step's last block staged by all four loaders (each stages in order, so the earlier
-        // ones are too)
-        flag_wait(&ready[(kb + BG - 1) % kTSlots], 4u * (uint32_t)((kb + BG - 1) / kTSlots + 1));
+    for (int u = 0; u < UJ; ++u) {
+      const int st = s0 + u, kb = kb0 + st;
+      // after the barrier every wave's writes of this step's activations are visible, and every
+      // wave is done with the previous step, whose slot takes the next step's
+      lds_release();
+      __builtin_amdgcn_s_barrier();
+      lds_acquire();
+      store_act((u + 1) % P, st + 1);
+      load_act((u + 1) % P, st + 1 + P);
+      v8i at[NSUB];
+      int sar[NSUB];
+      v4f sx4[NSUB];
+      v8i bA = v8i{0, 0, 0, 0, 0, 0, 0, 0}, bB = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      const uint8_t* blk = ring + (st & 1) * SLOT + kh * HALF;
+      const uint32_t* ss = sxs + kb * SXP;
 #pragma unroll
-        for (int h = 0; h < BG; ++h) {
-          const int s = (kb + h) % kTSlots;
-          const uint8_t* slot = ring + s * SLOT;
-          const uint32_t* ss = (const uint32_t*)(slot + TM * kTPitch);
+      for (int i = 0; i < NSUB; ++i) {
+        const int r = i * 16 + jl, c = (lane >> 4) * 2;
+        const u32x4 a0 = *(const u32x4*)(blk + tswz(r, c)), a1 = *(const u32x4*)(blk + tswz(r, c + 1));
+        at[i] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        if (E8) sar[i] = (int)ss[r];
+        else sx4[i] = *(const v4f*)(ss + i * 16 + 4 * (lane >> 4));
+      }
+      if (NA) bA = __builtin_bit_cast(v8i, __builtin_shufflevector(wa[u % P][0], wa[u % P][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (HASB) {
+        const int bs = (u / SB) % NBS;
+        bB = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[bs][0], wb[bs][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (SB > 1) {
+          const uint32_t bmask = (sl == u % SB) ? 0xFFFFFFFFu : 0u;  // lanes of this K block
 #pragma unroll
-          for (int i = 0; i < NSUB; ++i) {
-            const int r = i * 16 + jl;
-            const u32x4* ap = (const u32x4*)(slot + r * kTPitch + (lane >> 4) * 32);
-            const u32x4 a0 = ap[0], a1 = ap[1];
-            at[h][i] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            if (E8) sar[h][i] = (int)ss[r];
-            else sx4[h][i] = *(const v4f*)(ss + i * 16 + 4 * (lane >> 4));
-          }
-          bA[h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          bB[h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          if (NA) bA[h] = __builtin_bit_cast(v8i, __builtin_shufflevector(wa[u + h][0], wa[u + h][1], 0, 1, 2, 3, 4, 5, 6, 7));
-          if (HASB) {
-            bB[h] = __builtin_bit_cast(v8i, __builtin_shufflevector(wb[(u + h) / SB][0], wb[(u + h) / SB][1], 0, 1, 2, 3, 4, 5, 6, 7));
-            if (SB > 1) {
-              const uint32_t bmask = (sl == (u + h) % SB) ? 0xFFFFFFFFu : 0u;  // lanes of this K block
-#pragma unroll
-              for (int d = 0; d < 8; ++d) bB[h][d] = (int)((uint32_t)bB[h][d] & bmask);
-            }
-          }
-          const int k = kb + h;  // past the row: the loader stored zeros
-          ea[h] = NA ? (int)swr[k] : 0;
-          eb[h] = HASB ? (int)swr[kTiledMaxKB + k] : 0;
-        }
-        if (E8) {
-#pragma unroll
-          for (int h = 0; h < BG; ++h)
-#pragma unroll
-            for (int i = 0; i < NSUB; ++i) {
-              if (NA) accA[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bA[h], accA[i], 0, 0, 0, sar[h][i], 0, ea[h]);
-              if (HASB) accB[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bB[h], accB[i], 0, 0, 0, sar[h][i], 0, eb[h]);
-            }
-        } else {
-#pragma unroll
-          for (int h = 0; h < BG; ++h) {
-            v4f fa[NSUB], fb[NSUB];
-#pragma unroll
-            for (int i = 0; i < NSUB; ++i) {
-              if (NA) fa[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bA[h], v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                                0, 0, 0, 127, 0, 127);
-              if (HASB) fb[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[h][i], bB[h], v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                                  0, 0, 0, 127, 0, 127);
-            }
-            const float swA = __int_as_float(ea[h]), swB = __int_as_float(eb[h]);  // the fp32 scales' bits
-#pragma unroll
-            for (int i = 0; i < NSUB; ++i)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (NA) accA[i][e] = __builtin_fmaf(sx4[h][i][e] * swA, fa[i][e], accA[i][e]);
-                if (HASB) accB[i][e] = __builtin_fmaf(sx4[h][i][e] * swB, fb[i][e], accB[i][e]);
-              }
-          }
-        }
-        // the step's results join the accumulators in the MFMAs' own basic block
-#pragma unroll
-        for (int i = 0; i < NSUB; ++i) asm volatile("" : "+v"(accA[i]), "+v"(accB[i]));
-        lds_release();  // this wave's reads of the step's slots are done
-        if (lane == 0) {
-#pragma unroll
-          for (int h = 0; h < BG; ++h)
-            __hip_atomic_fetch_add(&consumed[(kb + h) % kTSlots], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-#pragma unroll
-        for (int h = 0; h < BG; ++h) {
-          load_wa(u + h, kb + h + TDW);
-          if ((u + h) % SB == SB - 1) load_wb((u + h) / SB, (kb + h + TDW) / SB);  // the slot's last use was this block
+          for (int d = 0; d < 8; ++d) bB[d] = (int)((uint32_t)bB[d] & bmask);
         }
       }
+      const int ea = NA ? (int)swr[kb] : 0;  // past the row: zeros
+      const int eb = HASB ? (int)swr[kTiledMaxKB + kb] : 0;
+      if (E8) {
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i) {
+          if (NA) accA[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[i], bA, accA[i], 0, 0, 0, sar[i], 0, ea);
+          if (HASB) accB[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[i], bB, accB[i], 0, 0, 0, sar[i], 0, eb);
+        }
+      } else {
+        v4f fa[NSUB], fb[NSUB];
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i) {
+          if (NA) fa[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[i], bA, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                            0, 0, 0, 127, 0, 127);
+          if (HASB) fb[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at[i], bB, v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                              0, 0, 0, 127, 0, 127);
+        }
+        const float swA = __int_as_float(ea), swB = __int_as_float(eb);  // the fp32 scales' bits
+#pragma unroll
+        for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (NA) accA[i][e] = __builtin_fmaf(sx4[i][e] * swA, fa[i][e], accA[i][e]);
+            if (HASB) accB[i][e] = __builtin_fmaf(sx4[i][e] * swB, fb[i][e], accB[i][e]);
+          }
+      }
+      // the step's results join the accumulators in the MFMAs' own basic block
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) asm volatile("" : "+v"(accA[i]), "+v"(accB[i]));
+      __builtin_amdgcn_sched_barrier(0);
+      // the registers of this step's fragments take the fragments P steps on
+      load_wa(u % P, kb + P);
+      if ((u + P) % SB == 0) load_wb(((u + P) / SB) % NBS, (kb + P) / SB);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // 16 wait states on every path before the accumulators are read (the loop ends in branches)
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(accA[i]), "+v"(accB[i]));
-  if (!owner) return;
+  // every wave is done reading the ring: it now takes the second half's accumulators
+  lds_release();
+  __builtin_amdgcn_s_barrier();
+  lds_acquire();
+  float* red = (float*)ring + rw * (2 * NSUB * 4 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (NA) red[(i * 4 + e) * 64 + lane] = accA[i][e];
+        if (HASB) red[((NSUB + i) * 4 + e) * 64 + lane] = accB[i][e];
+      }
+  }
+  lds_release();
+  __builtin_amdgcn_s_barrier();
+  lds_acquire();
+  if (kh == 1 || !owner) return;
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (NA) accA[i][e] += red[(i * 4 + e) * 64 + lane];
+      if (HASB) accB[i][e] += red[((NSUB + i) * 4 + e) * 64 + lane];
+    }
   // output: lane l holds MFMA column l % 16, rows 4 (l / 16) + e of each subtile
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
@@ -1421,7 +1446,7 @@ void launch_tiled_tm(const Layout& L, int M, int K, const uint8_t* q, int64_t ld
                      const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, hipStream_t stream) {
   const dim3 grid((L.nwg + kTiledRegions - 1) / kTiledRegions, (M + TM - 1) / TM);
 #define TILED_K(na, hasb, sb)                                                                        \
-  hipLaunchKernelGGL((tiled_gemm_kernel<TM, E8, na, hasb, sb>), grid, dim3(512), 0, stream, q, ldq, \
+  hipLaunchKernelGGL((tiled_gemm_kernel<TM, E8, na, hasb, sb>), grid, dim3(kTThreads), 0, stream, q, ldq, \
                      sa, wp, sw, y, ldy, M, K, L.cb, L.nwg)
   if (L.cb == 0) TILED_K(1, false, 1);
   else if (L.na == 1) {

@@ -46,7 +46,9 @@ def test_gemm_kernels_use_no_scratch(device_asm):
     assert len(others) == 2
     moe = re.findall(r"^(_Z\S*moe_(?:gate_up_pairs|gate_up_items|down)_kernel\S*):", text, re.M)
     assert len(moe) == 10
-    kernels += others + moe
+    tiled = re.findall(r"^(_Z\S*tiled_gemm_kernel\S*):", text, re.M)
+    assert len(tiled) == 28
+    kernels += others + moe + tiled
     spills = []
     for k in kernels:
         seg = text[text.index(k + ":"):]
