@@ -238,7 +238,7 @@ def crossover_beyond(P, torch, np, synthgen, dev, copies, reps):
         for M in (33, 48, 64, 128, 256):
             x = torch.from_numpy(synthgen.gen_x(M, K, seed=0).view(np.int16).copy()).to(dev).view(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            need = P.smallm_fp8bs_quant_gemm_workspace_bytes(max(M, 41), N, K)
+            need = P.smallm_fp8bs_quant_gemm_workspace_bytes(max(M, 33), N, K)
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
             def chunks(i):
@@ -247,7 +247,7 @@ def crossover_beyond(P, torch, np, synthgen, dev, copies, reps):
                 assert st == 0, st
 
             def two(i):
-                # the workspace entry's second path, called directly (it takes it from 41 rows)
+                # the workspace entry's second path, called directly (it takes it from 33 rows)
                 q = ws[: M * K].view(M, K)
                 sx = ws[(M * K + 255) // 256 * 256:][: M * (K // 128) * 4].view(torch.float32).view(M, K // 128)
                 P.smallm_fp8bs_quant(x, q=q, sx=sx)

@@ -208,13 +208,12 @@ int smallm_fp8bs_quant_gemm_e8m0(const uint16_t* x, int64_t ldx, const uint8_t* 
                                  uint8_t* sx_dbg_e8m0, void* stream);
 
 /* Bytes of workspace smallm_fp8bs_quant_gemm_ws takes for (M, N, K): 0 when it runs the fused
- * kernel (M <= 40, where the fused kernel's 32-row chunks are measured faster, or a shape the
- * tiled kernel does not take), else M * K rounded up to 256 plus 4 * M * K / 128. */
+ * kernel (M <= 32, or a shape the tiled kernel does not take), else M * K rounded up to 256 plus 4 * M * K / 128. */
 size_t smallm_fp8bs_quant_gemm_workspace_bytes(int M, int N, int K);
 
 /* smallm_fp8bs_quant_gemm for any M with a caller-owned workspace (device memory, 256-byte
  * aligned, at least smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K) bytes; may be NULL when that
- * is 0).  Up to 40 rows: the fused kernel.  Beyond: the standalone quantisation into the
+ * is 0).  Up to 32 rows: the fused kernel.  Beyond: the standalone quantisation into the
  * workspace, then the tiled GEMM on it -- the pages hand inputs past the small-M cap to a
  * separate quant + GEMM path ("[AMD] Small-M FP8 block-scale GEMM with fused activation quant for
  * gfx950 (Qwen3.5)", Modifications); the results equal smallm_fp8bs_quant then smallm_fp8bs_gemm

@@ -1700,11 +1700,11 @@ int smallm_fp8bs_quant_gemm_e8m0(const uint16_t* x, int64_t ldx, const uint8_t* 
                                (void*)sx_dbg_e8m0, (hipStream_t)stream);
 }
 
-// Rows up to which the fused kernel (in 32-row chunks above 32) beats the standalone quantisation
-// plus the tiled GEMM: measured on the pages' shapes (5120x4096, 4608x4096, 4096x2048, 2048x4096),
-// graph replay over 24 cold weight copies -- at 33 rows the two 32-row chunks are faster on all
-// four, from 48 rows the quant + tiled pair.
-constexpr int kFusedUpToM = 40;
+// Rows up to which the fused kernel beats the standalone quantisation plus the tiled GEMM:
+// measured on the pages' shapes (5120x4096, 4608x4096, 4096x2048, 2048x4096), graph replay over 24
+// cold weight copies -- at 33 rows the quant + tiled pair is faster than the fused kernel's two
+// 32-row chunks on all four (8.6 against 10.0 us on 4096x2048, 14.2 against 18.7 on 5120x4096).
+constexpr int kFusedUpToM = 32;
 
 size_t smallm_fp8bs_quant_gemm_workspace_bytes(int M, int N, int K) {
   if (check_mnk(M, N, K) != SMALLM_OK || M <= kFusedUpToM || !tiled_ok(M, K, K)) return 0;

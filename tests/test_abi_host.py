@@ -93,7 +93,7 @@ def test_version_layout_and_strerror():
 
 def test_workspace_entry_sizes_and_host_checks():
     assert P.smallm_fp8bs_quant_gemm_workspace_bytes(32, 4096, 2048) == 0      # the fused kernel
-    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(40, 4096, 2048) == 0      # two fused chunks
+    assert P.smallm_fp8bs_quant_gemm_workspace_bytes(33, 4096, 2048) == (33 * 2048 + 255) // 256 * 256 + 33 * 16 * 4
     assert P.smallm_fp8bs_quant_gemm_workspace_bytes(41, 4096, 2048) == (41 * 2048 + 255) // 256 * 256 + 41 * 16 * 4
     assert P.smallm_fp8bs_quant_gemm_workspace_bytes(256, 5120, 4096) == 256 * 4096 + 256 * 32 * 4
     assert P.smallm_fp8bs_quant_gemm_workspace_bytes(64, 4096, 128 * 129) == 0   # K past the tiled kernel
