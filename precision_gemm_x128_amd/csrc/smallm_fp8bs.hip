@@ -95,8 +95,27 @@ __device__ __forceinline__ int e8m0_round_exponent(float amax) {
 // x / s for the 32 elements as described below, then e4m3 with round to nearest even, four at a
 // time; RESCALE multiplies x by k first.
 template <bool RESCALE>
-__device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float yh, float yl, float k,
+__device__ __forceinline__ void quant32_codes(const float (&xf)[32], float yh, float yl, float k,
                                               uint32_t (&w)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float f = xf[4 * j + t];
+      if (RESCALE) f *= k;
+      q[t] = __builtin_fmaf(f, yh, f * yl);
+    }
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
+    w[j] = (uint32_t)p;
+  }
+}
+
+// The same from the packed bf16 pairs, widening each value where it is used.
+template <bool RESCALE>
+__device__ __forceinline__ void quant32_codes_packed(const u32x4 (&xv)[4], float yh, float yl, float k,
+                                                     uint32_t (&w)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float q[4];
@@ -113,8 +132,23 @@ __device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float yh, fl
   }
 }
 
+// max(m, |a|, |b|) in one instruction (the absolute values are source modifiers)
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(m));
+  return r;
+}
+
 // Quantise 32 consecutive bf16 of one 1x128 group (this lane's quarter; the group is spread
 // over a DPP quad) with an fp32 group scale.  Returns the scale, writes 32 e4m3 bytes.
+//
+// Group amax, two forms with the same result on finite input: WIDE widens the 32 bf16 values to
+// fp32 once (exact) for both the amax (a three-input max over magnitudes, two elements per
+// instruction) and the quotients, which takes fewer instructions but holds 32 more registers
+// while the scale is formed; otherwise the amax is taken on the bf16 bit patterns (with the sign
+// cleared, integer order is magnitude order) and each value is widened where it is used.  Either
+// way the magnitudes are non-negative, so the integer order of their bit patterns is their order
+// across the quad.
 //
 // x / s is formed with a two-term reciprocal, 1/s ~ yh + yl: yh is 1/s rounded toward zero (the
 // correctly rounded reciprocal, stepped down one unit when the residual 1 - s yh comes out
@@ -124,14 +158,28 @@ __device__ __forceinline__ void quant32_codes(const u32x4 (&xv)[4], float yh, fl
 // |x| <= 448 s keeping x 2^64 below 448) so that 1/s stays finite.  Over every pair of bf16 amax
 // and bf16 x with |x| <= amax, the e4m3 code of q equals that of the correctly rounded division
 // RN(x / s): q differs from RN(x / s) only by quotients that no e4m3 rounding boundary separates.
+template <bool WIDE>
 __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[2]) {
-  // group amax on the bf16 bit patterns: with the sign cleared, integer order is magnitude order
-  u16x2 mx = u16x2{0, 0};
+  float xf[32];
+  float am;
+  if constexpr (WIDE) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, xv[i >> 2][i & 3] & 0x7FFF7FFFu));
-  const uint32_t amb = quad_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1]));
-  const float am = __uint_as_float(amb << 16);
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t d = xv[i >> 2][i & 3];
+      xf[2 * i] = __uint_as_float(d << 16);
+      xf[2 * i + 1] = __uint_as_float(d & 0xFFFF0000u);
+    }
+    float mf = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mf = max3_abs(mf, xf[2 * i], xf[2 * i + 1]);
+    am = __uint_as_float(quad_max_u32(__float_as_uint(mf)));
+  } else {
+    u16x2 mx = u16x2{0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, xv[i >> 2][i & 3] & 0x7FFF7FFFu));
+    am = __uint_as_float(quad_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1])) << 16);
+  }
   const float s = am / 448.0f;                          // correctly rounded fp32 division
   const bool tiny = s > 0.0f && s < 0x1p-64f;       // (an all-zero group needs no rescaling)
   const float k = tiny ? 0x1p64f : 1.0f;                // rescaling of a tiny group
@@ -145,8 +193,13 @@ __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[
   const float yl = e * yh;                               // all-zero group: yh = yl = 0
   uint32_t w[8];
   // the rescaling multiply only runs when some group of the wave needs it (a wave-wide vote)
-  if (__builtin_amdgcn_ballot_w64(tiny) != 0) quant32_codes<true>(xv, yh, yl, k, w);
-  else quant32_codes<false>(xv, yh, yl, k, w);
+  if constexpr (WIDE) {
+    if (__builtin_amdgcn_ballot_w64(tiny) != 0) quant32_codes<true>(xf, yh, yl, k, w);
+    else quant32_codes<false>(xf, yh, yl, k, w);
+  } else {
+    if (__builtin_amdgcn_ballot_w64(tiny) != 0) quant32_codes_packed<true>(xv, yh, yl, k, w);
+    else quant32_codes_packed<false>(xv, yh, yl, k, w);
+  }
   qv[0] = u32x4{w[0], w[1], w[2], w[3]};
   qv[1] = u32x4{w[4], w[5], w[6], w[7]};
   return s;
@@ -325,7 +378,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   for (int i = 0; i < 4; ++i) xv[i] = valid ? xp[i] : u32x4{0, 0, 0, 0};
   u32x4 qv[2];
   if (!E8M0) {
-    const float s = quant32_fp32(xv, qv);
+    const float s = quant32_fp32<false>(xv, qv);
     if (valid && c == 0) ((float*)sx)[(int64_t)m * KB + kb] = s;
   } else {
     const uint32_t e = quant32_e8m0(xv, qv);
@@ -497,7 +550,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
       u32x4 qv[2];
       const int g = l >> 2, KB = H >> 7;
       if (!E8M0) {
-        const float sc = quant32_fp32(yv, qv);
+        const float sc = quant32_fp32<false>(yv, qv);
         if (valid && (l & 3) == 0) ((float*)sx)[(int64_t)m * KB + g] = sc;
       } else {
         const uint32_t e = quant32_e8m0(yv, qv);
@@ -837,7 +890,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
             uint32_t eb = 0;
             if constexpr (!Cfg::kPreq) {
               if constexpr (Cfg::kE8) eb = quant32_e8m0(xv[p], qv);
-              else sc = quant32_fp32(xv[p], qv);
+              else sc = quant32_fp32<false>(xv[p], qv);  // one tile: every pass's loads are held at once
             } else {
               qv[0] = xv[p][0];
               qv[1] = xv[p][1];
@@ -892,7 +945,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
           uint32_t eb = 0;
           if constexpr (!Cfg::kPreq) {
             if constexpr (Cfg::kE8) eb = quant32_e8m0(v, qv);
-            else sc = quant32_fp32(v, qv);
+            else sc = quant32_fp32<true>(v, qv);  // two tiles: two passes in flight
           } else {
             qv[0] = v[0];
             qv[1] = v[1];
