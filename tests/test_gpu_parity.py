@@ -549,6 +549,8 @@ PREQ_CASES = [
     (384, 640, 33), (384, 640, 100), (4096, 128, 64), (4096, 2048, 48), (4096, 2048, 256),
     (4096, 4736, 77), (5120, 4096, 40), (2048, 4096, 96), (4608, 4096, 65), (4608, 640, 200),
     (5120, 2048, 129), (1024, 12416, 48),
+    # the largest K the tiled kernel takes (128 K blocks: four batches of row scales at 64 rows)
+    (256, 16384, 256), (384, 16384, 33),
 ]
 
 
