@@ -180,7 +180,11 @@ __device__ __forceinline__ float quant32_fp32(const u32x4 (&xv)[4], u32x4 (&qv)[
       mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, xv[i >> 2][i & 3] & 0x7FFF7FFFu));
     am = __uint_as_float(quad_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1])) << 16);
   }
-  const float s = am / 448.0f;                          // correctly rounded fp32 division
+  // the correctly rounded fp32 quotient amax / 448, as a multiply by RN(1 / 448) and one
+  // correction with the exact remainder (equal to the IEEE division for every bf16 amax, the
+  // subnormal ones included, with fp32 denormals kept)
+  const float s0 = am * (1.0f / 448.0f);
+  const float s = __builtin_fmaf(__builtin_fmaf(-s0, 448.0f, am), 1.0f / 448.0f, s0);
   const bool tiny = s > 0.0f && s < 0x1p-64f;       // (an all-zero group needs no rescaling)
   const float k = tiny ? 0x1p64f : 1.0f;                // rescaling of a tiny group
   const float sk = s * k;

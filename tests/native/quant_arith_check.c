@@ -1,6 +1,9 @@
 // Exhaustive CPU check of the fused kernel's activation-quotient recipe.
 //
-// The kernel forms x / s, s = RN(amax / 448), as q = fma(x, yh, x yl) with a two-term reciprocal:
+// The kernel forms s = RN(amax / 448) as s0 = amax RN(1/448) corrected once with the exact
+// remainder, s = fma(fma(-s0, 448, amax), RN(1/448), s0); this program checks that it equals the
+// IEEE division for every bf16 amax.
+// The kernel forms x / s as q = fma(x, yh, x yl) with a two-term reciprocal:
 // yh = 1 / s rounded toward zero (RN(1 / s), stepped down one unit when the residual
 // e = fma(-s, yh, 1) is negative) and yl = e yh >= 0, after rescaling x and s by 2^64 when
 // 0 < s < 2^-64.
@@ -32,11 +35,13 @@ static uint8_t enc(float v) {
   return sg | (uint8_t)code;
 }
 int main(void) {
-  long long checked = 0, bad = 0, fbad = 0;
-  #pragma omp parallel for reduction(+:checked,bad,fbad) schedule(dynamic)
+  long long checked = 0, bad = 0, fbad = 0, sbad = 0;
+  #pragma omp parallel for reduction(+:checked,bad,fbad,sbad) schedule(dynamic)
   for (int ab = 1; ab < 0x7F80; ++ab) {
     const float am = bf((uint16_t)ab);
-    const float s = am / 448.0f;
+    const float s0 = am * (1.0f / 448.0f);
+    const float s = fmaf(fmaf(-s0, 448.0f, am), 1.0f / 448.0f, s0);
+    if (s != am / 448.0f) { printf("scale differs from the division: am=%a\n", am); ++sbad; }
     const float k = (s > 0.0f && s < 0x1p-64f) ? 0x1p64f : 1.0f;
     const float sk = s * k;
     float yh = 1.0f / sk;
@@ -58,6 +63,7 @@ int main(void) {
       }
     }
   }
-  printf("pairs %lld, fp32 quotient mismatches %lld, e4m3 code mismatches %lld\n", checked, fbad, bad);
-  return bad != 0;
+  printf("pairs %lld, fp32 quotient mismatches %lld, e4m3 code mismatches %lld, scale mismatches %lld\n",
+         checked, fbad, bad, sbad);
+  return bad != 0 || sbad != 0;
 }
