@@ -218,6 +218,43 @@ def test_quant_exhaustive_bf16_values():
                               sx_ref.view(np.uint8 if e8m0 else np.uint32))
 
 
+def every_amax_value_pair_groups():
+    """1x128 groups holding, for every positive finite bf16 amax, that amax and then every bf16 x
+    with |x| <= amax, both signs, 127 to a group (the last group of an amax padded with zeros):
+    about 8.4 million groups, 1.07e9 values."""
+    parts = []
+    for ab in range(1, 0x7F80):
+        v = np.arange(ab + 1, dtype=np.uint16)
+        v = np.concatenate([v, v | np.uint16(0x8000)])
+        n = (len(v) + 126) // 127
+        g = np.zeros((n, 128), dtype=np.uint16)
+        g[:, 0] = ab
+        g[:, 1:].reshape(-1)[:len(v)] = v
+        parts.append(g)
+    return np.concatenate(parts)
+
+
+@pytest.mark.gpu
+def test_quant_every_amax_value_pair():
+    """The standalone quantiser (fp32 group scales) against the oracle over every pair of a bf16
+    amax and a bf16 x with |x| <= amax: codes and scales bit-exact.  This runs the kernel's own
+    instruction sequence over the whole domain the CPU proof of the quotient recipe covers."""
+    note("quant every amax/value pair")
+    groups = every_amax_value_pair_groups()
+    per = 256 * 512                                   # groups per call: 256 rows x K = 65536
+    for c0 in range(0, len(groups), per):
+        chunk = groups[c0:c0 + per]
+        if len(chunk) < per:
+            chunk = np.concatenate([chunk, np.zeros((per - len(chunk), 128), dtype=np.uint16)])
+        x = chunk.reshape(256, 65536)
+        q_ref, sx_ref = oracle.quant_act(x)
+        q, sx = P.smallm_fp8bs_quant(to_dev_bf16(x))
+        torch.cuda.synchronize()
+        assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32)), f"scales, groups from {c0}"
+        assert np.array_equal(q.cpu().numpy(), q_ref), f"codes, groups from {c0}"
+        print(f"  groups {min(c0 + per, len(groups))} of {len(groups)} checked", flush=True)
+
+
 def every_amax_groups(seed=7):
     """One 1x128 group per positive finite bf16 amax (0x0001 .. 0x7F7F): the amax itself plus 127
     random bf16 of magnitude <= amax with random signs, as rows of 32 groups (K = 4096).  Covers
