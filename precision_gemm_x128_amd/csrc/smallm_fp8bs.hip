@@ -997,10 +997,13 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
   }
 
   __syncthreads();
+  // thread t: row t / 32 and column t % 32 of the region (at most 24 columns); every slot is read
+  // and those of absent ranges are replaced by -0 (x + -0 == x) without a branch
   const int na16 = 16 * NA;
-  const int nout = Mc * cols;
-  for (int t = tid; t < nout; t += blockDim.x) {
-    const int row = t / cols, ci = t - row * cols;
+  static_assert(16 * NA + 8 <= 32, "a region has at most 32 columns");
+  for (int t = tid; t < MP * 32; t += blockDim.x) {
+    const int row = t >> 5, ci = t & 31;
+    if (row >= Mc || ci >= cols) continue;
     const int mt = row >> 4, r = row & 15, e = r & 3;
     const bool inA = ci < na16;
     const int part = inA ? 0 : 1;
@@ -1008,10 +1011,10 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
     const float* rp = (const float*)smem + ((part * MT + mt) * 4 + e) * 64 + li;
     float v[Cfg::kRanges];
 #pragma unroll
-    for (int w = 0; w < Cfg::kRanges; ++w) v[w] = (w < NW) ? rp[w * (Cfg::kWave / 4)] : -0.0f;  // x + -0 == x
+    for (int w = 0; w < Cfg::kRanges; ++w) v[w] = rp[w * (Cfg::kWave / 4)];
     float sum = v[0];
 #pragma unroll
-    for (int w = 1; w < Cfg::kRanges; ++w) sum += v[w];
+    for (int w = 1; w < Cfg::kRanges; ++w) sum += (w < NW) ? v[w] : -0.0f;
     const int col = inA ? 16 * wg + ci : na16 * NWG + CB * wg + (ci - na16);
     y[(int64_t)(m0 + row) * ldy + col] = bf16_rne(sum);
   }
