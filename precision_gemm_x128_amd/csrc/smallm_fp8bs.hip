@@ -106,7 +106,9 @@ __device__ __forceinline__ void quant32_codes(const float (&xf)[32], float yh, f
       if (RESCALE) f *= k;
       q[t] = __builtin_fmaf(f, yh, f * yl);
     }
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    // the first conversion's other half is overwritten by the second, so any register serves as
+    // its old value (q[0]'s own: no copy of a zero)
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __float_as_int(q[0]), false);
     p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
     w[j] = (uint32_t)p;
   }
@@ -126,7 +128,7 @@ __device__ __forceinline__ void quant32_codes_packed(const u32x4 (&xv)[4], float
       if (RESCALE) f *= k;
       q[t] = __builtin_fmaf(f, yh, f * yl);
     }
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __float_as_int(q[0]), false);
     p = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], p, true);
     w[j] = (uint32_t)p;
   }
