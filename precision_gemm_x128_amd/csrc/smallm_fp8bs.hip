@@ -1098,20 +1098,24 @@ __global__ __launch_bounds__(kTThreads) void tiled_gemm_kernel(
     }
   };
   // unconditional stores (a conditional one lets the compiler sink its load past the loads issued
-  // after it): elements past the tile go to a pad entry nothing reads
+  // after it): elements past the tile go to a pad entry nothing reads.  Row e / KB by a float
+  // multiply: for an element of the tile (e < TM KB <= 8192), (e + 1/2) / KB < 64 lies at least
+  // 1/(2 KB) >= 1/256 from an integer, and the product with the reciprocal (a few units of 2^-24
+  // relative) is within 2^-16 of it, so it floors to the exact quotient.
+  const float rkb = __builtin_amdgcn_rcpf((float)KB);
   auto store_sx = [&](const uint32_t (&v)[4], int e0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + kTThreads * j + tid;
-      const int row = e / KB, kb = e - row * KB;
+      const int row = (int)(((float)e + 0.5f) * rkb), kb = e - row * KB;
       sxs[(e < nsx) ? kb * SXP + row : TM] = v[j];
     }
   };
-  // weight block scales: thread t takes region t / 128, row (A or remainder) (t / 64) % 2, K
-  // blocks lane and lane + 64
-  const int sreg = min((int)blockIdx.x * kTiledRegions + (tid >> 7), NWG - 1);
-  const int snb = ((tid >> 6) & 1) ? (16 * NA * NWG + CB * sreg) >> 7 : (16 * sreg) >> 7;
-  const bool sown = ((tid >> 6) & 1) ? HASB : (NA != 0);
+  // weight block scales: wave w takes region w / 2, row (A or remainder) w % 2, K blocks lane and
+  // lane + 64 (wave-uniform, so the buffer resource is a scalar one)
+  const int sreg = min((int)blockIdx.x * kTiledRegions + (wave >> 1), NWG - 1);
+  const int snb = (wave & 1) ? (16 * NA * NWG + CB * sreg) >> 7 : (16 * sreg) >> 7;
+  const bool sown = (wave & 1) ? HASB : (NA != 0);
   const __amdgpu_buffer_rsrc_t swsr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint8_t*)sw + (int64_t)snb * KB * es), 0, sown ? KB * (int)es : 0, 0x00020000);
   uint32_t sv[2], xv[4];
@@ -1290,6 +1294,9 @@ __global__ __launch_bounds__(kTThreads) void tiled_gemm_kernel(
   // 16 wait states on every path before the accumulators are read (the loop ends in branches)
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(accA[i]), "+v"(accB[i]));
+  // this lane's first output row (rows 4 (lane / 16) + e of each subtile), formed before the
+  // barriers
+  uint16_t* const ylane = y + (int64_t)(m0 + 4 * (lane >> 4)) * ldy;
   // every wave is done reading the ring: it now takes the second half's accumulators
   lds_release();
   __builtin_amdgcn_s_barrier();
@@ -1332,9 +1339,9 @@ __global__ __launch_bounds__(kTThreads) void tiled_gemm_kernel(
     for (int e = 0; e < 4; ++e) {
       const int r = i * 16 + 4 * (lane >> 4) + e;
       if (r < Mt) {
-        if (NA) y[(int64_t)(m0 + r) * ldy + 16 * reg + jl] = bf16_rne(accA[i][e]);
-        if (HASB && bcol && sl == 0)
-          y[(int64_t)(m0 + r) * ldy + 16 * NA * NWG + CB * reg + jl / SB] = bf16_rne(pb[e]);
+        uint16_t* const yr = ylane + (int64_t)(i * 16 + e) * ldy;
+        if (NA) yr[16 * reg + jl] = bf16_rne(accA[i][e]);
+        if (HASB && bcol && sl == 0) yr[16 * NA * NWG + CB * reg + jl / SB] = bf16_rne(pb[e]);
       }
     }
   }
