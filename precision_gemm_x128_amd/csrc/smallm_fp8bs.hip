@@ -853,6 +853,30 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
     const uint32_t sbytes_x = (uint32_t)(Mc * KB) * (Cfg::kE8 ? 1u : 4u);
     const __amdgpu_buffer_rsrc_t sxr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)sa_src + (int64_t)m0 * KB * (Cfg::kE8 ? 1 : 4)), 0, (int)sbytes_x, 0x00020000);
+    // Which 32 values of its group lane c of a quad holds.  bf16 rows with one 16-row tile:
+    // lane c's load i takes elements 32 i + 8 c + [0, 8), so each load instruction reads 64
+    // contiguous bytes of every group (half of one 128-byte line, where lane-contiguous quarters
+    // touch two lines); the quantiser is indifferent to the order, and the staged row gets the
+    // lane's codes back in place.  Otherwise lane c holds the contiguous values 32 c + [0, 32):
+    // pre-quantised rows take one line per group anyway, and the two-tile loop measured no
+    // better interleaved.
+    constexpr bool kInter = !Cfg::kPreq && MT == 1;
+    constexpr int lane_elem = kInter ? 8 : 32;
+    constexpr uint32_t load_step = kInter ? 64u : 16u;
+    auto stage = [&](uint8_t* row, int c, const u32x4 (&qv)[2]) {
+      if constexpr (!kInter) {
+        u32x4* dp = (u32x4*)(row + c * 32);
+        dp[0] = qv[0];
+        dp[1] = qv[1];
+      } else {
+        // the lane's codes in element order: bytes 8 i + [0, 8) belong at 32 i + 8 c + [0, 8)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4& h = qv[i >> 1];
+          *(uint2*)(row + 32 * i + 8 * c) = (i & 1) ? uint2{h[2], h[3]} : uint2{h[0], h[1]};
+        }
+      }
+    };
     uint32_t rd = 0;
     for (int kr = kw0; kr < kw1; kr += RC, ++rd) {
       int ln;
@@ -871,10 +895,10 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
             const int g = p * 16 + grp;
             const int m = g / RC, kbl = g & (RC - 1);
             const bool valid = g < G && kbl < nk;
-            const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * 32) * rowb) : xbytes;
+            const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * lane_elem) * rowb) : xbytes;
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-              xv[p][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0));
+              xv[p][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + load_step * i, 0, 0));
             if (Cfg::kPreq) {
               const uint32_t so = valid ? (uint32_t)(m * KB + kr + kbl) * (Cfg::kE8 ? 1u : 4u) : sbytes_x;
               xs[p] = Cfg::kE8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sxr, so, 0, 0)
@@ -906,9 +930,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
             // K blocks past the range (a short last round) are staged too: their loads returned
             // zeros, so the MFMAs on them see zero codes and scales instead of stale LDS
             if (g < G) {
-              u32x4* dp = (u32x4*)(stq + (kbl * MP + m) * kRowStride + c * 32);
-              dp[0] = qv[0];
-              dp[1] = qv[1];
+              stage(stq + (kbl * MP + m) * kRowStride, c, qv);
               if (c == 0) {
                 if (Cfg::kE8) sts_b[kbl * MP + m] = (uint8_t)eb;
                 else sts_f[kbl * MP + m] = sc;
@@ -933,10 +955,10 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
           const int g = p * 16 + grp;
           const int m = g / RC, kbl = g & (RC - 1);
           const bool valid = g < G && kbl < nk;
-          const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * 32) * rowb) : xbytes;
+          const uint32_t off = valid ? (uint32_t)(((int64_t)m * lda + (kr + kbl) * 128 + c * lane_elem) * rowb) : xbytes;
 #pragma unroll
           for (int i = 0; i < NV; ++i)
-            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0));
+            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + load_step * i, 0, 0));
           if (Cfg::kPreq) {
             const uint32_t so = valid ? (uint32_t)(m * KB + kr + kbl) * (Cfg::kE8 ? 1u : 4u) : sbytes_x;
             sv = Cfg::kE8 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sxr, so, 0, 0)
@@ -959,9 +981,7 @@ __global__ __launch_bounds__(1024) void smallm_gemm_kernel(
             else sc = __uint_as_float(sv);
           }
           if (g < G) {
-            u32x4* dp = (u32x4*)(stq + (kbl * MP + m) * kRowStride + c * 32);
-            dp[0] = qv[0];
-            dp[1] = qv[1];
+            stage(stq + (kbl * MP + m) * kRowStride, c, qv);
             if (c == 0) {
               if (Cfg::kE8) sts_b[kbl * MP + m] = (uint8_t)eb;
               else sts_f[kbl * MP + m] = sc;
