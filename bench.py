@@ -322,7 +322,8 @@ def moe_sweeps(P, torch, np, synthgen, dev, reps, layers=MOE_LAYERS):
             nbytes = sum(P.moe_algorithmic_bytes(r[0], E, H, I, mxfp4=fp4) for r in routes) / layers
             gbs = nbytes / (us * 1e-6) / 1e9
             e = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes), "GB_s": round(gbs, 1),
-                 "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1), "launches": 2 + (P.smallm_fp8bs_moe_splits(T, S) > 1)}
+                 "pct_peak": round(100 * gbs / PEAK_HBM_GBS, 1), "launches": 2,
+                 "splits": P.smallm_fp8bs_moe_splits(T, S)}
             if not fp4 and T in PAGES_MOE_FP8_US[I]:
                 e["pages_fp8_kernel_us"] = PAGES_MOE_FP8_US[I][T]
             d[str(T)] = e

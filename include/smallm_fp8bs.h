@@ -271,14 +271,16 @@ int smallm_fp8bs_moe_unpack(const uint8_t* w_packed, uint8_t* w8, int E, int R, 
 /* Workspace bytes smallm_fp8bs_moe needs for (T, S, H, I), 0 when out of range: the bf16
  * intermediate h [T * S, I] rounded up to 256 bytes, then, when the down projection is split over
  * NS = smallm_fp8bs_moe_splits(T, S) > 1 workgroups per output tile, fp32 partial sums
- * [NS, T, H].  Its contents need no initialisation; calls that share a workspace must not
- * overlap. */
+ * [NS, T, H] and one uint32 arrival counter per 16 output columns (each rounded up to 256
+ * bytes).  Its contents need no initialisation (the first launch clears the counters); calls that
+ * share a workspace must not overlap. */
 size_t smallm_fp8bs_moe_workspace_bytes(int T, int S, int H, int I);
 
 /* NS for (T, S): 1 when T * S <= 128, else 2; 0 when out of range. */
 int smallm_fp8bs_moe_splits(int T, int S);
 
-/* The layer: two launches on `stream`, three when NS > 1.  x: bf16 [T, ldx]; topk_ids: int32
+/* The layer: two launches on `stream` (with NS > 1 the second launch's workgroup that finishes a
+ * tile last adds the tile's partial sums, in split order).  x: bf16 [T, ldx]; topk_ids: int32
  * [T, S] expert ids (a pair whose id lies outside [0, E) contributes nothing and its h row is not
  * written; a token may name one expert in several slots, whose weights then add); topk_w: fp32
  * [T, S]; w13_packed / w2_packed from smallm_fp8bs_moe_pack with layout_id =

@@ -22,7 +22,8 @@
 //    columns, each over a contiguous range of pairs; every workgroup finds the first pair of each expert with an LDS integer min
 //    and its waves walk the experts whose first pair lies in its range, gathering each expert's
 //    tokens into MFMA rows as phase 1 does.  With NS > 1 the workgroups leave fp32 partial sums
-//    in the caller's workspace and a third launch adds them in range order.
+//    in the caller's workspace and the last of a tile's workgroups to finish adds them in range
+//    order (two launches in every case).
 //  * Packed weights: every 16-row x 128-K block of an expert matrix is one 2 KiB fragment in
 //    the lane order of an MFMA operand (lane l = 16 c + j holds row j and K bytes [32 c, 32 c + 32)
 //    of the block, bytes 0..15 in the first KiB and 16..31 in the second), fragments of one
@@ -265,6 +266,12 @@ __device__ __forceinline__ void gather_tokens(int e, int T, int S, const int* s_
   if (lane == 0) s_tok[SMALLM_FP8BS_MOE_MAX_T] = __popcll(m);
 }
 
+// Phase 2's per-tile arrival counters start every call at zero: one workgroup of phase 1 clears
+// them (the launches are ordered on the stream, so phase 2 sees the zeros).
+__device__ __forceinline__ void zero_counters(uint32_t* cnt, int ncnt) {
+  for (int i = threadIdx.x; i < ncnt; i += blockDim.x) cnt[i] = 0u;
+}
+
 // Up to 128 pairs (32 for MXFP4): grid (T * S, I / 8).  Workgroup (p, q) works when pair p is
 // the first pair naming its expert e, on item (e, q); the others leave after one pass over the
 // ids in LDS.
@@ -272,13 +279,15 @@ template <bool FP4>
 __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
-    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
+    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h, uint32_t* __restrict__ cnt,
+    int ncnt) {
   __shared__ int s_ids[kMoePairs];
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];
   __shared__ float s_red[kGateWaves * 4 * 64];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int P = T * S;
   const int p = blockIdx.x, q = blockIdx.y;
+  if (p == 0 && q == 0) zero_counters(cnt, ncnt);
   for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
   __syncthreads();
   const int e = s_ids[p];
@@ -300,7 +309,8 @@ __global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(8)
 void moe_gate_up_items_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
-    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h) {
+    const uint8_t* __restrict__ s13, int H, int I, uint16_t* __restrict__ h, uint32_t* __restrict__ cnt,
+    int ncnt) {
   __shared__ int s_ids[kMoePairs];
   __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];   // first pair naming each expert
   __shared__ int s_dexp[kMoePairs];                 // the distinct experts, by first pair
@@ -312,6 +322,7 @@ void moe_gate_up_items_kernel(
   // stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = T * S;
+  if (blockIdx.x == 0) zero_counters(cnt, ncnt);
   for (int i = tid; i < P; i += kGateThreads) s_ids[i] = ids[i];
   for (int i = tid; i < E; i += kGateThreads) s_first[i] = INT_MAX;
   __syncthreads();
@@ -356,19 +367,21 @@ void moe_gate_up_items_kernel(
 // (ascending, each with the first slot naming e and the sum of the top-k weights of the slots
 // naming e), runs one 16-row MFMA tile per 16 of those tokens over the expert's K blocks, and adds
 // weight * (h . w2[e]^T) into the token's row of its own LDS slice.  The slices meet in wave
-// order.  With NS = 1 the workgroup writes bf16 y, else the fp32 partial [z][t][n] that
-// moe_reduce_kernel adds in z order.  (Adding the partials in the last workgroup to arrive would
-// need a device-scope fence per workgroup, which on this target writes back and invalidates the
-// whole L2 and measured several times slower than the extra launch.)  Every result is
-// deterministic.
+// order.  With NS = 1 the workgroup writes bf16 y.  Otherwise it writes its fp32 partial
+// [z][t][n] with device-coherent stores (written through to the point where every XCD sees them;
+// a device-scope fence instead would write back and invalidate the whole L2, which measured
+// several times slower), waits until they are complete, and counts its arrival on the tile's
+// counter; the workgroup that arrives last reads the other partials with device-coherent loads,
+// adds them in z order and writes bf16 y.  Every result is deterministic.
 
 template <int MT, bool FP4>
 __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ tw,
     int T, int S, int E, const uint8_t* __restrict__ w2, const float* __restrict__ sw2,
     const uint8_t* __restrict__ s2, int H, int I, uint16_t* __restrict__ y, int64_t ldy,
-    float* __restrict__ part) {
+    float* __restrict__ part, uint32_t* __restrict__ cnt) {
   constexpr int ROWS = 16 * MT;
+  __shared__ int s_last;
   __shared__ int s_ids[kMoePairs];
   __shared__ float s_tw[kMoePairs];
   __shared__ int s_first[SMALLM_FP8BS_MOE_MAX_E];
@@ -481,36 +494,35 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
   }
   __syncthreads();
 
-  // this workgroup's T x 16 result: the wave slices in wave order
+  // this workgroup's T x 16 result: the wave slices in wave order (T * 16 <= 768 outputs, at
+  // most one per thread)
+  static_assert(SMALLM_FP8BS_MOE_MAX_T * 16 <= kDownThreads, "one output per thread");
   const int64_t col0 = (int64_t)blockIdx.x * 16;
-  for (int o = tid; o < T * 16; o += kDownThreads) {
-    const int t = o >> 4, c = o & 15;
-    float v = 0.0f;
+  const int o = tid, t = o >> 4, c = o & 15;
+  const bool has = o < T * 16;
+  float v = 0.0f;
+  if (has) {
 #pragma unroll
     for (int w = 0; w < kDownWaves; ++w) v = v + s_acc[w][t][c];
-    if (NS == 1)
-      y[(int64_t)t * ldy + col0 + c] = bf16_bits(v);
-    else
-      part[((int64_t)z * T + t) * H + col0 + c] = v;
   }
-}
-
-// y[t, n] = bf16(sum over z = 0 .. NS-1 of part[z][t][n]), four outputs per thread
-__global__ __launch_bounds__(256) void moe_reduce_kernel(const float* __restrict__ part, int NS,
-                                                         int T, int H, uint16_t* __restrict__ y,
-                                                         int64_t ldy) {
-  const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (o >= (int64_t)T * H) return;
-  v4f v = *(const v4f*)(part + o);
-  for (int z = 1; z < NS; ++z) {
-    const v4f w = *(const v4f*)(part + (int64_t)z * T * H + o);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = v[i] + w[i];
+  if (NS == 1) {
+    if (has) y[(int64_t)t * ldy + col0 + c] = bf16_bits(v);
+    return;
   }
-  const int64_t t = o / H, n = o % H;
-  uint16_t* yp = y + t * ldy + n;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) yp[i] = bf16_bits(v[i]);
+  if (has) __hip_atomic_store(part + ((int64_t)z * T + t) * H + col0 + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial is stored
+  __syncthreads();                     // and every thread's
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(NS - 1);
+  __syncthreads();
+  if (!s_last || !has) return;
+  float sum = 0.0f;
+  for (int zz = 0; zz < NS; ++zz) {
+    const float w = zz == z ? v : __hip_atomic_load(part + ((int64_t)zz * T + t) * H + col0 + c, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+    sum = zz == 0 ? w : sum + w;
+  }
+  y[(int64_t)t * ldy + col0 + c] = bf16_bits(sum);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -636,9 +648,14 @@ inline int moe_splits(int T, int S) { return T * S <= 128 ? 1 : 2; }
 
 inline size_t moe_h_bytes(int T, int S, int I) { return ((size_t)T * S * I * 2 + 255) & ~(size_t)255; }
 
-inline size_t moe_workspace_bytes(int T, int S, int H, int I) {
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline size_t moe_part_bytes(int T, int S, int H) {
   const int ns = moe_splits(T, S);
-  return moe_h_bytes(T, S, I) + (ns > 1 ? (size_t)ns * T * H * 4 : 0);
+  return ns > 1 ? align256((size_t)ns * T * H * 4) : 0;
+}
+// h, then with NS > 1 the partial sums and one arrival counter per 16-column output tile
+inline size_t moe_workspace_bytes(int T, int S, int H, int I) {
+  return moe_h_bytes(T, S, I) + (moe_splits(T, S) > 1 ? moe_part_bytes(T, S, H) + align256((size_t)(H / 16) * 4) : 0);
 }
 
 template <int MT, bool FP4>
@@ -647,25 +664,22 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
                 const float* sw2, const uint8_t* s2, int E, int H, int I, uint8_t* ws,
                 uint16_t* y, int64_t ldy, hipStream_t st) {
   uint16_t* h = (uint16_t*)ws;
-  float* part = (float*)(ws + moe_h_bytes(T, S, I));
   const int ns = moe_splits(T, S);
+  float* part = ns > 1 ? (float*)(ws + moe_h_bytes(T, S, I)) : nullptr;
+  uint32_t* cnt = ns > 1 ? (uint32_t*)(ws + moe_h_bytes(T, S, I) + moe_part_bytes(T, S, H)) : nullptr;
+  const int ncnt = ns > 1 ? H / 16 : 0;
   if (T * S <= (FP4 ? kGateItemsFromFp4 : kGateItemsFrom)) {
     hipLaunchKernelGGL((moe_gate_up_pairs_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st,
-                       x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
+                       x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h, cnt, ncnt);
   } else {
     const int max_items = (T * S < E ? T * S : E) * (I / 8);
     const int most = FP4 ? kGateGridFp4 : kGateGrid;
     const int grid = max_items < most ? max_items : most;
     hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(grid),
-                       dim3(kGateThreads), 0, st, x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h);
+                       dim3(kGateThreads), 0, st, x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h, cnt, ncnt);
   }
   hipLaunchKernelGGL((moe_down_kernel<MT, FP4>), dim3(H / 16, ns), dim3(kDownThreads), 0, st, h, ids,
-                     tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part);
-  if (ns > 1) {
-    const int64_t quads = (int64_t)T * H / 4;
-    hipLaunchKernelGGL(moe_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
-                       part, ns, T, H, y, ldy);
-  }
+                     tw, T, S, E, w2, sw2, s2, H, I, y, ldy, part, cnt);
 }
 
 // Shared argument checks (all before any launch) and the M-bucket dispatch of both weight formats.

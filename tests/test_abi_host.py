@@ -235,7 +235,8 @@ def test_moe_rejections_happen_before_any_launch():
     assert P.smallm_fp8bs_moe_splits(0, 11) == 0 and P.smallm_fp8bs_moe_splits(4, 17) == 0
     assert P.smallm_fp8bs_moe_workspace_bytes(1, 11, 4096, 256) == 11 * 256 * 2          # 22 x 256 bytes
     assert P.smallm_fp8bs_moe_workspace_bytes(1, 3, 4096, 128) == 768
-    assert P.smallm_fp8bs_moe_workspace_bytes(20, 11, 4096, 256) == 220 * 256 * 2 + 2 * 20 * 4096 * 4
+    # h, the split partials, one arrival counter per 16 output columns (256 counters = 1 KiB)
+    assert P.smallm_fp8bs_moe_workspace_bytes(20, 11, 4096, 256) == 220 * 256 * 2 + 2 * 20 * 4096 * 4 + 1024
     assert P.smallm_fp8bs_moe_workspace_bytes(49, 11, 4096, 256) == 0
     assert P.smallm_fp8bs_moe_supported(48, 16, 4096, 16384, 2048) == 0
     assert P.smallm_fp8bs_moe_supported(1, 1, 1, 128, 128) == 0

@@ -265,7 +265,7 @@ def test_moe_deterministic_and_graph_replay_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
-    assert P.smallm_fp8bs_moe_splits(T, S) > 1          # the three-launch form is captured
+    assert P.smallm_fp8bs_moe_splits(T, S) > 1          # the split form is captured
     yg = torch.zeros_like(y1)
     ws = P.moe_workspace(T, S, H, I)
     hg = P.moe_h_view(ws, T, S, I)
@@ -288,6 +288,46 @@ def test_moe_deterministic_and_graph_replay_bitwise():
         assert torch.equal(hg.view(torch.int16), h1.view(torch.int16)), f"replay {i}"
         _ = (x.float() * 2).sum()
         torch.cuda.synchronize()
+
+
+def test_moe_split_partials_summed_by_the_last_workgroup():
+    # Above 128 pairs two workgroups share each output tile; the one that finishes last reads the
+    # other's fp32 partial (written through to the device coherence point) and writes y.  A graph
+    # of 48 calls alternating between two inputs over one workspace must give every call the
+    # output of an eager call on its own input, bit for bit: a partial read before it landed, or
+    # one left over from the previous call (the other input), would show as a mismatch.
+    note("moe split partials, 48 calls in a graph")
+    T, S, E, H, I = 24, 11, 513, 4096, 128
+    assert P.smallm_fp8bs_moe_splits(T, S) > 1
+    B = bank(E, H, I)
+    ids, tw = synthgen.gen_moe_routing(T, S, E, seed=31)
+    w13p, sw13, w2p, sw2 = B.packed(ids)
+    idd = torch.from_numpy(ids).to(DEV)
+    twd = torch.from_numpy(tw).to(DEV)
+    xs = [to_dev_bf16(synthgen.gen_x(T, H, seed=31 + k)) for k in range(2)]
+    refs = [P.smallm_fp8bs_moe(x, idd, twd, w13p, sw13, w2p, sw2)[0] for x in xs]
+    torch.cuda.synchronize()
+    assert not torch.equal(refs[0].view(torch.int16), refs[1].view(torch.int16))
+    n = 48
+    ws = P.moe_workspace(T, S, H, I)
+    ys = torch.zeros((n, T, H), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        P.smallm_fp8bs_moe(xs[0], idd, twd, w13p, sw13, w2p, sw2, workspace=ws, y=ys[0])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            P.smallm_fp8bs_moe(xs[i % 2], idd, twd, w13p, sw13, w2p, sw2, workspace=ws, y=ys[i])
+    for rep in range(3):
+        ys.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(n):
+            assert torch.equal(ys[i].view(torch.int16), refs[i % 2].view(torch.int16)), f"replay {rep} call {i}"
 
 
 def test_moe_binding_errors_on_device():
