@@ -262,7 +262,8 @@ __device__ __forceinline__ void gather_tokens(int e, int T, int S, const int* s_
   if (lane < T)
     for (int s = 0; s < S; ++s) mine |= (s_ids[lane * S + s] == e);
   const uint64_t m = __ballot(mine);
-  if (mine) s_tok[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+  // the routed lanes below this one, counted by mbcnt (no 64-bit lane mask held in registers)
+  if (mine) s_tok[__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = lane;
   if (lane == 0) s_tok[SMALLM_FP8BS_MOE_MAX_T] = __popcll(m);
 }
 
