@@ -192,13 +192,15 @@ def smallm_fp8bs_launch_plan(M: int, N: int, K: int) -> dict:
 def kernel_name(M: int, N: int, K: int, mode: int = 0) -> str:
     """Name of the GEMM kernel instantiation (mode 0 fused fp32, 1 fused e8m0, 2/3 pre-quantised),
     as the profiler prints it.  Above the small-M range the pre-quantised entries run the tiled
-    kernel (32-row tiles up to 64 rows, else 64), and the fused entries with a workspace run the
+    kernel (32-row tiles up to 128 rows or on layouts without a 16-column group, else 64), and
+    the fused entries with a workspace run the
     standalone quantisation before it (the library asks for a workspace exactly then)."""
     p = smallm_fp8bs_launch_plan(M, N, K)
     hasb = "true" if p["CB"] else "false"
     if smallm_fp8bs_quant_gemm_workspace_bytes(M, N, K) > 0:
         e8 = "true" if mode in (1, 3) else "false"
-        tiled = f"tiled_gemm_kernel<{32 if M <= 64 else 64}, {e8}, {p['NA']}, {hasb}, {p['SB']}>"
+        tm = 32 if (M <= 128 or p["NA"] == 0) else 64
+        tiled = f"tiled_gemm_kernel<{tm}, {e8}, {p['NA']}, {hasb}, {p['SB']}>"
         return tiled if mode >= 2 else f"quant_act_kernel<{e8}> + {tiled}"
     return f"smallm_gemm_kernel<{p['MT']}, {mode}, {p['NA']}, {hasb}, {p['SB']}, {p['RC']}>"
 

@@ -1520,14 +1520,21 @@ void launch_mt(const Layout& L, int K, dim3 grid, hipStream_t stream, const void
 
 constexpr int kTiledFromM = 32;  // M above which the pre-quantised GEMM is tiled
 
-// Rows per workgroup tile of the tiled kernel at M rows.
-int tiled_tm(int M) { return M <= 64 ? 32 : 64; }
+// Rows per workgroup tile of the tiled kernel at M rows on layout L.  Up to 128 rows 32-row tiles:
+// on the pages' shapes (64 tiles of four column regions) they give 128-256 workgroups where
+// 64-row tiles give 64-128, half the CUs idle.  Above 128 rows 64-row tiles (half the weight
+// re-reads), except on layouts without a 16-column group, whose 32-row kernel fits two
+// workgroups per CU.  Measured (GEMM alone, graph replay over 24 cold copies, us, 32 / 64-row
+// tiles): 4096x2048 at 96 / 128 / 192 / 256 rows 5.8 / 7.8, 5.9 / 7.9, 8.0 / 8.0, 8.5 / 8.3;
+// 5120x4096 12.0 / 15.7, 12.1 / 16.0, 19.4 / 16.1, 20.4 / 17.3; 4608x4096 like 5120x4096;
+// 2048x4096 7.4 / 10.8, 7.7 / 10.9, 10.3 / 10.9, 10.9 / 11.2.
+int tiled_tm(int M, const Layout& L) { return (M <= 128 || L.na == 0) ? 32 : 64; }
 
 // The tiled kernel takes the shape: at most 128 K blocks (its e8m0 weight scales sit in two
 // registers) and a tile's activation rows inside a 32-bit buffer offset.
-bool tiled_ok(int M, int K, int64_t ldq) {
+bool tiled_ok(int M, int K, int64_t ldq, const Layout& L) {
   return M > kTiledFromM && K / 128 <= kTiledMaxKB &&
-         (ldq * (tiled_tm(M) - 1) + K) < ((int64_t)1 << 31);
+         (ldq * (tiled_tm(M, L) - 1) + K) < ((int64_t)1 << 31);
 }
 
 template <bool E8, int TM>
@@ -1553,7 +1560,7 @@ void launch_tiled_tm(const Layout& L, int M, int K, const uint8_t* q, int64_t ld
 template <bool E8>
 void launch_tiled(const Layout& L, int M, int K, const uint8_t* q, int64_t ldq, const void* sa,
                   const uint8_t* wp, const void* sw, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  if (tiled_tm(M) == 32) launch_tiled_tm<E8, 32>(L, M, K, q, ldq, sa, wp, sw, y, ldy, stream);
+  if (tiled_tm(M, L) == 32) launch_tiled_tm<E8, 32>(L, M, K, q, ldq, sa, wp, sw, y, ldy, stream);
   else launch_tiled_tm<E8, 64>(L, M, K, q, ldq, sa, wp, sw, y, ldy, stream);
 }
 
@@ -1562,7 +1569,7 @@ int launch_gemm(const void* a, int64_t lda, const void* sa, const uint8_t* wp, c
                 uint16_t* y, int64_t ldy, int M, int N, int K, uint8_t* q_dbg, void* sx_dbg,
                 hipStream_t stream) {
   const Layout L = layout_for(N, K);
-  if ((MODE & 2) && tiled_ok(M, K, lda)) {
+  if ((MODE & 2) && tiled_ok(M, K, lda, L)) {
     // pre-quantised input beyond the small-M range: every weight fragment is read by
     // ceil(M / TM) workgroups instead of ceil(M / 32) small-M workgroups
     launch_tiled<(MODE & 1) != 0>(L, M, K, (const uint8_t*)a, lda, sa, wp, sw, y, ldy, stream);
@@ -1796,7 +1803,7 @@ int smallm_fp8bs_quant_gemm_e8m0(const uint16_t* x, int64_t ldx, const uint8_t* 
 constexpr int kFusedUpToM = 32;
 
 size_t smallm_fp8bs_quant_gemm_workspace_bytes(int M, int N, int K) {
-  if (check_mnk(M, N, K) != SMALLM_OK || M <= kFusedUpToM || !tiled_ok(M, K, K)) return 0;
+  if (check_mnk(M, N, K) != SMALLM_OK || M <= kFusedUpToM || !tiled_ok(M, K, K, layout_for(N, K))) return 0;
   const size_t qb = ((size_t)M * K + 255) / 256 * 256;
   return qb + (size_t)M * (K / 128) * 4;
 }

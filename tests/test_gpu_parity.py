@@ -450,7 +450,7 @@ def test_config_beyond_small_m(M):
 
 
 @pytest.mark.parametrize("e8m0", [False, True])
-@pytest.mark.parametrize("M", [33, 64, 256])
+@pytest.mark.parametrize("M", [33, 64, 128, 256])
 @pytest.mark.parametrize("N,K", [(5120, 4096), (4608, 4096), (4096, 2048), (2048, 4096)])
 def test_beyond_small_m_every_layout(N, K, M, e8m0):
     """Past the small-M cap on each packed layout (16-column groups; 16 + 4, 16 + 2 and 8-column
