@@ -363,11 +363,12 @@ void moe_gate_up_items_kernel(
 // ---------------------------------------------------------------------------------------------
 //
 // grid (H / 16, NS), 1024 threads.  Workgroup (b, z) owns output columns [16 b, 16 b + 16) and the
-// pairs [z P / NS, (z + 1) P / NS).  Wave w takes the pairs of that range with index = w (mod 16)
-// that are the first pair of their expert e.  It gathers the tokens routed to e with a ballot
-// (ascending, each with the first slot naming e and the sum of the top-k weights of the slots
-// naming e), runs one 16-row MFMA tile per 16 of those tokens over the expert's K blocks, and adds
-// weight * (h . w2[e]^T) into the token's row of its own LDS slice.  The slices meet in wave
+// pairs [z P / NS, (z + 1) P / NS).  The experts whose first pair lies in that range, in pair
+// order, are dealt round-robin to the 16 waves; for each of its experts e a wave gathers the
+// tokens routed to e with a ballot (ascending, each with the first slot naming e and the sum of
+// the top-k weights of the slots naming e), runs one 16-row MFMA tile per 16 of those tokens over
+// the expert's K blocks, and adds weight * (h . w2[e]^T) into the token's row of its own LDS
+// slice.  The slices meet in wave
 // order.  With NS = 1 the workgroup writes bf16 y.  Otherwise it writes its fp32 partial
 // [z][t][n] with device-coherent stores (written through to the point where every XCD sees them;
 // a device-scope fence instead would write back and invalidate the whole L2, which measured
@@ -414,81 +415,94 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
   const int j = lane & 15, chunk = lane >> 4;
   const uint8_t* wtile = w2 + (int64_t)blockIdx.x * KB2 * (FP4 ? 1024 : 2048) + lane * 16;
 
-  for (int p = lo + wave; p < hi; p += kDownWaves) {
-    const int e = s_ids[p];
-    if (e < 0 || e >= E || s_first[e] != p) continue;
-    const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
-    const uint8_t* sbp =
-        FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
-    const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
-    // the first K block's weights and scale depend only on the expert, so they are loaded before
-    // the gather and are in flight during it
-    u32x4 pre0 = u32x4{0u, 0u, 0u, 0u}, pre1 = u32x4{0u, 0u, 0u, 0u};
-    float pre_s = 0.0f;
-    if constexpr (!FP4) {
-      pre0 = load_nt(wp);
-      pre1 = load_nt(wp + 1024);
-      pre_s = swp[0];
-    } else {
-      pre0 = load_nt(wp);
-      pre_s = e8m0_f32(sbp[0]);
-    }
-    // gather: lane t (< T) is routed to e when some slot of token t names it
-    int slot = -1;
-    float wsum = 0.0f;
-    if (lane < T)
-      for (int s = 0; s < S; ++s)
-        if (s_ids[lane * S + s] == e) {
-          if (slot < 0) slot = s;
-          wsum = wsum + s_tw[lane * S + s];
-        }
-    const uint64_t m = __ballot(slot >= 0);
-    if (slot >= 0) {
-      const int k = __popcll(m & ((1ull << lane) - 1ull));
-      s_tok[wave][k] = lane;
-      s_hrow[wave][k] = lane * S + slot;
-      s_wt[wave][k] = wsum;
-    }
-    const int Me = __popcll(m);
-    for (int tile = 0; tile * 16 < Me; ++tile) {
-      const int k = 16 * tile + j;
-      const bool ok = k < Me;
-      const uint16_t* hr = h + (int64_t)(ok ? s_hrow[wave][k] : 0) * I + chunk * 32;
-      v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int kb = 0; kb < KB2; ++kb) {
-        v8bf bv[4];
-        float sc;
-        if constexpr (FP4) {
-          // the group scale is applied by the conversion; the partial needs no block scale
-          const bool first = tile == 0 && kb == 0;
-          fp4x32_to_bf16(first ? pre0 : load_nt(wp + (int64_t)kb * 1024),
-                         first ? pre_s : e8m0_f32(sbp[(int64_t)kb * 64]), bv);
-          sc = 1.0f;
-        } else {
-          const bool first = tile == 0 && kb == 0;
-          const u32x4 b0 = first ? pre0 : load_nt(wp + (int64_t)kb * 2048);
-          const u32x4 b1 = first ? pre1 : load_nt(wp + (int64_t)kb * 2048 + 1024);
-          sc = first ? pre_s : swp[kb];
-          e4m3x32_to_bf16(b0, b1, bv);
-        }
-        const u32x4* ha = (const u32x4*)(hr + kb * 128);
-        u32x4 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = ok ? ha[i] : u32x4{0u, 0u, 0u, 0u};
-        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + sc * pm[i];
+  // the distinct experts of the range (each at its first pair), in pair order, dealt round-robin
+  // to the waves: every wave scans the range 64 pairs at a time and takes the experts whose rank
+  // in the list is its index mod kDownWaves, so no wave has more than one expert over another
+  int d0 = 0;  // distinct experts before this batch of pairs
+  for (int c0 = lo; c0 < hi; c0 += 64) {
+    const int pp = c0 + lane;
+    const int ec = pp < hi ? s_ids[pp] : -1;
+    const bool first = ec >= 0 && ec < E && s_first[ec] == pp;
+    const uint64_t m = __ballot(first);
+    const int rank = d0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    uint64_t mine = __ballot(first && (rank % kDownWaves) == wave);
+    d0 += __popcll(m);
+    while (mine) {
+      const int e = __builtin_amdgcn_readlane(ec, __builtin_ctzll(mine));
+      mine &= mine - 1;
+      const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
+      const uint8_t* sbp =
+          FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
+      const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
+      // the first K block's weights and scale depend only on the expert, so they are loaded before
+      // the gather and are in flight during it
+      u32x4 pre0 = u32x4{0u, 0u, 0u, 0u}, pre1 = u32x4{0u, 0u, 0u, 0u};
+      float pre_s = 0.0f;
+      if constexpr (!FP4) {
+        pre0 = load_nt(wp);
+        pre1 = load_nt(wp + 1024);
+        pre_s = swp[0];
+      } else {
+        pre0 = load_nt(wp);
+        pre_s = e8m0_f32(sbp[0]);
       }
-      // D row r = 4 (lane / 16) + i is gathered row 16 tile + r; its token's LDS row gets the
-      // weighted partial (rows are distinct tokens, so no two lanes add to one element)
+      // gather: lane t (< T) is routed to e when some slot of token t names it
+      int slot = -1;
+      float wsum = 0.0f;
+      if (lane < T)
+        for (int s = 0; s < S; ++s)
+          if (s_ids[lane * S + s] == e) {
+            if (slot < 0) slot = s;
+            wsum = wsum + s_tw[lane * S + s];
+          }
+      const uint64_t m = __ballot(slot >= 0);
+      if (slot >= 0) {
+        const int k = __popcll(m & ((1ull << lane) - 1ull));
+        s_tok[wave][k] = lane;
+        s_hrow[wave][k] = lane * S + slot;
+        s_wt[wave][k] = wsum;
+      }
+      const int Me = __popcll(m);
+      for (int tile = 0; tile * 16 < Me; ++tile) {
+        const int k = 16 * tile + j;
+        const bool ok = k < Me;
+        const uint16_t* hr = h + (int64_t)(ok ? s_hrow[wave][k] : 0) * I + chunk * 32;
+        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb = 0; kb < KB2; ++kb) {
+          v8bf bv[4];
+          float sc;
+          if constexpr (FP4) {
+            // the group scale is applied by the conversion; the partial needs no block scale
+            const bool first = tile == 0 && kb == 0;
+            fp4x32_to_bf16(first ? pre0 : load_nt(wp + (int64_t)kb * 1024),
+                           first ? pre_s : e8m0_f32(sbp[(int64_t)kb * 64]), bv);
+            sc = 1.0f;
+          } else {
+            const bool first = tile == 0 && kb == 0;
+            const u32x4 b0 = first ? pre0 : load_nt(wp + (int64_t)kb * 2048);
+            const u32x4 b1 = first ? pre1 : load_nt(wp + (int64_t)kb * 2048 + 1024);
+            sc = first ? pre_s : swp[kb];
+            e4m3x32_to_bf16(b0, b1, bv);
+          }
+          const u32x4* ha = (const u32x4*)(hr + kb * 128);
+          u32x4 a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * tile + 4 * chunk + i;
-        if (r < Me) {
-          const int t = s_tok[wave][r];
-          s_acc[wave][t][j] = s_acc[wave][t][j] + s_wt[wave][r] * acc[i];
+          for (int i = 0; i < 4; ++i) a[i] = ok ? ha[i] : u32x4{0u, 0u, 0u, 0u};
+          v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = acc[i] + sc * pm[i];
+        }
+        // D row r = 4 (lane / 16) + i is gathered row 16 tile + r; its token's LDS row gets the
+        // weighted partial (rows are distinct tokens, so no two lanes add to one element)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * tile + 4 * chunk + i;
+          if (r < Me) {
+            const int t = s_tok[wave][r];
+            s_acc[wave][t][j] = s_acc[wave][t][j] + s_wt[wave][r] * acc[i];
+          }
         }
       }
     }
