@@ -101,19 +101,23 @@ __device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi
   }
 }
 
-// the 16 fp4x2 bytes a lane holds (32 e2m1 values of one 32-wide scale group, even K element in
-// each byte's low nibble) as four 8-value bf16 MFMA operands, scaled by the group's power of two
-// inside the conversion
+// the eight e2m1 values of one dword (even K element in each byte's low nibble) as one 8-value
+// bf16 MFMA operand, scaled by a power of two inside the conversion
+__device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t d, float scale) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+  const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// the 16 fp4x2 bytes a lane holds (32 e2m1 values of one 32-wide scale group) as four 8-value
+// bf16 MFMA operands, scaled by the group's power of two inside the conversion
 __device__ __forceinline__ void fp4x32_to_bf16(const u32x4& w, float scale, v8bf out[4]) {
-  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 0);
-    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 1);
-    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 2);
-    const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], scale, 3);
-    out[j] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
-  }
+  out[0] = fp4x8_to_bf16(w.x, scale);
+  out[1] = fp4x8_to_bf16(w.y, scale);
+  out[2] = fp4x8_to_bf16(w.z, scale);
+  out[3] = fp4x8_to_bf16(w.w, scale);
 }
 
 // e8m0 byte b (1 <= b <= 254) as the fp32 2^(b - 127)
@@ -144,22 +148,34 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // 48 to 120 and, with fewer workgroups per CU, measured slower from four tokens on).
 // e4m3 weights (FP4 false): each block's four MFMAs give the fp32 partial that its 128x128 scale
 // multiplies into acc.  MXFP4 weights (FP4 true): the 32-wide group scales are applied by the
-// conversion to bf16, so the partial is added to acc as it is.  Every partial is added in the same
-// block of code as its MFMAs (no MFMA result crosses a branch).
+// conversion to bf16, so the MFMAs accumulate into acc.  Every partial is added in the same block
+// of code as its MFMAs (no MFMA result crosses a branch).  NSL consecutive slices of the expert
+// (16 columns each, their fragments adjacent in the packed layout) share each block's activation
+// loads, one accumulator each.
 // DENSE: every lane loads its activation row (rows past the token count read a valid row and are
 // zeroed after the load), which saves the exec-mask branches and the registers they hold; masked
 // loads (DENSE false) keep the empty rows off the load pipeline that the weight stream shares.
-template <bool FP4, bool DENSE>
-__device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp, const uint8_t* sbp,
-                                            const uint16_t* xr, bool row_ok, int KB, int wave) {
-  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+template <bool FP4, bool DENSE, int NSL>
+__device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp,
+                                             __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                             const uint16_t* xr, bool row_ok, int KB, int wave,
+                                             v4f (&acc)[NSL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) acc[sl] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int kb = wave; kb < KB; kb += kGateWaves) {
-    u32x4 b0, b1;
-    if constexpr (FP4) {
-      b0 = load_nt(wp + (int64_t)kb * 1024);
-    } else {
-      b0 = load_nt(wp + (int64_t)kb * 2048);
-      b1 = load_nt(wp + (int64_t)kb * 2048 + 1024);
+    u32x4 b0[NSL], b1[NSL];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if constexpr (FP4) {
+        // MXFP4: the item's fragments and group scales through wave-uniform buffer resources
+        // (32-bit lane offsets instead of 64-bit addresses)
+        b0[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               wr, (uint32_t)((sl * KB + kb) * 1024 + lane * 16), 0, 2));
+      } else {
+        b0[sl] = load_nt(wp + (int64_t)(sl * KB + kb) * 2048);
+        b1[sl] = load_nt(wp + (int64_t)(sl * KB + kb) * 2048 + 1024);
+      }
     }
     const u32x4* xa = (const u32x4*)(xr + kb * 128);
     u32x4 a[4];
@@ -172,28 +188,45 @@ __device__ __forceinline__ v4f gate_up_loop(const uint8_t* wp, const float* swp,
         a[i] = row_ok ? xa[i] : u32x4{0u, 0u, 0u, 0u};
       }
     }
-    v8bf bv[4];
-    float sc;
     if constexpr (FP4) {
-      fp4x32_to_bf16(b0, e8m0_f32(sbp[(int64_t)kb * 64]), bv);
-      sc = 1.0f;
+      // the group scales are applied by the conversion (one 8-value operand at a time, into the
+      // MFMA that takes it): the MFMAs accumulate into acc
+      float scl[NSL];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+        scl[sl] = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(sr, (uint32_t)((sl * KB + kb) * 64 + lane), 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+          acc[sl] = mfma_bf16(a[i], fp4x8_to_bf16(b0[sl][i], scl[sl]), acc[sl]);
     } else {
-      sc = swp[kb];
-      e4m3x32_to_bf16(b0, b1, bv);
+      // e4m3: each block's four MFMAs give the fp32 partial that its 128x128 scale multiplies
+      const float sc = swp[kb];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        v8bf bv[4];
+        e4m3x32_to_bf16(b0[sl], b1[sl], bv);
+        v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[sl][i] = acc[sl][i] + sc * pm[i];
+      }
     }
-    v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = acc[i] + sc * pm[i];
   }
-  return acc;
+  // MXFP4: the loop ends in a branch and its last MFMAs write acc; 16 wait states on every path
+  // before acc is read
+  if constexpr (FP4) {
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[sl]));
+  }
 }
 
 // Phase 1 for one work item: expert e's 8-column slice q, for the Me tokens listed (ascending) in
 // s_tok.  All threads of the workgroup call it; it ends with a barrier, after which s_tok may be
 // rewritten.
-template <bool FP4, bool DENSE>
+template <bool FP4, bool DENSE, int NSL>
 __device__ __forceinline__ void gate_up_item(
     int e, int q, int Me, const int* s_ids, const int* s_tok, float* s_red,
     const uint16_t* __restrict__ x, int64_t ldx, int S, const uint8_t* __restrict__ w13,
@@ -212,29 +245,30 @@ __device__ __forceinline__ void gate_up_item(
   const int j = lane & 15, chunk = lane >> 4;
   // column j < 8 is gate row 8q + j (scale block row q / 16), j >= 8 the matching up row
   const int srow = (j < 8) ? (q >> 4) : ((I >> 7) + (q >> 4));
-  const float* swp = nullptr;
-  const uint8_t* sbp = nullptr;
-  const uint8_t* wp;
-  if constexpr (FP4) {
-    // 1 KiB fragments; the packed group scales follow the fragment order, one byte per lane
-    wp = w13 + (int64_t)e * I * H + (int64_t)q * KB * 1024 + lane * 16;
-    sbp = s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64 + lane;
-  } else {
-    swp = sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
-    wp = w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
-  }
+  // MXFP4: 1 KiB fragments (the item's NSL slices one after another) and the packed group scales
+  // in fragment order, one byte per lane, through wave-uniform buffer resources
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w13 + (int64_t)e * I * H + (int64_t)q * KB * 1024), 0, FP4 ? NSL * KB * 1024 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64), 0, FP4 ? NSL * KB * 64 : 0, 0x00020000);
+  // e4m3: the slice's 2 KiB fragments and its 128x128 block scales
+  const float* swp = FP4 ? nullptr : sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
+  const uint8_t* wp = FP4 ? nullptr : w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
   // the row tiles one after another (only an expert with more than 16 tokens, in practice the
   // shared one, has a second or third; its weight slice is then re-read from L2)
   for (int tile = 0; tile < tiles; ++tile) {
     const int idx = 16 * tile + j;
     const bool row_ok = idx < Me;
     const uint16_t* xr = x + (int64_t)(row_ok ? s_tok[idx] : 0) * ldx + chunk * 32;
-    const v4f acc = gate_up_loop<FP4, DENSE>(wp, swp, sbp, xr, row_ok, KB, wave);
+    v4f acc[NSL];
+    gate_up_loop<FP4, DENSE, NSL>(wp, swp, wr, sr, xr, row_ok, KB, wave, acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[(wave * 4 + i) * 64 + lane] = acc[i];
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_red[((sl * kGateWaves + wave) * 4 + i) * 64 + lane] = acc[sl][i];
     __syncthreads();
-    if (tid < 128) {
-      const int r = tid >> 3, c = tid & 7;
+    if (tid < 128 * NSL) {
+      const int sl = tid >> 7, r = (tid >> 3) & 15, c = tid & 7;
       const int k = 16 * tile + r;
       if (k < Me) {
         const int t = s_tok[k];
@@ -243,12 +277,12 @@ __device__ __forceinline__ void gate_up_item(
         float g = 0.0f, u = 0.0f;
 #pragma unroll
         for (int w = 0; w < kGateWaves; ++w) {
-          g = g + s_red[w * 256 + base];
-          u = u + s_red[w * 256 + base + 8];
+          g = g + s_red[(sl * kGateWaves + w) * 256 + base];
+          u = u + s_red[(sl * kGateWaves + w) * 256 + base + 8];
         }
         const uint16_t hb = bf16_bits((g / (1.0f + expf(-g))) * u);
         for (int s = 0; s < S; ++s)
-          if (s_ids[t * S + s] == e) h[(int64_t)(t * S + s) * I + 8 * q + c] = hb;
+          if (s_ids[t * S + s] == e) h[(int64_t)(t * S + s) * I + 8 * (q + sl) + c] = hb;
       }
     }
     __syncthreads();
@@ -297,8 +331,8 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
   for (int i = tid; i < p; i += kGateThreads) earlier |= (s_ids[i] == e);
   if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
   if (__syncthreads_or(earlier)) return;
-  gate_up_item<FP4, false>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
-                           w13, sw13, s13, H, I, h);
+  gate_up_item<FP4, false, 1>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
+                              w13, sw13, s13, H, I, h);
 }
 
 // Above that: at most kGateGrid workgroups.  Every workgroup lists the distinct experts in
@@ -317,7 +351,8 @@ void moe_gate_up_items_kernel(
   __shared__ int s_dexp[kMoePairs];                 // the distinct experts, by first pair
   __shared__ int s_nd;
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];
-  __shared__ float s_red[kGateWaves * 4 * 64];
+  constexpr int NSL = FP4 ? 2 : 1;  // 8-column slices per item
+  __shared__ float s_red[NSL * kGateWaves * 4 * 64];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index in a scalar register: loop counters, scale loads and addresses derived from it
   // stay scalar
@@ -345,16 +380,16 @@ void moe_gate_up_items_kernel(
     if (lane == 0) s_nd = nd;
   }
   __syncthreads();
-  const int QN = I >> 3;
+  const int QN = (I >> 3) / NSL;
   const int items = s_nd * QN;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int e = s_dexp[item / QN], q = item % QN;
+    const int e = s_dexp[item / QN], q = NSL * (item % QN);
     if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
     __syncthreads();
     // unmasked activation loads bring the FP8 kernel to 64 VGPRs; the MXFP4 one fits with masked
     // loads, which measured faster for it
-    gate_up_item<FP4, !FP4>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
-                            w13, sw13, s13, H, I, h);
+    gate_up_item<FP4, !FP4, NSL>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
+                                 w13, sw13, s13, H, I, h);
   }
 }
 
@@ -687,7 +722,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
     hipLaunchKernelGGL((moe_gate_up_pairs_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st,
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h, cnt, ncnt);
   } else {
-    const int max_items = (T * S < E ? T * S : E) * (I / 8);
+    const int max_items = (T * S < E ? T * S : E) * (I / 8) / (FP4 ? 2 : 1);  // items of two slices for MXFP4
     const int most = FP4 ? kGateGridFp4 : kGateGrid;
     const int grid = max_items < most ? max_items : most;
     hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(grid),
