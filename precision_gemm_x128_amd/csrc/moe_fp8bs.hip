@@ -61,9 +61,11 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
 // Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs (kGateItemsFromFp4 for
-// MXFP4); above, a fixed grid of kGateGrid (kGateGridFp4) workgroups walking the (expert, slice)
-// items.  The item kernels fit 64 VGPRs without spills (a scalar wave index; unmasked activation
-// loads for FP8), so four workgroups share a CU: 1024 are resident at once.  A grid of exactly
+// MXFP4); above, a fixed grid of kGateGrid (kGateGridFp4) workgroups walking the (expert, two
+// slices) items.  With one slice per item both item kernels fitted 64 VGPRs without spills (a
+// scalar wave index; unmasked activation loads for FP8), so four workgroups shared a CU: 1024
+// resident at once; the grids below were measured then, and rechecked with two slices (FP8 at
+// three workgroups per CU: 1536 workgroups were level with 2048).  A grid of exactly
 // 1024 assigns every workgroup ceil or floor of items / 1024 items, and a last round that only a
 // few workgroups have costs a whole round (3088 items at 24 tokens, intermediate 128: four rounds
 // for an average of three).  With two or three workgroups per slot the later ones start as slots
@@ -99,6 +101,15 @@ __device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi
     const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j + 1], 1.0f, true);
     out[j] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
   }
+}
+
+// the eight e4m3 bytes of two dwords as one 8-value bf16 MFMA operand (exact)
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t d0, uint32_t d1) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+  const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
 // the eight e2m1 values of one dword (even K element in each byte's low nibble) as one 8-value
@@ -156,26 +167,22 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 // zeroed after the load), which saves the exec-mask branches and the registers they hold; masked
 // loads (DENSE false) keep the empty rows off the load pipeline that the weight stream shares.
 template <bool FP4, bool DENSE, int NSL>
-__device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp,
-                                             __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+__device__ __forceinline__ void gate_up_loop(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr, int srow,
                                              const uint16_t* xr, bool row_ok, int KB, int wave,
                                              v4f (&acc)[NSL]) {
   const int lane = threadIdx.x & 63;
+  constexpr uint32_t FB = FP4 ? 1024u : 2048u;  // bytes of a 16-column fragment of one K block
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) acc[sl] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int kb = wave; kb < KB; kb += kGateWaves) {
+    // the item's fragments (its NSL slices one after another) through a wave-uniform buffer
+    // resource: 32-bit lane offsets instead of 64-bit addresses
     u32x4 b0[NSL], b1[NSL];
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
-      if constexpr (FP4) {
-        // MXFP4: the item's fragments and group scales through wave-uniform buffer resources
-        // (32-bit lane offsets instead of 64-bit addresses)
-        b0[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               wr, (uint32_t)((sl * KB + kb) * 1024 + lane * 16), 0, 2));
-      } else {
-        b0[sl] = load_nt(wp + (int64_t)(sl * KB + kb) * 2048);
-        b1[sl] = load_nt(wp + (int64_t)(sl * KB + kb) * 2048 + 1024);
-      }
+      const uint32_t o = (uint32_t)(sl * KB + kb) * FB + (uint32_t)lane * 16u;
+      b0[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 2));
+      if constexpr (!FP4) b1[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, o + 1024u, 0, 2));
     }
     const u32x4* xa = (const u32x4*)(xr + kb * 128);
     u32x4 a[4];
@@ -188,9 +195,9 @@ __device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp
         a[i] = row_ok ? xa[i] : u32x4{0u, 0u, 0u, 0u};
       }
     }
+    // each 8-value operand is converted just before the MFMA that takes it
     if constexpr (FP4) {
-      // the group scales are applied by the conversion (one 8-value operand at a time, into the
-      // MFMA that takes it): the MFMAs accumulate into acc
+      // the group scales are applied by the conversion: the MFMAs accumulate into acc
       float scl[NSL];
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl)
@@ -201,15 +208,17 @@ __device__ __forceinline__ void gate_up_loop(const uint8_t* wp, const float* swp
         for (int sl = 0; sl < NSL; ++sl)
           acc[sl] = mfma_bf16(a[i], fp4x8_to_bf16(b0[sl][i], scl[sl]), acc[sl]);
     } else {
-      // e4m3: each block's four MFMAs give the fp32 partial that its 128x128 scale multiplies
-      const float sc = swp[kb];
+      // e4m3: each block's MFMAs give the fp32 partial that its 128x128 scale (the same for the
+      // item's slices) multiplies into acc
+      const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(srow * KB + kb) * 4u, 0, 0));
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) {
-        v8bf bv[4];
-        e4m3x32_to_bf16(b0[sl], b1[sl], bv);
         v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pm = mfma_bf16(a[i], bv[i], pm);
+        for (int i = 0; i < 4; ++i) {
+          const u32x4& w = i < 2 ? b0[sl] : b1[sl];
+          pm = mfma_bf16(a[i], e4m3x8_to_bf16(w[2 * (i & 1)], w[2 * (i & 1) + 1]), pm);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[sl][i] = acc[sl][i] + sc * pm[i];
       }
@@ -245,15 +254,15 @@ __device__ __forceinline__ void gate_up_item(
   const int j = lane & 15, chunk = lane >> 4;
   // column j < 8 is gate row 8q + j (scale block row q / 16), j >= 8 the matching up row
   const int srow = (j < 8) ? (q >> 4) : ((I >> 7) + (q >> 4));
-  // MXFP4: 1 KiB fragments (the item's NSL slices one after another) and the packed group scales
-  // in fragment order, one byte per lane, through wave-uniform buffer resources
+  // the item's weights: MXFP4 1 KiB fragments and, in fragment order, one group-scale byte per
+  // lane; e4m3 2 KiB fragments and the expert's 128x128 block scales [2I / 128, KB]
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(w13 + (int64_t)e * I * H + (int64_t)q * KB * 1024), 0, FP4 ? NSL * KB * 1024 : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64), 0, FP4 ? NSL * KB * 64 : 0, 0x00020000);
-  // e4m3: the slice's 2 KiB fragments and its 128x128 block scales
-  const float* swp = FP4 ? nullptr : sw13 + ((int64_t)e * (I >> 6) + srow) * KB;
-  const uint8_t* wp = FP4 ? nullptr : w13 + (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048 + lane * 16;
+      (void*)(w13 + (FP4 ? (int64_t)e * I * H + (int64_t)q * KB * 1024 : (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048)),
+      0, NSL * KB * (FP4 ? 1024 : 2048), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = FP4
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64), 0,
+                                          NSL * KB * 64, 0x00020000)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)(sw13 + (int64_t)e * (I >> 6) * KB), 0, (I >> 6) * KB * 4, 0x00020000);
   // the row tiles one after another (only an expert with more than 16 tokens, in practice the
   // shared one, has a second or third; its weight slice is then re-read from L2)
   for (int tile = 0; tile < tiles; ++tile) {
@@ -261,7 +270,7 @@ __device__ __forceinline__ void gate_up_item(
     const bool row_ok = idx < Me;
     const uint16_t* xr = x + (int64_t)(row_ok ? s_tok[idx] : 0) * ldx + chunk * 32;
     v4f acc[NSL];
-    gate_up_loop<FP4, DENSE, NSL>(wp, swp, wr, sr, xr, row_ok, KB, wave, acc);
+    gate_up_loop<FP4, DENSE, NSL>(wr, sr, srow, xr, row_ok, KB, wave, acc);
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
@@ -336,11 +345,12 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate_up_pairs_kernel(
 }
 
 // Above that: at most kGateGrid workgroups.  Every workgroup lists the distinct experts in
-// LDS, ordered by the first pair naming each, and takes the items (d-th distinct expert, slice q)
-// blockIdx.x, blockIdx.x + gridDim.x, ...; every wave runs the same bounded loop.
-// At most 64 VGPRs (eight waves per SIMD): four workgroups per CU.
+// LDS, ordered by the first pair naming each, and takes the items (d-th distinct expert, slices
+// q and q + 1) blockIdx.x, blockIdx.x + gridDim.x, ...; every wave runs the same bounded loop.
+// MXFP4 fits 64 VGPRs (eight waves per SIMD, four workgroups per CU); FP8, with twice the weight
+// registers, 72 (seven waves per SIMD, three workgroups per CU).
 template <bool FP4>
-__global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ __launch_bounds__(kGateThreads) __attribute__((amdgpu_waves_per_eu(FP4 ? 8 : 7)))
 void moe_gate_up_items_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ ids, int T, int S,
     int E, const uint8_t* __restrict__ w13, const float* __restrict__ sw13,
@@ -351,7 +361,7 @@ void moe_gate_up_items_kernel(
   __shared__ int s_dexp[kMoePairs];                 // the distinct experts, by first pair
   __shared__ int s_nd;
   __shared__ int s_tok[SMALLM_FP8BS_MOE_MAX_T + 1];
-  constexpr int NSL = FP4 ? 2 : 1;  // 8-column slices per item
+  constexpr int NSL = 2;  // 8-column slices per item
   __shared__ float s_red[NSL * kGateWaves * 4 * 64];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index in a scalar register: loop counters, scale loads and addresses derived from it
@@ -386,9 +396,8 @@ void moe_gate_up_items_kernel(
     const int e = s_dexp[item / QN], q = NSL * (item % QN);
     if (wave == 0) gather_tokens(e, T, S, s_ids, s_tok);
     __syncthreads();
-    // unmasked activation loads bring the FP8 kernel to 64 VGPRs; the MXFP4 one fits with masked
-    // loads, which measured faster for it
-    gate_up_item<FP4, !FP4, NSL>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
+    // masked activation loads (unmasked ones measured no faster with two slices per item)
+    gate_up_item<FP4, false, NSL>(e, q, s_tok[SMALLM_FP8BS_MOE_MAX_T], s_ids, s_tok, s_red, x, ldx, S,
                                  w13, sw13, s13, H, I, h);
   }
 }
@@ -722,7 +731,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
     hipLaunchKernelGGL((moe_gate_up_pairs_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st,
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h, cnt, ncnt);
   } else {
-    const int max_items = (T * S < E ? T * S : E) * (I / 8) / (FP4 ? 2 : 1);  // items of two slices for MXFP4
+    const int max_items = (T * S < E ? T * S : E) * (I / 16);  // items of two slices
     const int most = FP4 ? kGateGridFp4 : kGateGrid;
     const int grid = max_items < most ? max_items : most;
     hipLaunchKernelGGL((moe_gate_up_items_kernel<FP4>), dim3(grid),
