@@ -60,9 +60,8 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // of its expert, and a larger workgroup makes that dearer)
 constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
-// Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs (kGateItemsFromFp4 for
-// MXFP4); above, a fixed grid of kGateGrid (kGateGridFp4) workgroups walking the (expert, two
-// slices) items.  With one slice per item both item kernels fitted 64 VGPRs without spills (a
+// Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs; above, a fixed grid
+// of kGateGrid (kGateGridFp4) workgroups walking the (expert, two slices) items.  With one slice per item both item kernels fitted 64 VGPRs without spills (a
 // scalar wave index; unmasked activation loads for FP8), so four workgroups shared a CU: 1024
 // resident at once; the grids below were measured then, and rechecked with two slices (FP8 at
 // three workgroups per CU: 1536 workgroups were level with 2048).  A grid of exactly
@@ -73,13 +72,14 @@ constexpr int kGateWaves = kGateThreads / 64;
 // / 2048 / 3072 workgroups took 73.7 / 70.5 / 72.4 us at 24 tokens, 87.4 / 83.4 / 84.3 at 32 and
 // 113.8 / 109.8 / 109.4 at 48; MXFP4 took 74.6 / 72.8 / 70.8 us at 16 tokens and 145.7 / 141.8 /
 // 136.5 at 40; one workgroup per possible item was no better and less steady.
-// Against the per-pair grid, on the pages' shapes (11 slots): the item grid took 87 us instead of
-// 102 at 32 tokens and 114 instead of 129 at 48 (FP8, intermediate 128), 145 instead of 156 at 40
-// (MXFP4); at 16 tokens it was 3-4 % faster for both formats, and for MXFP4 it was 3 % faster from
-// four tokens on.  For FP8 at 8 tokens and intermediate 256 it was 1.6 % slower, hence the two
-// thresholds.
-constexpr int kGateItemsFrom = 128;
-constexpr int kGateItemsFromFp4 = 32;
+// Against the per-pair grid, on the pages' shapes (11 slots), with one slice per item: the item
+// grid took 87 us instead of 102 at 32 tokens and 114 instead of 129 at 48 (FP8, intermediate
+// 128), 145 instead of 156 at 40 (MXFP4); 3-4 % faster at 16 tokens for both formats, and for
+// MXFP4 3 % faster from four tokens on, while FP8 at 8 tokens and intermediate 256 was 1.6 %
+// slower (the FP8 threshold was then 128 pairs).  With two slices per item the FP8 item grid is
+// ahead from four tokens on as well: 54.5 -> 49.9 us at 8 tokens and 33.5 -> 31.5 at 4
+// (intermediate 256), 34.0 -> 32.5 at 8 (intermediate 128; level at 4); one threshold serves both.
+constexpr int kGateItemsFrom = 32;
 constexpr int kGateGrid = 2048;
 constexpr int kGateGridFp4 = 3072;
 // phase 2: 16 waves per workgroup, each walking its own experts, at most 64 VGPRs so that two
@@ -727,7 +727,7 @@ void launch_moe(const uint16_t* x, int64_t ldx, const int32_t* ids, const float*
   float* part = ns > 1 ? (float*)(ws + moe_h_bytes(T, S, I)) : nullptr;
   uint32_t* cnt = ns > 1 ? (uint32_t*)(ws + moe_h_bytes(T, S, I) + moe_part_bytes(T, S, H)) : nullptr;
   const int ncnt = ns > 1 ? H / 16 : 0;
-  if (T * S <= (FP4 ? kGateItemsFromFp4 : kGateItemsFrom)) {
+  if (T * S <= kGateItemsFrom) {
     hipLaunchKernelGGL((moe_gate_up_pairs_kernel<FP4>), dim3(T * S, I / 8), dim3(kGateThreads), 0, st,
                        x, ldx, ids, T, S, E, w13, sw13, s13, H, I, h, cnt, ncnt);
   } else {

@@ -198,8 +198,10 @@ SMALL_CASES = [
     (48, 16, 4096, 256, 128, False, 9),   # largest T, S and E: 768 pairs, item grid, full expert table
     (3, 2, 3, 16384, 256, False, 10),     # largest hidden size: 128 K blocks in phase 1
     (3, 2, 3, 1024, 2048, False, 12),     # largest intermediate: 16 K blocks in phase 2
-    (8, 16, 200, 512, 256, False, 13),    # 128 pairs: the largest per-pair grid in phase 1
-    (43, 3, 200, 512, 256, False, 14),    # 129 pairs: the smallest item grid in phase 1
+    (8, 16, 200, 512, 256, False, 13),    # 128 pairs: the largest unsplit down projection
+    (43, 3, 200, 512, 256, False, 14),    # 129 pairs: the smallest split one
+    (2, 16, 200, 512, 256, False, 15),    # 32 pairs: the largest per-pair grid in phase 1
+    (11, 3, 200, 512, 256, False, 16),    # 33 pairs: the smallest item grid in phase 1
 ]
 
 
