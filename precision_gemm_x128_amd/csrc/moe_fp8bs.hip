@@ -475,20 +475,27 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
       const int e = __builtin_amdgcn_readlane(ec, __builtin_ctzll(mine));
       mine &= mine - 1;
       const float* swp = FP4 ? nullptr : sw2 + ((int64_t)e * (H >> 7) + nb) * KB2;
-      const uint8_t* sbp =
-          FP4 ? s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64 + lane : nullptr;
       const uint8_t* wp = wtile + (int64_t)e * H * I / (FP4 ? 2 : 1);
+      // MXFP4: the expert's fragments of this tile and their group-scale bytes
+      const __amdgpu_buffer_rsrc_t wr4 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(w2 + (int64_t)e * H * I / 2 + (int64_t)blockIdx.x * KB2 * 1024), 0, FP4 ? KB2 * 1024 : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t sr4 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(s2 + (int64_t)e * H * (I >> 5) + (int64_t)blockIdx.x * KB2 * 64), 0, FP4 ? KB2 * 64 : 0, 0x00020000);
       // the first K block's weights and scale depend only on the expert, so they are loaded before
       // the gather and are in flight during it
       u32x4 pre0 = u32x4{0u, 0u, 0u, 0u}, pre1 = u32x4{0u, 0u, 0u, 0u};
-      float pre_s = 0.0f;
+      float pre_s = 0.0f, pre_s1 = 0.0f;
       if constexpr (!FP4) {
         pre0 = load_nt(wp);
         pre1 = load_nt(wp + 1024);
         pre_s = swp[0];
       } else {
-        pre0 = load_nt(wp);
-        pre_s = e8m0_f32(sbp[0]);
+        // MXFP4: the second K block's 1 KiB fragment and scale too (zeros past the expert's
+        // blocks), through wave-uniform buffer resources
+        pre0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr4, (uint32_t)lane * 16u, 0, 2));
+        pre1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr4, 1024u + (uint32_t)lane * 16u, 0, 2));
+        pre_s = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(sr4, (uint32_t)lane, 0, 0));
+        pre_s1 = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(sr4, 64u + (uint32_t)lane, 0, 0));
       }
       // gather: lane t (< T) is routed to e when some slot of token t names it
       int slot = -1;
@@ -517,9 +524,13 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
           float sc;
           if constexpr (FP4) {
             // the group scale is applied by the conversion; the partial needs no block scale
-            const bool first = tile == 0 && kb == 0;
-            fp4x32_to_bf16(first ? pre0 : load_nt(wp + (int64_t)kb * 1024),
-                           first ? pre_s : e8m0_f32(sbp[(int64_t)kb * 64]), bv);
+            const bool pre = tile == 0 && kb < 2;
+            fp4x32_to_bf16(pre ? (kb == 0 ? pre0 : pre1)
+                               : __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               wr4, (uint32_t)(kb * 1024 + lane * 16), 0, 2)),
+                           pre ? (kb == 0 ? pre_s : pre_s1)
+                               : e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(sr4, (uint32_t)(kb * 64 + lane), 0, 0)),
+                           bv);
             sc = 1.0f;
           } else {
             const bool first = tile == 0 && kb == 0;
