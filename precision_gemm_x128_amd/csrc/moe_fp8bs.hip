@@ -61,10 +61,11 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kGateThreads = 512;
 constexpr int kGateWaves = kGateThreads / 64;
 // Phase 1 grid: one workgroup per pair and slice up to kGateItemsFrom pairs; above, a fixed grid
-// of kGateGrid (kGateGridFp4) workgroups walking the (expert, two slices) items.  With one slice per item both item kernels fitted 64 VGPRs without spills (a
-// scalar wave index; unmasked activation loads for FP8), so four workgroups shared a CU: 1024
-// resident at once; the grids below were measured then, and rechecked with two slices (FP8 at
-// three workgroups per CU: 1536 workgroups were level with 2048).  A grid of exactly
+// of kGateGrid (kGateGridFp4) workgroups walking the (expert, two slices) items.  With one slice
+// per item both item kernels fitted 64 VGPRs without spills (a scalar wave index; unmasked
+// activation loads for FP8), so four workgroups shared a CU: 1024 resident at once; the grids
+// below were measured then, and rechecked with two slices (FP8 at three workgroups per CU: 1536
+// workgroups were level with 2048).  A grid of exactly
 // 1024 assigns every workgroup ceil or floor of items / 1024 items, and a last round that only a
 // few workgroups have costs a whole round (3088 items at 24 tokens, intermediate 128: four rounds
 // for an average of three).  With two or three workgroups per slot the later ones start as slots
@@ -90,19 +91,6 @@ constexpr int kMoePairs = SMALLM_FP8BS_MOE_MAX_T * SMALLM_FP8BS_MOE_MAX_S;
 constexpr uint32_t kMoeLayoutId = 0x4D4F4510u;
 constexpr uint32_t kMoeFp4LayoutId = 0x4D4F4504u;
 
-// the 32 e4m3 bytes a lane holds for one 128-K block, as four 8-value bf16 MFMA operands
-__device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi, v8bf out[4]) {
-  const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j], 1.0f, false);
-    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j], 1.0f, true);
-    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j + 1], 1.0f, false);
-    const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * j + 1], 1.0f, true);
-    out[j] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
-  }
-}
-
 // the eight e4m3 bytes of two dwords as one 8-value bf16 MFMA operand (exact)
 __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t d0, uint32_t d1) {
   const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
@@ -110,6 +98,14 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t d0, uint32_t d1) {
   const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
   const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// the 32 e4m3 bytes a lane holds for one 128-K block, as four 8-value bf16 MFMA operands
+__device__ __forceinline__ void e4m3x32_to_bf16(const u32x4& lo, const u32x4& hi, v8bf out[4]) {
+  out[0] = e4m3x8_to_bf16(lo.x, lo.y);
+  out[1] = e4m3x8_to_bf16(lo.z, lo.w);
+  out[2] = e4m3x8_to_bf16(hi.x, hi.y);
+  out[3] = e4m3x8_to_bf16(hi.z, hi.w);
 }
 
 // the eight e2m1 values of one dword (even K element in each byte's low nibble) as one 8-value
@@ -182,7 +178,8 @@ __device__ __forceinline__ void gate_up_loop(__amdgpu_buffer_rsrc_t wr, __amdgpu
     for (int sl = 0; sl < NSL; ++sl) {
       const uint32_t o = (uint32_t)(sl * KB + kb) * FB + (uint32_t)lane * 16u;
       b0[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 2));
-      if constexpr (!FP4) b1[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, o + 1024u, 0, 2));
+      if constexpr (!FP4)
+        b1[sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, o + 1024u, 0, 2));
     }
     const u32x4* xa = (const u32x4*)(xr + kb * 128);
     u32x4 a[4];
@@ -201,7 +198,8 @@ __device__ __forceinline__ void gate_up_loop(__amdgpu_buffer_rsrc_t wr, __amdgpu
       float scl[NSL];
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl)
-        scl[sl] = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(sr, (uint32_t)((sl * KB + kb) * 64 + lane), 0, 0));
+        scl[sl] = e8m0_f32(
+            __builtin_amdgcn_raw_buffer_load_b8(sr, (uint32_t)((sl * KB + kb) * 64 + lane), 0, 0));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -210,7 +208,8 @@ __device__ __forceinline__ void gate_up_loop(__amdgpu_buffer_rsrc_t wr, __amdgpu
     } else {
       // e4m3: each block's MFMAs give the fp32 partial that its 128x128 scale (the same for the
       // item's slices) multiplies into acc
-      const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(srow * KB + kb) * 4u, 0, 0));
+      const float sc = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)(srow * KB + kb) * 4u, 0, 0));
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) {
         v4f pm = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -232,9 +231,9 @@ __device__ __forceinline__ void gate_up_loop(__amdgpu_buffer_rsrc_t wr, __amdgpu
   }
 }
 
-// Phase 1 for one work item: expert e's 8-column slice q, for the Me tokens listed (ascending) in
-// s_tok.  All threads of the workgroup call it; it ends with a barrier, after which s_tok may be
-// rewritten.
+// Phase 1 for one work item: expert e's 8-column slices q .. q + NSL - 1, for the Me tokens listed
+// (ascending) in s_tok.  All threads of the workgroup call it; it ends with a barrier, after which
+// s_tok may be rewritten.
 template <bool FP4, bool DENSE, int NSL>
 __device__ __forceinline__ void gate_up_item(
     int e, int q, int Me, const int* s_ids, const int* s_tok, float* s_red,
@@ -256,13 +255,15 @@ __device__ __forceinline__ void gate_up_item(
   const int srow = (j < 8) ? (q >> 4) : ((I >> 7) + (q >> 4));
   // the item's weights: MXFP4 1 KiB fragments and, in fragment order, one group-scale byte per
   // lane; e4m3 2 KiB fragments and the expert's 128x128 block scales [2I / 128, KB]
+  const int64_t wbase = FP4 ? (int64_t)e * I * H + (int64_t)q * KB * 1024
+                            : (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(w13 + (FP4 ? (int64_t)e * I * H + (int64_t)q * KB * 1024 : (int64_t)e * 2 * I * H + (int64_t)q * KB * 2048)),
-      0, NSL * KB * (FP4 ? 1024 : 2048), 0x00020000);
-  const __amdgpu_buffer_rsrc_t sr = FP4
-      ? __builtin_amdgcn_make_buffer_rsrc((void*)(s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64), 0,
-                                          NSL * KB * 64, 0x00020000)
-      : __builtin_amdgcn_make_buffer_rsrc((void*)(sw13 + (int64_t)e * (I >> 6) * KB), 0, (I >> 6) * KB * 4, 0x00020000);
+      (void*)(w13 + wbase), 0, NSL * KB * (FP4 ? 1024 : 2048), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr =
+      FP4 ? __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(s13 + (int64_t)e * 2 * I * (H >> 5) + (int64_t)q * KB * 64), 0, NSL * KB * 64, 0x00020000)
+          : __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(sw13 + (int64_t)e * (I >> 6) * KB), 0, (I >> 6) * KB * 4, 0x00020000);
   // the row tiles one after another (only an expert with more than 16 tokens, in practice the
   // shared one, has a second or third; its weight slice is then re-read from L2)
   for (int tile = 0; tile < tiles; ++tile) {
@@ -468,7 +469,8 @@ __global__ __launch_bounds__(kDownThreads, 8) void moe_down_kernel(
     const int ec = pp < hi ? s_ids[pp] : -1;
     const bool first = ec >= 0 && ec < E && s_first[ec] == pp;
     const uint64_t m = __ballot(first);
-    const int rank = d0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const int rank =
+        d0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     uint64_t mine = __ballot(first && (rank % kDownWaves) == wave);
     d0 += __popcll(m);
     while (mine) {
