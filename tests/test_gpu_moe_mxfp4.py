@@ -316,7 +316,7 @@ def test_mxfp4_deterministic_and_graph_replay_bitwise():
     x = to_dev_bf16(synthgen.gen_x(T, H, seed=21))
     idd = torch.from_numpy(ids).to(DEV)
     twd = torch.from_numpy(tw).to(DEV)
-    assert P.smallm_fp8bs_moe_splits(T, S) > 1          # the three-launch form is captured
+    assert P.smallm_fp8bs_moe_splits(T, S) > 1          # the split form is captured
     y1, h1 = P.smallm_fp8bs_moe_mxfp4(x, idd, twd, w13p, s13p, w2p, s2p)
     y2, h2 = P.smallm_fp8bs_moe_mxfp4(x, idd, twd, w13p, s13p, w2p, s2p)
     torch.cuda.synchronize()
